@@ -1,0 +1,91 @@
+"""Seeded synthetic inputs shared by the CPU oracle and the GPU path.
+
+Only input generation lives here (keys, the counter-based generator, the
+workload shapes); none of the MoE arithmetic does.  Host generation goes
+through libdg_host.so, device generation through libdg_device.so; both
+produce identical bf16 bits for the same key and element index.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from .build import HOST_SO, DEV_SO
+
+# tensor families / ids used in keys
+FAMILY_TINY = 1
+FAMILY_LING = 2
+TENSOR_X = 1
+TENSOR_ROUTER = 2
+TENSOR_GATE_UP = 3
+TENSOR_DOWN = 4
+TENSOR_LMHEAD = 5
+
+SIGMA_W = 0.02   # weights ~ N(0, 0.02^2)
+SIGMA_X = 1.0    # inputs ~ N(0, 1)
+
+_host = None
+_dev = None
+
+
+def _host_lib():
+    global _host
+    if _host is None:
+        if not os.path.exists(HOST_SO):
+            raise RuntimeError("libdg_host.so is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(HOST_SO)
+        lib.dg_key_c.restype = ctypes.c_uint64
+        lib.dg_key_c.argtypes = [ctypes.c_uint64] + [ctypes.c_uint32] * 5
+        lib.dg_ih12_c.restype = ctypes.c_int32
+        lib.dg_ih12_c.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+        lib.dg_fill_bf16.restype = None
+        lib.dg_fill_bf16.argtypes = [ctypes.c_void_p, ctypes.c_uint64] + [ctypes.c_int64] * 5 + [ctypes.c_float]
+        _host = lib
+    return _host
+
+
+def _dev_lib():
+    global _dev
+    if _dev is None:
+        if not os.path.exists(DEV_SO):
+            raise RuntimeError("libdg_device.so is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(DEV_SO)
+        lib.dg_fill_bf16_dev.restype = ctypes.c_int
+        lib.dg_fill_bf16_dev.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int] + \
+            [ctypes.c_int64] * 6 + [ctypes.c_float, ctypes.c_void_p]
+        _dev = lib
+    return _dev
+
+
+def scale_for(sigma):
+    """fp32 multiplier that maps an Irwin-Hall(12) integer to a sample of std sigma."""
+    return float(np.float32(sigma / 65536.0))
+
+
+def key(seed, family, layer, tensor, expert=0, attempt=0):
+    return int(_host_lib().dg_key_c(seed, family, layer, tensor, expert, attempt))
+
+
+def ih12(k, n):
+    return int(_host_lib().dg_ih12_c(k, n))
+
+
+def fill_host(k, rows, cols, sigma, row0=0, col0=0, ld_full=None):
+    """bf16 bits (uint16 array [rows, cols]) of a slice of the keyed tensor."""
+    if ld_full is None:
+        ld_full = cols
+    out = np.empty((rows, cols), dtype=np.uint16)
+    _host_lib().dg_fill_bf16(out.ctypes.data, k, row0, col0, rows, cols, ld_full,
+                             scale_for(sigma))
+    return out
+
+
+def fill_device(out_ptr, keys_dev_ptr, n_blocks, block_stride, rows, cols, sigma,
+                row0=0, col0=0, ld_full=None, stream=0):
+    """Fill n_blocks device slices (block b at out_ptr + 2*b*block_stride bytes)."""
+    if ld_full is None:
+        ld_full = cols
+    rc = _dev_lib().dg_fill_bf16_dev(out_ptr, keys_dev_ptr, n_blocks, block_stride, row0, col0,
+                                     rows, cols, ld_full, scale_for(sigma), stream)
+    if rc != 0:
+        raise RuntimeError("dg_fill_bf16_dev failed (%d)" % rc)

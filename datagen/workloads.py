@@ -1,0 +1,103 @@
+"""The synthetic workloads: shapes, seeds and the keyed slices of every tensor.
+
+Shapes follow the Ling-3.0-flash model table ("Ling-3.0-flash on 4 Blackwell
+GPUs", section "The model"): hidden 2560, 512 routed experts + 1 shared,
+top-8, expert intermediate 768, vocabulary about 157k (157184 here), with the
+tensor-parallel shard taking a quarter of the intermediate size.  All weights
+are ~N(0, 0.02^2) and inputs ~N(0, 1) (Irwin-Hall(12) approximation, see
+dg_core.h).  Nothing here computes any part of the MoE layer.
+"""
+from dataclasses import dataclass
+
+from . import (FAMILY_LING, FAMILY_TINY, SIGMA_W, SIGMA_X, TENSOR_DOWN, TENSOR_GATE_UP,
+               TENSOR_LMHEAD, TENSOR_ROUTER, TENSOR_X, fill_host, key)
+
+WEIGHT_SEED = 0x5EED0001
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    cfg_id: int
+    family: int
+    H: int
+    E: int
+    K: int
+    I: int          # intermediate size of this call (the shard's share under TP)
+    S: int          # shared experts (0 or 1)
+    M: int          # token rows
+    x_seed: int
+    n_layers: int = 1
+    V: int = 0      # lm_head vocabulary (0 = no lm_head)
+    n_shards: int = 1
+    shard: int = 0
+    out_f32: bool = False
+    residual: bool = False
+
+    @property
+    def I_full(self):
+        return self.I * self.n_shards
+
+    def expert_bytes(self):
+        return 3 * self.H * self.I * 2
+
+    def router_bytes(self):
+        return self.E * self.H * 2
+
+    def layer_bytes(self):
+        return self.router_bytes() + (self.E + self.S) * self.expert_bytes()
+
+
+C1 = Workload("tiny_moe_layer_m1", 1, FAMILY_TINY, H=256, E=16, K=2, I=64, S=1, M=1, x_seed=101)
+C2 = Workload("ling_moe_layer_m1", 2, FAMILY_LING, H=2560, E=512, K=8, I=768, S=1, M=1,
+              x_seed=202)
+C3 = Workload("ling_moe_layer_m6", 3, FAMILY_LING, H=2560, E=512, K=8, I=768, S=1, M=6,
+              x_seed=303)
+C4 = Workload("ling_tp4_shard_moe_layer_m6", 4, FAMILY_LING, H=2560, E=512, K=8, I=192, S=1,
+              M=6, x_seed=404, n_shards=4, shard=0, out_f32=True)
+C5 = Workload("ling_chain16_lmhead_m6", 5, FAMILY_LING, H=2560, E=512, K=8, I=768, S=1, M=6,
+              x_seed=505, n_layers=16, V=157184, residual=True)
+
+ALL = (C1, C2, C3, C4, C5)
+
+
+# ---- host slices ------------------------------------------------------------
+
+def x_row(wl, m, attempt=0):
+    k = key(wl.x_seed, wl.family, wl.cfg_id, TENSOR_X, m, attempt)
+    return fill_host(k, 1, wl.H, SIGMA_X)[0]
+
+
+def x_rows(wl, attempts):
+    import numpy as np
+    return np.stack([x_row(wl, m, a) for m, a in enumerate(attempts)])
+
+
+def router(wl, layer=0):
+    k = key(WEIGHT_SEED, wl.family, layer, TENSOR_ROUTER)
+    return fill_host(k, wl.E, wl.H, SIGMA_W)
+
+
+def expert_gate_up(wl, layer, e):
+    """[2I][H]: this shard's gate rows, then its up rows, of the full [2*I_full][H] tensor."""
+    import numpy as np
+    k = key(WEIGHT_SEED, wl.family, layer, TENSOR_GATE_UP, e)
+    g = fill_host(k, wl.I, wl.H, SIGMA_W, row0=wl.shard * wl.I, ld_full=wl.H)
+    u = fill_host(k, wl.I, wl.H, SIGMA_W, row0=wl.I_full + wl.shard * wl.I, ld_full=wl.H)
+    return np.concatenate([g, u], axis=0)
+
+
+def expert_down(wl, layer, e):
+    """[H][I]: this shard's columns of the full [H][I_full] tensor."""
+    k = key(WEIGHT_SEED, wl.family, layer, TENSOR_DOWN, e)
+    return fill_host(k, wl.H, wl.I, SIGMA_W, col0=wl.shard * wl.I, ld_full=wl.I_full)
+
+
+def lmhead(wl):
+    k = key(WEIGHT_SEED, wl.family, 0, TENSOR_LMHEAD)
+    return fill_host(k, wl.V, wl.H, SIGMA_W)
+
+
+def lmhead_rows(wl, v0, n):
+    k = key(WEIGHT_SEED, wl.family, 0, TENSOR_LMHEAD)
+    return fill_host(k, n, wl.H, SIGMA_W, row0=v0, ld_full=wl.H)

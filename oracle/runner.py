@@ -1,0 +1,95 @@
+"""Run the oracle on a synthetic workload (TEST INFRASTRUCTURE ONLY).
+
+Generates, through the shared seeded generator, exactly the weights the
+oracle's own routing selects, so a layer never needs the full expert tensor
+on the host.
+"""
+import numpy as np
+
+from datagen import workloads as W
+
+from . import experts_combine, lmhead_argmax, residual, router_topk, cast_bf16
+
+
+class ExpertCache:
+    """Host copies of generated expert weights, keyed by (layer, expert)."""
+
+    def __init__(self, wl):
+        self.wl = wl
+        self.gu = {}
+        self.d = {}
+
+    def get(self, layer, e):
+        k = (layer, e)
+        if k not in self.gu:
+            self.gu[k] = W.expert_gate_up(self.wl, layer, e)
+            self.d[k] = W.expert_down(self.wl, layer, e)
+        return self.gu[k], self.d[k]
+
+    def drop_layer(self, layer):
+        for k in [k for k in self.gu if k[0] == layer]:
+            del self.gu[k]
+            del self.d[k]
+
+
+def layer(wl, x, layer_idx=0, cache=None, w_router=None):
+    """One MoE layer: returns dict(idx, gate, logits, acc fp32 [M, H])."""
+    if w_router is None:
+        w_router = W.router(wl, layer_idx)
+    idx, gate, logits = router_topk(x, w_router, wl.K)
+    cache = cache or ExpertCache(wl)
+    used = sorted(set(int(e) for e in idx.ravel()))
+    if wl.S:
+        used.append(wl.E)
+    gu, d = {}, {}
+    for e in used:
+        gu[e], d[e] = cache.get(layer_idx, e)
+    acc = experts_combine(x, idx, gate, gu, d, wl.E, wl.S)
+    return dict(idx=idx, gate=gate, logits=logits, acc=acc)
+
+
+def layer_output(wl, res):
+    """The layer's output as the call returns it (fp32 partial or one bf16 cast)."""
+    return res["acc"] if wl.out_f32 else cast_bf16(res["acc"])
+
+
+def chain(wl, x, n_layers=None, keep_cache=False):
+    """Residual chain h_{l+1} = bf16(h_l + MoE_l(h_l)); returns (h_L, per-layer results)."""
+    n_layers = wl.n_layers if n_layers is None else n_layers
+    h = np.ascontiguousarray(x, dtype=np.uint16)
+    per = []
+    cache = ExpertCache(wl)
+    for l in range(n_layers):
+        r = layer(wl, h, l, cache)
+        r["h_in"] = h
+        h = residual(h, r["acc"])
+        per.append(r)
+        if not keep_cache:
+            cache.drop_layer(l)
+    return h, per
+
+
+def router_margin(logits, K):
+    """Per row: K-th largest logit minus (K+1)-th largest (how far from a tie the selection is)."""
+    s = -np.sort(-logits.astype(np.float64), axis=1)
+    if s.shape[1] <= K:
+        return np.full(s.shape[0], np.inf)
+    return s[:, K - 1] - s[:, K]
+
+
+def lmhead_margin(h, w):
+    """Per row: gap between the two largest float64 lm_head logits."""
+    hf = (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    z = np.empty((h.shape[0], w.shape[0]))
+    step = 16384
+    for v0 in range(0, w.shape[0], step):
+        wf = (w[v0:v0 + step].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        z[:, v0:v0 + step] = hf @ wf.T
+    s = -np.sort(-z, axis=1)
+    return s[:, 0] - s[:, 1]
+
+
+def lm_head(wl, h, w=None):
+    if w is None:
+        w = W.lmhead(wl)
+    return lmhead_argmax(h, w)

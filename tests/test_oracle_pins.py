@@ -1,0 +1,447 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each check is chosen so that a plausible mistake in the oracle (a dropped term,
+a swapped gate/up half, a transposed operand, a wrong sign in silu, a wrong
+tie-break, a double rounding) fails at least one of them:
+exact rational arithmetic on dyadic inputs, float64 error bounds, brute-force
+selection, library routines (torch's bf16 rounding, numpy's stable sort,
+scipy's softmax), closed forms and invariants.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import runner
+from datagen import workloads as W
+
+U32 = 2.0 ** -24  # unit roundoff of fp32
+
+
+def bf16_bits_torch(x64):
+    """Library rounding: float64 -> bf16 via torch (round to nearest even)."""
+    t = torch.tensor(np.asarray(x64, dtype=np.float64)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().astype(np.uint16)
+
+
+def f32(bits):
+    return oracle.bf16_to_f32(bits)
+
+
+def to_bf16_bits_exact(vals):
+    """bf16 bits of values that are exactly representable in bf16."""
+    b = bf16_bits_torch(vals)
+    assert np.array_equal(f32(b).astype(np.float64), np.asarray(vals, np.float64))
+    return b
+
+
+def dyadic(rng, shape, lim=16):
+    """Values k/8 with |k| <= lim: exact in bf16, products and short sums exact in fp32."""
+    return rng.integers(-lim, lim + 1, size=shape) / 8.0
+
+
+def gamma(n):
+    return n * U32 / (1 - n * U32)
+
+
+# ---------------------------------------------------------------- bf16 rounding
+
+def test_bf16_rounding_matches_library(rng):
+    vals = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-30).astype(np.float32),
+        (rng.standard_normal(2000) * 1e30).astype(np.float32),
+        np.array([0.0, -0.0, 1.0, -1.0, 3.0e38], np.float32),
+    ])
+    # exact halfway cases: bf16 value plus half an ulp (both even and odd neighbours)
+    base = f32(rng.integers(0x3F00, 0x4100, 2000).astype(np.uint16))
+    half = (base.view(np.uint32) + np.uint32(0x8000)).view(np.float32)
+    vals = np.concatenate([vals, half])
+    mine = oracle.f32_to_bf16(vals)
+    ref = torch.tensor(vals).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    assert np.array_equal(mine, ref)
+    assert np.array_equal(oracle.cast_bf16(vals), ref)
+
+
+# ---------------------------------------------------------------- router GEMV
+
+def test_router_logits_exact_on_dyadic_inputs(rng):
+    M, H, E = 2, 8, 6
+    x = dyadic(rng, (M, H))
+    w = dyadic(rng, (E, H))
+    lg = oracle.router_logits(to_bf16_bits_exact(x), to_bf16_bits_exact(w))
+    for m in range(M):
+        for e in range(E):
+            exact = sum(Fraction(x[m, h]) * Fraction(w[e, h]) for h in range(H))
+            assert Fraction(float(lg[m, e])) == exact
+
+
+def test_router_logits_within_float64_bound(rng):
+    wl = W.C3
+    x = W.x_rows(wl, [0] * 3)
+    w = W.router(wl)[:64]
+    lg = oracle.router_logits(x, w).astype(np.float64)
+    xf, wf = f32(x).astype(np.float64), f32(w).astype(np.float64)
+    ref = xf @ wf.T
+    bound = gamma(wl.H) * (np.abs(xf) @ np.abs(wf).T)
+    assert np.all(np.abs(lg - ref) <= bound)
+    # a transposed or shifted operand would be far outside the bound
+    assert np.abs(lg - ref).max() < 1e-4
+
+
+# ---------------------------------------------------------------- selection and gates
+
+def test_selection_matches_bruteforce_and_stable_sort(rng):
+    E, K = 7, 3
+    for trial in range(200):
+        lg = rng.integers(-3, 4, size=(1, E)).astype(np.float32)  # many exact ties
+        idx, _ = oracle.select_gates(lg, K)
+        S = list(idx[0])
+        # brute force: exactly one K-subset dominates its complement under
+        # (larger logit, then lower index); it must be the oracle's set
+        def beats(a, b):
+            return lg[0, a] > lg[0, b] or (lg[0, a] == lg[0, b] and a < b)
+        winners = [c for c in itertools.combinations(range(E), K)
+                   if all(beats(a, b) for a in c for b in range(E) if b not in c)]
+        assert len(winners) == 1 and set(winners[0]) == set(S)
+        # order: descending logit, lower index first among equals (numpy stable sort)
+        assert S == list(np.argsort(-lg[0], kind="stable")[:K])
+
+
+def test_gates_sum_to_one_and_closed_forms(rng):
+    from scipy.special import softmax
+    M, E, K = 6, 512, 8
+    lg = (rng.standard_normal((M, E)) * 1.0).astype(np.float32)
+    idx, g = oracle.select_gates(lg, K)
+    assert np.all(np.abs(g.astype(np.float64).sum(1) - 1.0) <= 4 * K * U32)
+    sm = softmax(lg.astype(np.float64), axis=1)
+    ref = np.take_along_axis(sm, idx, 1)
+    ref = ref / ref.sum(1, keepdims=True)
+    assert np.all(np.abs(g - ref) <= 1e-6 * ref + 1e-12)
+    # K = 1: the renormalised gate is exactly one
+    _, g1 = oracle.select_gates(lg, 1)
+    assert np.all(g1 == 1.0)
+    # K = E: the gates are the full softmax, in selection order
+    idxE, gE = oracle.select_gates(lg[:, :16], 16)
+    smE = np.take_along_axis(softmax(lg[:, :16].astype(np.float64), axis=1), idxE, 1)
+    assert np.all(np.abs(gE - smE) <= 1e-6 * smE)
+    # two experts: g0 = 1 / (1 + exp(l1 - l0))
+    two = np.array([[0.75, -0.5]], np.float32)
+    _, g2 = oracle.select_gates(two, 2)
+    assert abs(g2[0, 0] - 1.0 / (1.0 + math.exp(-1.25))) < 1e-7
+    # a common shift of every logit leaves the gates unchanged (within rounding)
+    _, gs = oracle.select_gates(lg + np.float32(3.0), K)
+    assert np.all(np.abs(gs - g) <= 1e-6)
+
+
+# ---------------------------------------------------------------- SwiGLU
+
+def test_swiglu_exhaustive_over_bf16(rng):
+    """All finite bf16 a with b = 1: h = bf16(silu(a)) up to a rounding-boundary tie."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    a = f32(bits)
+    finite = np.isfinite(a)
+    a = a[finite]
+    lib = oracle.lib()
+    mine = np.array([lib.oracle_swiglu(float(v), 1.0) for v in a], dtype=np.uint16)
+    a64 = a.astype(np.float64)
+    with np.errstate(over="ignore"):
+        s64 = a64 / (1.0 + np.exp(-a64))
+    ref = bf16_bits_torch(s64)
+    diff = mine != ref
+    # a difference is allowed only where silu lies within two fp32 ulps of a bf16 midpoint
+    lo = f32(ref[diff]).astype(np.float64)
+    other = f32(mine[diff]).astype(np.float64)
+    mid = (lo + other) / 2
+    assert np.all(np.abs(s64[diff] - mid) <= 2 * U32 * np.abs(s64[diff]) + 1e-45)
+    assert diff.sum() <= 8
+    # silu is asymmetric: swapping gate and up, or dropping the minus sign, is caught
+    assert lib.oracle_swiglu(-2.0, 1.0) != lib.oracle_swiglu(2.0, 1.0)
+    assert oracle.swiglu(2.0, 3.0) != oracle.swiglu(3.0, 2.0)
+
+
+def test_swiglu_random_pairs_against_float64(rng):
+    a = (rng.standard_normal(4000) * 3).astype(np.float32)
+    b = (rng.standard_normal(4000) * 3).astype(np.float32)
+    mine = np.array([oracle.swiglu(x, y) for x, y in zip(a, b)], dtype=np.uint16)
+    a64, b64 = a.astype(np.float64), b.astype(np.float64)
+    v = a64 / (1.0 + np.exp(-a64)) * b64
+    ref = bf16_bits_torch(v)
+    diff = mine != ref
+    assert diff.sum() <= 4
+    if diff.any():
+        mid = (f32(ref[diff]).astype(np.float64) + f32(mine[diff]).astype(np.float64)) / 2
+        assert np.all(np.abs(v[diff] - mid) <= 4 * U32 * np.abs(v[diff]))
+
+
+# ---------------------------------------------------------------- one expert
+
+def test_expert_gate_up_exact_and_down_within_bound(rng):
+    H, I = 8, 4
+    x = dyadic(rng, (H,))
+    wgu = dyadic(rng, (2 * I, H))
+    wd = dyadic(rng, (H, I))
+    y, h = oracle.expert(to_bf16_bits_exact(x), to_bf16_bits_exact(wgu), to_bf16_bits_exact(wd))
+    for j in range(I):
+        a = sum(Fraction(x[k]) * Fraction(wgu[j, k]) for k in range(H))
+        b = sum(Fraction(x[k]) * Fraction(wgu[I + j, k]) for k in range(H))
+        # a and b are exact fp32 numbers; h must be SwiGLU of exactly these (gate rows first)
+        assert h[j] == oracle.swiglu(float(a), float(b))
+    hf = f32(h).astype(np.float64)
+    for n in range(H):
+        exact = sum(Fraction(float(hf[j])) * Fraction(wd[n, j]) for j in range(I))
+        terms = sum(abs(float(hf[j]) * wd[n, j]) for j in range(I))
+        assert abs(float(y[n]) - float(exact)) <= gamma(I) * terms
+
+
+def test_identity_like_top1_reduces_to_swiglu_of_input(rng):
+    """K=1, zero shared expert, identical routed experts with W_g = W_u = [I | 0]
+    and W_d = [I ; 0]: out_n = bf16(silu(x_n) * x_n) for n < I, else 0."""
+    H, I, E, K = 64, 16, 4, 1
+    x = bf16_bits_torch(rng.standard_normal((2, H)) * 2)
+    eye_gu = np.zeros((2 * I, H))
+    eye_gu[np.arange(I), np.arange(I)] = 1.0
+    eye_gu[I + np.arange(I), np.arange(I)] = 1.0
+    eye_d = np.zeros((H, I))
+    eye_d[np.arange(I), np.arange(I)] = 1.0
+    gu = {e: to_bf16_bits_exact(eye_gu) for e in range(E)}
+    d = {e: to_bf16_bits_exact(eye_d) for e in range(E)}
+    gu[E] = np.zeros((2 * I, H), np.uint16)
+    d[E] = np.zeros((H, I), np.uint16)
+    wr = bf16_bits_torch(rng.standard_normal((E, H)) * 0.02)
+    idx, gate, _ = oracle.router_topk(x, wr, K)
+    assert np.all(gate == 1.0)
+    out = oracle.cast_bf16(oracle.experts_combine(x, idx, gate, gu, d, E, 1))
+    xf = f32(x).astype(np.float64)
+    ref = bf16_bits_torch(xf[:, :I] / (1.0 + np.exp(-xf[:, :I])) * xf[:, :I])
+    assert np.mean(out[:, :I] == ref) > 0.97
+    mism = out[:, :I] != ref
+    assert np.all(np.abs(f32(out[:, :I][mism]) - f32(ref[mism])) <=
+                  np.abs(f32(ref[mism])) * 2.0 ** -7)
+    assert np.all(f32(out[:, I:]) == 0.0)
+
+
+def test_top1_identical_experts_is_a_dense_swiglu_mlp(rng):
+    H, I, E = 256, 64, 8
+    wl = W.C1
+    x = W.x_rows(wl, [0, 1])
+    wgu = W.expert_gate_up(wl, 0, 0)
+    wd = W.expert_down(wl, 0, 0)
+    gu = {e: wgu for e in range(E)}
+    d = {e: wd for e in range(E)}
+    wr = W.router(wl)[:E]
+    idx, gate, _ = oracle.router_topk(x, wr, 1)
+    acc = oracle.experts_combine(x, idx, gate, gu, d, E, 0)
+    xf, gf, df = f32(x).astype(np.float64), f32(wgu).astype(np.float64), f32(wd).astype(np.float64)
+    for m in range(2):
+        a = gf[:I] @ xf[m]
+        b = gf[I:] @ xf[m]
+        h_ref = bf16_bits_torch(a / (1 + np.exp(-a)) * b)
+        y, h = oracle.expert(x[m], wgu, wd)
+        assert np.mean(h == h_ref) > 0.98          # rare 1-ulp flips at rounding boundaries
+        hf = f32(h).astype(np.float64)
+        ref = df @ hf
+        assert np.all(np.abs(y - ref) <= gamma(I) * (np.abs(df) @ np.abs(hf)))
+        assert np.array_equal(acc[m], y)           # gate 1, no shared expert: acc = 0 + 1*y
+
+
+# ---------------------------------------------------------------- combine invariants
+
+def _tiny_layer(rng, S=1, zero_x=False, M=2):
+    wl = W.C1
+    x = np.zeros((M, wl.H), np.uint16) if zero_x else W.x_rows(wl, list(range(M)))
+    return wl, x
+
+
+def test_zero_input_gives_zero_output():
+    wl = W.C1
+    x = np.zeros((3, wl.H), np.uint16)
+    r = runner.layer(wl, x)
+    assert np.all(r["idx"] == np.arange(wl.K)[None, :])    # all logits tie at +0
+    assert np.all(r["gate"] == np.float32(1.0 / wl.K))
+    assert np.all(r["acc"] == 0.0)
+    out = runner.layer_output(wl, r)
+    assert np.all((out == 0x0000) | (out == 0x8000))
+
+
+def test_identical_routed_experts_make_output_independent_of_router(rng):
+    wl = W.C1
+    x = W.x_rows(wl, [0, 1])
+    wgu = W.expert_gate_up(wl, 0, 3)
+    wd = W.expert_down(wl, 0, 3)
+    gu = {e: wgu for e in range(wl.E)}
+    d = {e: wd for e in range(wl.E)}
+    gu[wl.E] = W.expert_gate_up(wl, 0, wl.E)
+    d[wl.E] = W.expert_down(wl, 0, wl.E)
+    outs = []
+    for K, seed_layer in ((1, 0), (2, 0), (4, 1), (8, 2)):
+        wr = W.router(wl, seed_layer)
+        idx, gate, _ = oracle.router_topk(x, wr, K)
+        outs.append(oracle.experts_combine(x, idx, gate, gu, d, wl.E, 1).astype(np.float64))
+    y_sh = np.stack([oracle.expert(x[m], gu[wl.E], d[wl.E])[0] for m in range(2)])
+    y_r = np.stack([oracle.expert(x[m], wgu, wd)[0] for m in range(2)])
+    scale = np.abs(y_sh) + np.abs(y_r)
+    for o in outs:
+        assert np.all(np.abs(o - (y_sh + y_r)) <= 24 * U32 * scale + 1e-30)
+
+
+def test_expert_permutation_with_index_remap(rng):
+    wl = W.C1
+    x = W.x_rows(wl, [0, 1, 2])
+    wr = W.router(wl)
+    gu = {e: W.expert_gate_up(wl, 0, e) for e in range(wl.E + 1)}
+    d = {e: W.expert_down(wl, 0, e) for e in range(wl.E + 1)}
+    idx, gate, _ = oracle.router_topk(x, wr, wl.K)
+    acc = oracle.experts_combine(x, idx, gate, gu, d, wl.E, 1)
+    perm = rng.permutation(wl.E)
+    wr_p = np.empty_like(wr)
+    wr_p[perm] = wr
+    gu_p = {int(perm[e]): gu[e] for e in range(wl.E)}
+    d_p = {int(perm[e]): d[e] for e in range(wl.E)}
+    gu_p[wl.E], d_p[wl.E] = gu[wl.E], d[wl.E]
+    idx_p, gate_p, _ = oracle.router_topk(x, wr_p, wl.K)
+    assert np.array_equal(idx_p, perm[idx])
+    assert np.all(np.abs(gate_p - gate) <= 4 * U32 * gate)
+    acc_p = oracle.experts_combine(x, idx_p, gate_p, gu_p, d_p, wl.E, 1)
+    # the gates may move by a few ulps (the softmax sum runs in the new index
+    # order); bound the change by the magnitude of the terms being combined
+    for m in range(3):
+        T = np.abs(oracle.expert(x[m], gu[wl.E], d[wl.E])[0]).astype(np.float64)
+        for k in range(wl.K):
+            T += gate[m, k] * np.abs(oracle.expert(x[m], gu[idx[m, k]], d[idx[m, k]])[0])
+        assert np.all(np.abs(acc_p[m] - acc[m]) <= 8 * (wl.K + 1) * U32 * T)
+
+
+def test_rows_are_independent():
+    wl = W.C1
+    x = W.x_rows(wl, list(range(6)))
+    full = runner.layer(wl, x)
+    for m in range(6):
+        one = runner.layer(wl, x[m:m + 1])
+        assert np.array_equal(one["idx"][0], full["idx"][m])
+        assert np.array_equal(one["gate"][0], full["gate"][m])
+        assert np.array_equal(one["acc"][0], full["acc"][m])
+
+
+def test_tp_shards_sum_to_full_layer():
+    from dataclasses import replace
+    full_wl = replace(W.C1, M=3, x_seed=777)
+    x = W.x_rows(full_wl, [0, 1, 2])
+    full = runner.layer(full_wl, x)
+    parts = []
+    for r in range(4):
+        sh = replace(full_wl, I=16, n_shards=4, shard=r, out_f32=True)
+        parts.append(runner.layer(sh, x)["acc"].astype(np.float64))
+        assert np.array_equal(runner.layer(sh, x)["idx"], full["idx"])
+    tot = sum(parts)
+    ref = full["acc"].astype(np.float64)
+    scale = sum(np.abs(p) for p in parts) + np.abs(ref)
+    assert np.all(np.abs(tot - ref) <= 64 * 12 * U32 * scale + 1e-9)
+
+
+def test_thread_count_does_not_change_results():
+    wl = W.C1
+    x = W.x_rows(wl, [0, 1, 2])
+    oracle.set_threads(1)
+    a = runner.layer(wl, x)
+    w = W.lmhead_rows(W.C5, 0, 3000)
+    h = W.x_rows(W.C5, [0, 1])
+    t1 = oracle.lmhead_argmax(h, w)
+    oracle.set_threads(4)
+    b = runner.layer(wl, x)
+    t4 = oracle.lmhead_argmax(h, w)
+    oracle.set_threads(os.cpu_count() or 1)
+    assert np.array_equal(a["acc"], b["acc"]) and np.array_equal(a["gate"], b["gate"])
+    assert np.array_equal(t1[0], t4[0]) and np.array_equal(t1[1], t4[1])
+
+
+# ---------------------------------------------------------------- residual chain
+
+def test_residual_rounds_once():
+    rng = np.random.default_rng(5)
+    h = bf16_bits_torch(rng.standard_normal(5000))
+    acc = (rng.standard_normal(5000) * 0.05).astype(np.float32)
+    out = oracle.residual(h, acc)
+    v = f32(h).astype(np.float64) + acc.astype(np.float64)
+    ref = bf16_bits_torch(v)
+    diff = out != ref
+    assert diff.sum() <= 3   # only where fp32 rounding of h + acc lands on a bf16 midpoint
+    assert np.array_equal(oracle.residual(h, np.zeros(5000, np.float32)), h)
+
+
+def test_chain_with_zero_weights_is_identity():
+    wl = W.C1
+    x = W.x_rows(wl, [0, 1])
+    zero_gu = {e: np.zeros((2 * wl.I, wl.H), np.uint16) for e in range(wl.E + 1)}
+    zero_d = {e: np.zeros((wl.H, wl.I), np.uint16) for e in range(wl.E + 1)}
+    h = x
+    for _ in range(3):
+        idx, gate, _ = oracle.router_topk(h, np.zeros((wl.E, wl.H), np.uint16), wl.K)
+        acc = oracle.experts_combine(h, idx, gate, zero_gu, zero_d, wl.E, 1)
+        h = oracle.residual(h, acc)
+    assert np.array_equal(h, x)
+
+
+# ---------------------------------------------------------------- lm_head argmax
+
+def test_argmax_exact_with_ties_goes_to_lowest_index(rng):
+    M, H, V = 3, 8, 50
+    hx = dyadic(rng, (M, H), lim=4)
+    w = dyadic(rng, (V, H), lim=4)
+    w[37] = w[11]           # planted exact tie: the lower index must win
+    w[11] = np.abs(w[11]) + 0.0
+    w[37] = w[11]
+    hx[:, :] = np.abs(hx)   # nonnegative h makes rows 11/37 large
+    tok, mx = oracle.lmhead_argmax(to_bf16_bits_exact(hx), to_bf16_bits_exact(w))
+    for m in range(M):
+        z = [sum(Fraction(hx[m, k]) * Fraction(w[v, k]) for k in range(H)) for v in range(V)]
+        best = max(z)
+        assert tok[m] == z.index(best) and Fraction(float(mx[m])) == best
+
+
+def test_argmax_matches_float64_when_margin_is_clear():
+    wl = W.C5
+    w = W.lmhead_rows(wl, 0, 20000)
+    h = W.x_rows(wl, [0, 1, 2, 3])
+    tok, _ = oracle.lmhead_argmax(h, w)
+    z = f32(h).astype(np.float64) @ f32(w).astype(np.float64).T
+    srt = -np.sort(-z, axis=1)
+    for m in range(4):
+        if srt[m, 0] - srt[m, 1] > 1e-3:
+            assert tok[m] == int(np.argmax(z[m]))
+
+
+# ---------------------------------------------------------------- byte counts vs the pages
+
+def test_byte_counts_match_the_numbers_the_pages_print():
+    with open(os.path.join(os.path.dirname(__file__), "golden", "page_constants.json")) as f:
+        pc = json.load(f)
+    wl = W.C2
+    assert (wl.H, wl.E, wl.S, wl.K, wl.I) == (pc["hidden_size"]["value"], pc["routed_experts"]["value"],
+                                              pc["shared_experts"]["value"], pc["top_k"]["value"],
+                                              pc["moe_intermediate_size"]["value"])
+    assert abs(wl.V if wl.V else W.C5.V - pc["vocab_approx"]["value"]) <= \
+        pc["vocab_approx"]["rel_tol"] * pc["vocab_approx"]["value"]
+    assert abs(wl.router_bytes() / 1e6 - pc["router_weight_mb_bf16"]["value"]) <= \
+        pc["router_weight_mb_bf16"]["abs_tol"]
+    # one token routed to 8 distinct experts reads about 94 MB of expert weights
+    idx = np.arange(8, dtype=np.int32)[None, :] * 3
+    b, U = oracle.unique_weight_bytes(wl.H, wl.E, wl.K, wl.I, 0, idx, include_router=False)
+    assert U == 8 and abs(b / 1e6 - pc["activated_expert_mb_per_layer"]["value"]) <= \
+        pc["activated_expert_mb_per_layer"]["abs_tol"]
+    # MoE weights of all layers on one of four ranks: about 63 GB
+    per_rank = pc["layers"]["value"] * wl.layer_bytes() / pc["tp_degree"]["value"] / 1e9
+    assert abs(per_rank / pc["weights_gb_per_rank_tp4"]["value"] - 1) <= \
+        pc["weights_gb_per_rank_tp4"]["rel_tol"]
+    # the shard's intermediate size is a quarter of 768
+    assert W.C4.I * pc["tp_degree"]["value"] == pc["moe_intermediate_size"]["value"]
+    assert W.C3.M == pc["verify_rows"]["value"] and W.C3.M <= pc["max_rows_per_tile"]["value"]
+    # full M=1 layer call: router + 8 experts + shared expert
+    b1, _ = oracle.unique_weight_bytes(wl.H, wl.E, wl.K, wl.I, 1, idx, include_router=True)
+    assert b1 == 108_789_760
