@@ -33,6 +33,7 @@ class Workload:
     shard: int = 0
     out_f32: bool = False
     residual: bool = False
+    prenorm: bool = False   # chain: each layer's MoE sees bf16(RMSNorm(h_l))
 
     @property
     def I_full(self):
@@ -56,7 +57,7 @@ C3 = Workload("ling_moe_layer_m6", 3, FAMILY_LING, H=2560, E=512, K=8, I=768, S=
 C4 = Workload("ling_tp4_shard_moe_layer_m6", 4, FAMILY_LING, H=2560, E=512, K=8, I=192, S=1,
               M=6, x_seed=404, n_shards=4, shard=0, out_f32=True)
 C5 = Workload("ling_chain16_lmhead_m6", 5, FAMILY_LING, H=2560, E=512, K=8, I=768, S=1, M=6,
-              x_seed=505, n_layers=16, V=157184, residual=True)
+              x_seed=505, n_layers=16, V=157184, residual=True, prenorm=True)
 
 ALL = (C1, C2, C3, C4, C5)
 

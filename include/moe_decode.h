@@ -1,0 +1,171 @@
+/* libmoedecode: the small-M mixture-of-experts decoder step on one AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The step, for M = 1..8 token rows (batch-1 decode and speculative verify):
+ * a bf16 router GEMV, softmax top-k with renormalised gates, a gather of the
+ * selected experts' weights, fused gate/up GEMV with SwiGLU, the down GEMV,
+ * a gate-weighted combine plus the always-on shared expert, and optionally a
+ * bf16 lm_head GEMV with greedy argmax.
+ *
+ * Sources (page titles and sections):
+ *  [LING]  "Ling-3.0-flash on 4 Blackwell GPUs" (LMSYS blog), sections
+ *          "The model", "PDL: stacking the latency floors of small kernels",
+ *          "Two fusions and a retune", "bf16 router gate and lm_head".
+ *  [LLM]   "SGLang Low-Latency Mode: Kernels and Runtime", sections
+ *          "Low-Latency-Specific Optimizations" (item 3: at most eight rows,
+ *          bitmap placement) and "AMD Low-Latency Kernels" (step-tagged values,
+ *          a deadline on every wait, routing-independent weights loaded early).
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are DEVICE pointers owned by the caller, row-major and
+ *    contiguous; bf16 travels as uint16_t bit patterns.  Weight and activation
+ *    pointers must be 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls are asynchronous on it: they never synchronise, never allocate
+ *    device memory and never print.
+ *  - All argument checks run on the host before anything is enqueued and need
+ *    no device; a call that returns an error has enqueued nothing.
+ *  - The workspace `ws` is caller-allocated device memory of at least
+ *    moe_workspace_size() bytes, zeroed once by moe_workspace_init().  It holds
+ *    step tags, counters and the values passed between workgroups; one
+ *    workspace serves one stream at a time.  Calls on one workspace that
+ *    overlap in time race.
+ *  - Device-side failures (an out-of-range expert index in caller-provided
+ *    top-k input, a wait that missed its deadline) are recorded as a sticky
+ *    status in the workspace; read it with moe_last_device_status().
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Layer shape: H hidden size, E routed experts, K experts per row, I expert
+ * intermediate size (of this call: a tensor-parallel shard passes its share),
+ * S shared experts (0 or 1).  [LING] "The model": H=2560, E=512, K=8, I=768, S=1. */
+typedef struct {
+  int32_t hidden;
+  int32_t n_experts;
+  int32_t top_k;
+  int32_t inter;
+  int32_t n_shared;
+} moe_dims;
+
+/* One layer's weights (device pointers, bf16 bits):
+ *   w_router  [E][H]
+ *   w_gate_up [E+S][2I][H]  rows [0, I) are the gate projection, rows [I, 2I) the up projection
+ *   w_down    [E+S][H][I]
+ * The shared expert, if any, is stored at expert index E. */
+typedef struct {
+  const uint16_t* w_router;
+  const uint16_t* w_gate_up;
+  const uint16_t* w_down;
+} moe_layer_weights;
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_E_ARG = -1,          /* null pointer, bad size, bad mode */
+  MOE_E_UNSUPPORTED = -2,  /* shape or option outside what the kernels cover; use a general path */
+  MOE_E_ALIGN = -3,        /* a tensor pointer is not 16-byte aligned */
+  MOE_E_WORKSPACE = -4,    /* workspace missing or smaller than moe_workspace_size() */
+  MOE_E_HIP = -5,          /* the HIP runtime reported an error (device query or launch) */
+  MOE_E_TIMEOUT = -6,      /* device: a wait passed its deadline (sticky, in the workspace) */
+  MOE_E_INDEX = -7         /* device: caller-provided expert index out of range (sticky) */
+};
+
+enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1 };
+enum { MOE_CHAIN_RESIDUAL = 0, MOE_CHAIN_LAYER_ONLY = 1, MOE_CHAIN_PRENORM_RESIDUAL = 2 };
+
+#define MOE_MAX_ROWS 8      /* [LLM] item 3: at most eight rows per tile */
+#define MOE_MAX_LAYERS 64
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 16
+
+/* Bytes of workspace needed for calls with up to `max_rows` rows and up to
+ * `n_layers` chained layers (use n_layers = 1 for the single-layer calls).
+ * Pure host computation.  Returns MOE_OK or MOE_E_ARG / MOE_E_UNSUPPORTED. */
+int moe_workspace_size(const moe_dims* dims, int32_t max_rows, int32_t n_layers, size_t* bytes);
+
+/* Zero the workspace (tags, counters, sticky status) on `stream`.  Call once
+ * after allocation, before the first call that uses it. */
+int moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Router: logits[m][e] = sum_h x[m][h] * w_router[e][h] (fp32 accumulation of
+ * bf16 products), then per row the K largest logits in descending order (equal
+ * logits: lower expert index first) and gates g_k = p_k / sum_k' p_k' with
+ * p = softmax(logits[m]) -- the renormalised top-k softmax.
+ * [LING] "PDL: stacking the latency floors of small kernels" (router chain:
+ * gate matvec then top-k) and "bf16 router gate and lm_head".
+ *   x [M][H] bf16; topk_idx [M][K] int32 (out); topk_gate [M][K] fp32 (out);
+ *   logits [M][E] fp32 (out, optional: NULL to skip). */
+int moe_router_topk(const moe_dims* dims, int32_t M, const uint16_t* x, const uint16_t* w_router,
+                    int32_t* topk_idx, float* topk_gate, float* logits, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* Experts for given routing: for each row m and selected expert e = topk_idx[m][k]
+ * (and the shared expert), a = W_gate[e] x_m, b = W_up[e] x_m (fp32),
+ * h = bf16(silu(a) * b), y = W_down[e] h (fp32); then
+ *   acc[m] = y_shared + sum_k topk_gate[m][k] * y_{topk_idx[m][k]}   (fp32)
+ * and out[m] = bf16(acc[m]) (MOE_OUT_BF16) or acc[m] unrounded (MOE_OUT_F32, the
+ * partial sum of a tensor-parallel shard).  Every selected expert is streamed
+ * from HBM once per call, whatever the number of rows that chose it.
+ * [LING] "PDL: stacking ..." (MoE chain; fp32 combine, one final cast),
+ * "Two fusions and a retune" (SwiGLU in the up-projection epilogue, silu in
+ * float, one rounding), "The model" (top-8 plus one shared expert).
+ *   x [M][H] bf16; topk_idx [M][K] int32; topk_gate [M][K] fp32 (device);
+ *   w: host struct of device pointers; out [M][H] bf16 or fp32.
+ * An index outside [0, E) is skipped and sets the sticky MOE_E_INDEX. */
+int moe_experts_fused(const moe_dims* dims, int32_t M, const uint16_t* x, const int32_t* topk_idx,
+                      const float* topk_gate, const moe_layer_weights* w, void* out,
+                      int32_t out_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* n_layers MoE layers in ONE persistent launch: per layer the router, top-k,
+ * experts and combine above, with the layer-to-layer handoff done on the device
+ * by step-tagged values instead of kernel launches ([LLM] "AMD Low-Latency
+ * Kernels": tagged stage outputs, deadlines on waits).
+ *   MOE_CHAIN_RESIDUAL:   h_0 = x_in, h_{l+1} = bf16(h_l + acc_l); out = h_L.
+ *   MOE_CHAIN_LAYER_ONLY: n_layers must be 1; out = MoE(x_in) exactly as
+ *                         moe_experts_fused would return it (bf16 or fp32).
+ *   MOE_CHAIN_PRENORM_RESIDUAL: h_{l+1} = bf16(h_l + MoE_l(u_l)) with
+ *                         u_l = bf16(h_l * r), r = 1 / sqrt(mean(h_l^2) + 1e-6)
+ *                         (RMSNorm with unit gain, the norm that opens the
+ *                         router chain in [LING] "PDL: stacking ..."); keeps
+ *                         every layer's input at unit scale.  out = h_L.
+ *   layers: host array [n_layers] of device weight pointers;
+ *   x_in [M][H] bf16; out [M][H] (bf16, or fp32 in LAYER_ONLY); out may alias x_in;
+ *   topk_idx_all [n_layers][M][K] int32 (out, optional: NULL to skip). */
+int moe_layer_chain(const moe_dims* dims, int32_t M, int32_t n_layers,
+                    const moe_layer_weights* layers, const uint16_t* x_in, void* out,
+                    int32_t out_dtype, int32_t mode, int32_t* topk_idx_all, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/* bf16 lm_head GEMV and greedy argmax: z[m][v] = sum_h h[m][h] * w_lm[v][h]
+ * (fp32 accumulation), token[m] = the smallest v with the largest z[m][v].
+ * [LING] "bf16 router gate and lm_head"; greedy decoding.
+ *   h [M][H] bf16; w_lm [V][H] bf16; token [M] int32 (out);
+ *   max_logit [M] fp32 (out, optional). */
+int lmhead_argmax(int32_t M, int32_t H, int32_t V, const uint16_t* h, const uint16_t* w_lm,
+                  int32_t* token, float* max_logit, void* ws, size_t ws_bytes, void* stream);
+
+/* Synchronise `stream`, return the sticky device status recorded in the
+ * workspace (MOE_OK, MOE_E_TIMEOUT or MOE_E_INDEX) and clear it. */
+int moe_last_device_status(void* ws, size_t ws_bytes, void* stream);
+
+/* Test hook: set the wait deadline (microseconds, 0 = default 200 ms) and
+ * debug flags (bit 0: the router never publishes its logits, so every wait on
+ * them ends at the deadline) for later calls on this workspace. */
+int moe_workspace_debug(void* ws, size_t ws_bytes, uint32_t flags, uint32_t deadline_us,
+                        void* stream);
+
+/* Static description of a status code. */
+const char* moe_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DECODE_H */

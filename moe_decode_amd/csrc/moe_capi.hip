@@ -1,0 +1,417 @@
+// C-ABI boundary of libmoedecode (declared in include/moe_decode.h).
+//
+// Every argument check runs on the host before anything is enqueued and
+// touches no device, so a rejected call has no side effect.  A specialised
+// path states its coverage and fails early outside it, leaving the caller free
+// to use a general path (SGLang Low-Latency Mode, Plugin System: guard;
+// Ling-3.0-flash on 4 Blackwell GPUs, Two fusions and a retune: the pair-axis
+// kernel's hard size gate with fallback).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/moe_decode.h"
+#include "moe_kernels.hpp"
+
+using namespace moe;
+
+static_assert(MOE_MAX_LAYERS == 64, "layer table size must match the header");
+
+namespace {
+
+constexpr size_t kHdrBytes = (size_t)HDR_WORDS * 4;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct DevInfo {
+  int num_cu = 0;
+  int max_lds = 0;
+  bool ok = false;
+};
+
+std::mutex g_mu;
+DevInfo g_dev[64];
+
+int device_info(DevInfo* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_E_HIP;
+  std::lock_guard<std::mutex> lk(g_mu);
+  DevInfo& d = g_dev[dev];
+  if (!d.ok) {
+    if (hipDeviceGetAttribute(&d.num_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return MOE_E_HIP;
+    if (hipDeviceGetAttribute(&d.max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+        hipSuccess)
+      return MOE_E_HIP;
+    d.ok = true;
+  }
+  *out = d;
+  return MOE_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Chunk plan of a row of `len` bf16 values split over `lpr` lanes, `cpl`
+// 16-byte loads per lane.
+struct RowPlan {
+  int lpr, cpl;
+};
+
+bool plan_h_rows(int H, RowPlan* rp) {
+  if (H % 256) return false;
+  rp->lpr = 32;
+  rp->cpl = H / 256;
+  return true;
+}
+
+bool plan_i_rows(int I, RowPlan* rp) {
+  if (I % 64) return false;
+  const int c = I / 8;
+  for (int lpr : {32, 16, 8}) {
+    if (c % lpr == 0) {
+      rp->lpr = lpr;
+      rp->cpl = c / lpr;
+      return true;
+    }
+  }
+  return false;
+}
+
+// Compiled (CPLH, CPLI) variants of the layer kernel.
+typedef void (*LayerKern)(Params);
+LayerKern pick_layer_kernel(int cplh, int cpli) {
+#define MOE_K(a, b) \
+  if (cplh == a && cpli == b) return moe_layer_kernel<a, b>;
+  MOE_K(1, 1) MOE_K(1, 3) MOE_K(10, 1) MOE_K(10, 3) MOE_K(10, 2) MOE_K(10, 4)
+  MOE_K(8, 3) MOE_K(4, 3) MOE_K(2, 1)
+#undef MOE_K
+  return nullptr;
+}
+
+typedef void (*LmKern)(LmParams);
+LmKern pick_lm_kernel(int cplh) {
+  switch (cplh) {
+    case 1: return moe_lmhead_kernel<1>;
+    case 2: return moe_lmhead_kernel<2>;
+    case 4: return moe_lmhead_kernel<4>;
+    case 8: return moe_lmhead_kernel<8>;
+    case 10: return moe_lmhead_kernel<10>;
+    default: return nullptr;
+  }
+}
+
+int check_dims(const moe_dims* d) {
+  if (!d) return MOE_E_ARG;
+  if (d->hidden <= 0 || d->n_experts <= 0 || d->top_k <= 0 || d->inter <= 0) return MOE_E_ARG;
+  if (d->n_shared != 0 && d->n_shared != 1) return MOE_E_ARG;
+  if (d->top_k > d->n_experts) return MOE_E_ARG;
+  if (d->n_experts > MOE_MAX_EXPERTS || d->top_k > MOE_MAX_TOPK) return MOE_E_UNSUPPORTED;
+  RowPlan a, b;
+  if (!plan_h_rows(d->hidden, &a) || !plan_i_rows(d->inter, &b)) return MOE_E_UNSUPPORTED;
+  if (d->hidden > 16384 || d->inter > 16384) return MOE_E_UNSUPPORTED;
+  return MOE_OK;
+}
+
+struct WsLayout {
+  size_t lg, hb, res, total;
+  int pmax;
+};
+
+WsLayout ws_layout(const moe_dims& d, int M, int L) {
+  WsLayout w;
+  const size_t E = (size_t)d.n_experts, H = (size_t)d.hidden, I = (size_t)d.inter;
+  w.pmax = M * (d.top_k + d.n_shared);
+  w.lg = kHdrBytes;
+  w.hb = align_up(w.lg + (size_t)L * M * E * 8, 256);
+  w.res = align_up(w.hb + (size_t)L * w.pmax * (I / 2) * 8, 256);
+  w.total = align_up(w.res + (size_t)(L + 1) * M * (H / 2) * 8, 256);
+  return w;
+}
+
+struct LdsPlan {
+  int xs, r, ys, small, total, hb_pairs, nr_max;
+};
+
+int plan_lds(const moe_dims& d, int M, int G, int max_lds, bool experts, LdsPlan* lp) {
+  const int H = d.hidden, E = d.n_experts, K = d.top_k, I = d.inter, S = d.n_shared;
+  const int pmax = M * (K + S);
+  lp->nr_max = 2 * (((H / 2) + G - 1) / G);
+  if (lp->nr_max > 64) return MOE_E_UNSUPPORTED;  // residual rows kept in LDS
+  const int umax = M * K + S;
+  lp->xs = 0;
+  const int sx = (int)align_up((size_t)M * H * 2, 16);
+  const int sy = experts ? (int)align_up((size_t)umax * lp->nr_max * M * 4, 16) : 0;
+  const int ssm = (int)align_up(sizeof(Small), 16);
+  const int slg = (int)align_up((size_t)M * E * 4, 16);
+  const int avail = max_lds - sx - sy - ssm;
+  if (avail < slg) return MOE_E_UNSUPPORTED;
+  int hb = 0;
+  if (experts) {
+    hb = avail / (I * 2);
+    if (hb > pmax) hb = pmax;
+    if (hb < M) return MOE_E_UNSUPPORTED;
+  }
+  const int sr = (int)align_up((size_t)(hb * I * 2 > slg ? hb * I * 2 : slg), 16);
+  lp->r = sx;
+  lp->ys = sx + sr;
+  lp->small = lp->ys + sy;
+  lp->total = lp->small + ssm;
+  lp->hb_pairs = hb > 0 ? hb : M;
+  return lp->total <= max_lds ? MOE_OK : MOE_E_UNSUPPORTED;
+}
+
+int launch_layer(const moe_dims& d, int M, int L, uint32_t flags, const moe_layer_weights* layers,
+                 const uint16_t* x, void* out, const int32_t* tk_in, const float* tkg_in,
+                 int32_t* tk_out, float* tkg_out, float* logits_out, void* ws, hipStream_t st) {
+  DevInfo di;
+  int rc = device_info(&di);
+  if (rc) return rc;
+  RowPlan ph, pi;
+  plan_h_rows(d.hidden, &ph);
+  plan_i_rows(d.inter, &pi);
+  LayerKern kern = pick_layer_kernel(ph.cpl, pi.cpl);
+  if (!kern) return MOE_E_UNSUPPORTED;
+  const int G = di.num_cu;
+  const bool experts = !(flags & F_ROUTER_ONLY);
+  LdsPlan lp;
+  rc = plan_lds(d, M, G, di.max_lds, experts, &lp);
+  if (rc) return rc;
+  if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          lp.total) != hipSuccess)
+    return MOE_E_HIP;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, (const void*)kern, MOE_WG, lp.total) !=
+      hipSuccess)
+    return MOE_E_HIP;
+  if (nb < 1) return MOE_E_UNSUPPORTED;  // the persistent grid would not be co-resident
+
+  const WsLayout wl = ws_layout(d, M, L);
+  Params p;
+  memset(&p, 0, sizeof(p));
+  p.H = d.hidden;
+  p.E = d.n_experts;
+  p.K = d.top_k;
+  p.I = d.inter;
+  p.S = d.n_shared;
+  p.M = M;
+  p.L = L;
+  p.flags = flags;
+  p.lpr_i = pi.lpr;
+  p.hb_pairs = lp.hb_pairs;
+  p.nr_max = lp.nr_max;
+  p.pmax = wl.pmax;
+  p.lds_xs = lp.xs;
+  p.lds_r = lp.r;
+  p.lds_ys = lp.ys;
+  p.lds_small = lp.small;
+  p.x_in = x;
+  p.out = out;
+  p.tk_idx_in = tk_in;
+  p.tk_gate_in = tkg_in;
+  p.tk_idx_out = tk_out;
+  p.tk_gate_out = tkg_out;
+  p.logits_out = logits_out;
+  unsigned char* base = (unsigned char*)ws;
+  p.hdr = (uint32_t*)base;
+  p.lg_buf = (uint64_t*)(base + wl.lg);
+  p.h_buf = (uint64_t*)(base + wl.hb);
+  p.res_buf = (uint64_t*)(base + wl.res);
+  for (int l = 0; l < L; ++l) {
+    p.lw[l].wr = layers[l].w_router;
+    p.lw[l].wgu = layers[l].w_gate_up;
+    p.lw[l].wd = layers[l].w_down;
+  }
+  hipLaunchKernelGGL(kern, dim3(G), dim3(MOE_WG), lp.total, st, p);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
+int check_ws(const moe_dims* d, int M, int L, void* ws, size_t ws_bytes) {
+  if (!ws) return MOE_E_WORKSPACE;
+  if (!aligned16(ws)) return MOE_E_ALIGN;
+  const WsLayout wl = ws_layout(*d, M, L);
+  return ws_bytes >= wl.total ? MOE_OK : MOE_E_WORKSPACE;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(int s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_E_ARG: return "invalid argument";
+    case MOE_E_UNSUPPORTED: return "unsupported shape or option";
+    case MOE_E_ALIGN: return "pointer not 16-byte aligned";
+    case MOE_E_WORKSPACE: return "workspace missing or too small";
+    case MOE_E_HIP: return "HIP runtime error";
+    case MOE_E_TIMEOUT: return "device wait passed its deadline";
+    case MOE_E_INDEX: return "expert index out of range";
+    default: return "unknown status";
+  }
+}
+
+int moe_workspace_size(const moe_dims* dims, int32_t max_rows, int32_t n_layers, size_t* bytes) {
+  if (!bytes) return MOE_E_ARG;
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (max_rows < 1 || n_layers < 1) return MOE_E_ARG;
+  if (max_rows > MOE_MAX_ROWS || n_layers > MOE_MAX_LAYERS) return MOE_E_UNSUPPORTED;
+  *bytes = ws_layout(*dims, max_rows, n_layers).total;
+  return MOE_OK;
+}
+
+int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws) return MOE_E_WORKSPACE;
+  if (!aligned16(ws)) return MOE_E_ALIGN;
+  if (ws_bytes < kHdrBytes) return MOE_E_WORKSPACE;
+  return hipMemsetAsync(ws, 0, ws_bytes, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
+int moe_router_topk(const moe_dims* dims, int32_t M, const uint16_t* x, const uint16_t* w_router,
+                    int32_t* topk_idx, float* topk_gate, float* logits, void* ws, size_t ws_bytes,
+                    void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (M < 1) return MOE_E_ARG;
+  if (M > MOE_MAX_ROWS) return MOE_E_UNSUPPORTED;
+  if (!x || !w_router || !topk_idx || !topk_gate) return MOE_E_ARG;
+  if (!aligned16(x) || !aligned16(w_router)) return MOE_E_ALIGN;
+  rc = check_ws(dims, M, 1, ws, ws_bytes);
+  if (rc) return rc;
+  moe_layer_weights lw = {w_router, nullptr, nullptr};
+  return launch_layer(*dims, M, 1, F_ROUTER_ONLY, &lw, x, nullptr, nullptr, nullptr, topk_idx,
+                      topk_gate, logits, ws, (hipStream_t)stream);
+}
+
+int moe_experts_fused(const moe_dims* dims, int32_t M, const uint16_t* x, const int32_t* topk_idx,
+                      const float* topk_gate, const moe_layer_weights* w, void* out,
+                      int32_t out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (M < 1) return MOE_E_ARG;
+  if (M > MOE_MAX_ROWS) return MOE_E_UNSUPPORTED;
+  if (!x || !topk_idx || !topk_gate || !w || !out || !w->w_gate_up || !w->w_down) return MOE_E_ARG;
+  if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return MOE_E_ARG;
+  if (!aligned16(x) || !aligned16(w->w_gate_up) || !aligned16(w->w_down) || !aligned16(out))
+    return MOE_E_ALIGN;
+  if (((uintptr_t)topk_idx & 3u) || ((uintptr_t)topk_gate & 3u)) return MOE_E_ALIGN;
+  rc = check_ws(dims, M, 1, ws, ws_bytes);
+  if (rc) return rc;
+  const size_t osz = (size_t)M * dims->hidden * (out_dtype == MOE_OUT_F32 ? 4 : 2);
+  uint32_t flags = F_TOPK_IN | (out_dtype == MOE_OUT_F32 ? F_OUT_F32 : 0u);
+  if (overlaps(out, osz, x, (size_t)M * dims->hidden * 2)) flags |= F_ALIAS;
+  moe_layer_weights lw = {nullptr, w->w_gate_up, w->w_down};
+  return launch_layer(*dims, M, 1, flags, &lw, x, out, topk_idx, topk_gate, nullptr, nullptr,
+                      nullptr, ws, (hipStream_t)stream);
+}
+
+int moe_layer_chain(const moe_dims* dims, int32_t M, int32_t n_layers,
+                    const moe_layer_weights* layers, const uint16_t* x_in, void* out,
+                    int32_t out_dtype, int32_t mode, int32_t* topk_idx_all, void* ws,
+                    size_t ws_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (M < 1 || n_layers < 1) return MOE_E_ARG;
+  if (M > MOE_MAX_ROWS || n_layers > MOE_MAX_LAYERS) return MOE_E_UNSUPPORTED;
+  if (!layers || !x_in || !out) return MOE_E_ARG;
+  if (mode != MOE_CHAIN_RESIDUAL && mode != MOE_CHAIN_LAYER_ONLY &&
+      mode != MOE_CHAIN_PRENORM_RESIDUAL)
+    return MOE_E_ARG;
+  if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return MOE_E_ARG;
+  if (mode == MOE_CHAIN_LAYER_ONLY && n_layers != 1) return MOE_E_UNSUPPORTED;
+  if (mode != MOE_CHAIN_LAYER_ONLY && out_dtype != MOE_OUT_BF16) return MOE_E_UNSUPPORTED;
+  for (int l = 0; l < n_layers; ++l) {
+    const moe_layer_weights& w = layers[l];
+    if (!w.w_router || !w.w_gate_up || !w.w_down) return MOE_E_ARG;
+    if (!aligned16(w.w_router) || !aligned16(w.w_gate_up) || !aligned16(w.w_down))
+      return MOE_E_ALIGN;
+  }
+  if (!aligned16(x_in) || !aligned16(out)) return MOE_E_ALIGN;
+  if (topk_idx_all && ((uintptr_t)topk_idx_all & 3u)) return MOE_E_ALIGN;
+  rc = check_ws(dims, M, n_layers, ws, ws_bytes);
+  if (rc) return rc;
+  uint32_t flags = 0;
+  if (mode == MOE_CHAIN_RESIDUAL) flags |= F_RESIDUAL;
+  if (mode == MOE_CHAIN_PRENORM_RESIDUAL) flags |= F_RESIDUAL | F_PRENORM;
+  if (out_dtype == MOE_OUT_F32) flags |= F_OUT_F32;
+  const size_t osz = (size_t)M * dims->hidden * (out_dtype == MOE_OUT_F32 ? 4 : 2);
+  if (overlaps(out, osz, x_in, (size_t)M * dims->hidden * 2)) flags |= F_ALIAS;
+  return launch_layer(*dims, M, n_layers, flags, layers, x_in, out, nullptr, nullptr, topk_idx_all,
+                      nullptr, nullptr, ws, (hipStream_t)stream);
+}
+
+int lmhead_argmax(int32_t M, int32_t H, int32_t V, const uint16_t* h, const uint16_t* w_lm,
+                  int32_t* token, float* max_logit, void* ws, size_t ws_bytes, void* stream) {
+  if (M < 1 || H < 1 || V < 1) return MOE_E_ARG;
+  if (M > MOE_MAX_ROWS) return MOE_E_UNSUPPORTED;
+  if (!h || !w_lm || !token) return MOE_E_ARG;
+  if (!ws) return MOE_E_WORKSPACE;
+  if (ws_bytes < kHdrBytes) return MOE_E_WORKSPACE;
+  if (!aligned16(h) || !aligned16(w_lm) || !aligned16(ws)) return MOE_E_ALIGN;
+  if (((uintptr_t)token & 3u) || (max_logit && ((uintptr_t)max_logit & 3u))) return MOE_E_ALIGN;
+  RowPlan ph;
+  if (!plan_h_rows(H, &ph)) return MOE_E_UNSUPPORTED;
+  LmKern kern = pick_lm_kernel(ph.cpl);
+  if (!kern) return MOE_E_UNSUPPORTED;
+  DevInfo di;
+  int rc = device_info(&di);
+  if (rc) return rc;
+  const int lds = (int)align_up((size_t)M * H * 2, 16) + (MOE_LM_WG / 64) * MOE_MAXM * 8;
+  if (lds > di.max_lds) return MOE_E_UNSUPPORTED;
+  if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) !=
+      hipSuccess)
+    return MOE_E_HIP;
+  LmParams p;
+  p.M = M;
+  p.H = H;
+  p.V = V;
+  p.h = h;
+  p.w = w_lm;
+  p.token = token;
+  p.max_logit = max_logit;
+  p.hdr = (uint32_t*)ws;
+  long long rows = ((long long)V + 1) / 2;
+  long long waves = rows;  // at least one row pair per wave
+  int G = di.num_cu * 4;
+  if ((long long)G * (MOE_LM_WG / 64) > waves) G = (int)((waves + (MOE_LM_WG / 64) - 1) / (MOE_LM_WG / 64));
+  if (G < 1) G = 1;
+  hipLaunchKernelGGL(kern, dim3(G), dim3(MOE_LM_WG), lds, (hipStream_t)stream, p);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
+int moe_last_device_status(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws) return MOE_E_WORKSPACE;
+  if (ws_bytes < kHdrBytes) return MOE_E_WORKSPACE;
+  if (!aligned16(ws)) return MOE_E_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  if (hipStreamSynchronize(st) != hipSuccess) return MOE_E_HIP;
+  uint32_t v = 0;
+  uint32_t* sp = (uint32_t*)ws + HDR_STATUS;
+  if (hipMemcpy(&v, sp, 4, hipMemcpyDeviceToHost) != hipSuccess) return MOE_E_HIP;
+  const uint32_t zero = 0;
+  if (hipMemcpy(sp, &zero, 4, hipMemcpyHostToDevice) != hipSuccess) return MOE_E_HIP;
+  return (int)(int32_t)v;
+}
+
+int moe_workspace_debug(void* ws, size_t ws_bytes, uint32_t flags, uint32_t deadline_us,
+                        void* stream) {
+  if (!ws) return MOE_E_WORKSPACE;
+  if (ws_bytes < kHdrBytes) return MOE_E_WORKSPACE;
+  if (!aligned16(ws)) return MOE_E_ALIGN;
+  if (deadline_us > 40000000u) return MOE_E_ARG;  // 100 MHz ticks must fit 32 bits
+  hipStream_t st = (hipStream_t)stream;
+  if (hipStreamSynchronize(st) != hipSuccess) return MOE_E_HIP;
+  const uint32_t vals[2] = {flags, deadline_us * 100u};
+  if (hipMemcpy((uint32_t*)ws + HDR_FLAGS, vals, 8, hipMemcpyHostToDevice) != hipSuccess)
+    return MOE_E_HIP;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -39,6 +39,7 @@ def lib():
         L.oracle_cast_bf16.argtypes = [_I64, _P, _P]
         L.oracle_residual.argtypes = [_I64, _P, _P, _P]
         L.oracle_lmhead_argmax.argtypes = [_I, _I, _I, _P, _P, _P, _P]
+        L.oracle_rmsnorm.argtypes = [_I, _I, _P, ctypes.c_float, _P]
         L.oracle_unique_weight_bytes.restype = _I64
         L.oracle_unique_weight_bytes.argtypes = [_I] * 6 + [_P, _I, _P]
         _lib = L
@@ -153,6 +154,17 @@ def residual(h, acc):
     out = np.empty(h.shape, dtype=np.uint16)
     lib().oracle_residual(h.size, h.ctypes.data, acc.ctypes.data, out.ctypes.data)
     return out
+
+
+RMS_EPS = 1e-6
+
+
+def rmsnorm(h, eps=RMS_EPS):
+    h = _c(h, np.uint16)
+    M, H = h.shape
+    u = np.empty_like(h)
+    lib().oracle_rmsnorm(M, H, h.ctypes.data, eps, u.ctypes.data)
+    return u
 
 
 def lmhead_argmax(h, w):

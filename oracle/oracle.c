@@ -26,7 +26,9 @@
  * Readings where the pages are silent (each listed in the design notes):
  *  gates are a full softmax over all experts' logits renormalised over the
  *  selected K; ties in selection and argmax go to the lower index; the shared
- *  expert is added with weight 1; a residual chain rounds h + acc once.
+ *  expert is added with weight 1; a residual chain rounds h + acc once; the
+ *  chain workload feeds each layer bf16(RMSNorm(h)) with unit gain (without
+ *  it the residual stream of random layers diverges within a dozen layers).
  *
  * Parity pins: every exported function is pinned by the CPU tests
  * (exact rational arithmetic on dyadic inputs, float64 bounds, brute-force
@@ -200,6 +202,25 @@ void oracle_residual(int64_t n, const uint16_t* h, const float* acc, uint16_t* o
   for (int64_t i = 0; i < n; ++i) {
     float t = bf2f(h[i]) + acc[i];
     out[i] = oracle_f32_to_bf16(t);
+  }
+}
+
+/* Pre-norm of the residual chain (reading: the router chain of "PDL: stacking
+ * ..." starts with a norm, and the chain workload feeds every layer a unit-scale
+ * input): RMSNorm with unit gain,
+ *   ss = sum_n h_n^2 (fp32, n ascending), ms = ss / H (fp32),
+ *   r = 1 / sqrt(ms + eps) (double, rounded once to fp32), u_n = bf16(h_n * r). */
+void oracle_rmsnorm(int M, int H, const uint16_t* h, float eps, uint16_t* u) {
+  for (int m = 0; m < M; ++m) {
+    const uint16_t* hr = h + (size_t)m * H;
+    float ss = 0.0f;
+    for (int n = 0; n < H; ++n) {
+      float v = bf2f(hr[n]);
+      ss = ss + v * v;
+    }
+    float ms = ss / (float)H;
+    float r = (float)(1.0 / sqrt((double)ms + (double)eps));
+    for (int n = 0; n < H; ++n) u[(size_t)m * H + n] = oracle_f32_to_bf16(bf2f(hr[n]) * r);
   }
 }
 

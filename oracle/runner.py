@@ -8,7 +8,7 @@ import numpy as np
 
 from datagen import workloads as W
 
-from . import experts_combine, lmhead_argmax, residual, router_topk, cast_bf16
+from . import experts_combine, lmhead_argmax, residual, rmsnorm, router_topk, cast_bf16
 
 
 class ExpertCache:
@@ -53,15 +53,19 @@ def layer_output(wl, res):
     return res["acc"] if wl.out_f32 else cast_bf16(res["acc"])
 
 
-def chain(wl, x, n_layers=None, keep_cache=False):
-    """Residual chain h_{l+1} = bf16(h_l + MoE_l(h_l)); returns (h_L, per-layer results)."""
+def chain(wl, x, n_layers=None, keep_cache=False, prenorm=None, routers=None):
+    """Residual chain h_{l+1} = bf16(h_l + MoE_l(u_l)) with u_l = bf16(RMSNorm(h_l)) when
+    prenorm (the chain workload), else u_l = h_l; returns (h_L, per-layer results)."""
     n_layers = wl.n_layers if n_layers is None else n_layers
+    prenorm = wl.prenorm if prenorm is None else prenorm
     h = np.ascontiguousarray(x, dtype=np.uint16)
     per = []
     cache = ExpertCache(wl)
     for l in range(n_layers):
-        r = layer(wl, h, l, cache)
+        u = rmsnorm(h) if prenorm else h
+        r = layer(wl, u, l, cache, w_router=None if routers is None else routers[l])
         r["h_in"] = h
+        r["u_in"] = u
         h = residual(h, r["acc"])
         per.append(r)
         if not keep_cache:

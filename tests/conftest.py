@@ -29,3 +29,40 @@ _ensure_built()
 def rng():
     import numpy as np
     return np.random.default_rng(12345)
+
+
+# ---------------------------------------------------------------- GPU fixtures
+
+class _DeviceWeights:
+    """Device copies of the synthetic layers, generated on the GPU once per session."""
+
+    def __init__(self):
+        self.layers = {}
+        self.lm = None
+
+    def layer(self, wl, l):
+        from datagen import device as D
+        key = (wl.family, wl.I, wl.shard, wl.n_shards, l)
+        if key not in self.layers:
+            self.layers[key] = D.make_layer(wl, l)
+        return self.layers[key]
+
+    def lmhead(self, wl):
+        from datagen import device as D
+        if self.lm is None:
+            self.lm = D.make_lmhead(wl)
+        return self.lm
+
+
+@pytest.fixture(scope="session")
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="session")
+def dw(gpu):
+    return _DeviceWeights()

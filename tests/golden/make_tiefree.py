@@ -1,0 +1,65 @@
+"""Write tiefree_rows.json: per workload, the generator attempt index of each
+input row such that the oracle's routing has no near-tie (K-th minus (K+1)-th
+logit >= DELTA at every layer) and, for the lm_head workload, no near-tie in
+the argmax (top two float64 logits DELTA apart).
+
+Calls only the oracle and the seeded generator.  Usage:
+    python tests/golden/make_tiefree.py
+"""
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
+
+import numpy as np  # noqa: E402
+
+from datagen import workloads as W  # noqa: E402
+from oracle import router_topk, runner  # noqa: E402
+
+DELTA = 1e-3
+ROWS = {W.C1.name: 8, W.C2.name: 8, W.C3.name: 6, W.C4.name: 6, W.C5.name: 6}
+
+
+def row_ok_single(wl, xrow, wr):
+    _, _, lg = router_topk(xrow[None, :], wr, wl.K)
+    return runner.router_margin(lg, wl.K)[0] >= DELTA
+
+
+def row_ok_chain(wl, xrow, routers, lm):
+    h, per = runner.chain(wl, xrow[None, :], routers=routers)
+    if any(runner.router_margin(r["logits"], wl.K)[0] < DELTA for r in per):
+        return False
+    return runner.lmhead_margin(h, lm)[0] >= DELTA
+
+
+def main():
+    out = {"delta": DELTA, "workloads": {}}
+    for wl in W.ALL:
+        n = ROWS[wl.name]
+        attempts = []
+        if wl.n_layers == 1:
+            wr = W.router(wl, 0)
+            for m in range(n):
+                a = 0
+                while not row_ok_single(wl, W.x_row(wl, m, a), wr):
+                    a += 1
+                attempts.append(a)
+        else:
+            routers = [W.router(wl, l) for l in range(wl.n_layers)]
+            lm = W.lmhead(wl)
+            for m in range(n):
+                a = 0
+                while not row_ok_chain(wl, W.x_row(wl, m, a), routers, lm):
+                    a += 1
+                attempts.append(a)
+                print(wl.name, "row", m, "attempt", a, flush=True)
+        out["workloads"][wl.name] = attempts
+        print(wl.name, attempts, flush=True)
+    with open(os.path.join(HERE, "tiefree_rows.json"), "w") as f:
+        json.dump(out, f, indent=1)
+
+
+if __name__ == "__main__":
+    main()

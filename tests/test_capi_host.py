@@ -1,0 +1,164 @@
+"""The C-ABI library on the host: it loads, exports what include/moe_decode.h
+declares, and rejects bad arguments before anything reaches a device.
+
+No call here launches a kernel: every call either is pure host arithmetic
+(moe_workspace_size, moe_status_str) or fails validation, which runs before any
+HIP call.  Fake device addresses are plain integers that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import moe_decode_amd as md
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_decode.h")
+
+A = 1 << 20          # a fake, 16-byte aligned device address
+BAD = A + 2          # misaligned
+LING = dict(hidden=2560, n_experts=512, top_k=8, inter=768, n_shared=1)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", src,
+                       flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "sizeof")))
+
+
+def test_every_declared_function_is_exported():
+    decl = declared_functions()
+    assert set(decl) == set(md.EXPORTED), decl
+    out = subprocess.run(["nm", "-D", "--defined-only", md.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if " T " in l)
+    for name in decl:
+        assert name in exported, name
+        assert hasattr(md._lib, name)
+
+
+def test_library_links_only_the_hip_runtime_it_shares_with_torch():
+    out = subprocess.run(["readelf", "-d", md.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    needed = re.findall(r"\[(.*?)\]", "\n".join(l for l in out.splitlines() if "NEEDED" in l))
+    assert any(n.startswith("libamdhip64.so") for n in needed)
+    assert not any("torch" in n or "c10" in n for n in needed)
+
+
+def test_status_strings():
+    for s in range(-7, 1):
+        assert md.moe_status_str(s) != "unknown status"
+    assert md.moe_status_str(-99) == "unknown status"
+
+
+def test_workspace_size_layout_and_errors():
+    d = md.dims(**LING)
+    rc, b1 = md.moe_workspace_size(d, 1, 1)
+    assert rc == md.MOE_OK
+    rc, b6 = md.moe_workspace_size(d, 6, 16)
+    assert rc == md.MOE_OK and b6 > b1
+
+    def up(v):
+        return (v + 255) // 256 * 256
+    M, L, E, H, I, K, S = 6, 16, 512, 2560, 768, 8, 1
+    lg = 4096
+    hb = up(lg + L * M * E * 8)
+    res = up(hb + L * M * (K + S) * (I // 2) * 8)
+    assert b6 == up(res + (L + 1) * M * (H // 2) * 8)
+    assert md.moe_workspace_size(None, 1, 1)[0] == md.MOE_E_ARG
+    assert md.moe_workspace_size(d, 0, 1)[0] == md.MOE_E_ARG
+    assert md.moe_workspace_size(d, 9, 1)[0] == md.MOE_E_UNSUPPORTED
+    assert md.moe_workspace_size(d, 1, 65)[0] == md.MOE_E_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(n_shared=2), md.MOE_E_ARG),
+    (dict(top_k=0), md.MOE_E_ARG),
+    (dict(top_k=513), md.MOE_E_ARG),
+    (dict(n_experts=2048, top_k=8), md.MOE_E_UNSUPPORTED),
+    (dict(top_k=17), md.MOE_E_UNSUPPORTED),
+    (dict(hidden=2500), md.MOE_E_UNSUPPORTED),
+    (dict(inter=100), md.MOE_E_UNSUPPORTED),
+    (dict(hidden=-256), md.MOE_E_ARG),
+])
+def test_dims_validation(kw, rc):
+    d = md.dims(**dict(LING, **kw))
+    assert md.moe_workspace_size(d, 1, 1)[0] == rc
+    assert md.moe_router_topk(d, 1, A, A, A, A, None, A, 1 << 30, stream=0) == rc
+
+
+def test_router_topk_validation():
+    d = md.dims(**LING)
+    big = 1 << 30
+    assert md.moe_router_topk(d, 0, A, A, A, A, None, A, big, stream=0) == md.MOE_E_ARG
+    assert md.moe_router_topk(d, 9, A, A, A, A, None, A, big, stream=0) == md.MOE_E_UNSUPPORTED
+    assert md.moe_router_topk(d, 1, None, A, A, A, None, A, big, stream=0) == md.MOE_E_ARG
+    assert md.moe_router_topk(d, 1, A, None, A, A, None, A, big, stream=0) == md.MOE_E_ARG
+    assert md.moe_router_topk(d, 1, A, A, None, A, None, A, big, stream=0) == md.MOE_E_ARG
+    assert md.moe_router_topk(d, 1, BAD, A, A, A, None, A, big, stream=0) == md.MOE_E_ALIGN
+    assert md.moe_router_topk(d, 1, A, BAD, A, A, None, A, big, stream=0) == md.MOE_E_ALIGN
+    assert md.moe_router_topk(d, 1, A, A, A, A, None, None, big, stream=0) == md.MOE_E_WORKSPACE
+    assert md.moe_router_topk(d, 1, A, A, A, A, None, BAD, big, stream=0) == md.MOE_E_ALIGN
+    assert md.moe_router_topk(d, 1, A, A, A, A, None, A, 4096, stream=0) == md.MOE_E_WORKSPACE
+
+
+def test_experts_fused_validation():
+    d = md.dims(**LING)
+    big = 1 << 30
+    w = md.moe_layer_weights(0, A, A)
+    f = md.moe_experts_fused
+    assert f(d, 1, A, A, A, w, A, 2, A, big, stream=0) == md.MOE_E_ARG          # bad dtype
+    assert f(d, 1, A, A, A, None, A, 0, A, big, stream=0) == md.MOE_E_ARG
+    assert f(d, 1, A, A, A, md.moe_layer_weights(0, 0, A), A, 0, A, big, stream=0) == md.MOE_E_ARG
+    assert f(d, 1, A, A, A, md.moe_layer_weights(0, BAD, A), A, 0, A, big, stream=0) == md.MOE_E_ALIGN
+    assert f(d, 1, A, A + 1, A, w, A, 0, A, big, stream=0) == md.MOE_E_ALIGN     # idx not 4-aligned
+    assert f(d, 1, A, A, A, w, BAD, 0, A, big, stream=0) == md.MOE_E_ALIGN
+    assert f(d, 1, A, A, A, w, A, 0, A, 100, stream=0) == md.MOE_E_WORKSPACE
+
+
+def test_layer_chain_validation():
+    d = md.dims(**LING)
+    big = 1 << 30
+    lw = md.moe_layer_weights(A, A, A)
+    c = md.moe_layer_chain
+    R, LO, PN = md.MOE_CHAIN_RESIDUAL, md.MOE_CHAIN_LAYER_ONLY, md.MOE_CHAIN_PRENORM_RESIDUAL
+    assert c(d, 1, [lw, lw], A, A, 0, LO, None, A, big, stream=0) == md.MOE_E_UNSUPPORTED
+    assert c(d, 1, [lw], A, A, 1, R, None, A, big, stream=0) == md.MOE_E_UNSUPPORTED
+    assert c(d, 1, [lw], A, A, 1, PN, None, A, big, stream=0) == md.MOE_E_UNSUPPORTED
+    assert c(d, 1, [lw], A, A, 0, 7, None, A, big, stream=0) == md.MOE_E_ARG
+    assert c(d, 1, [], A, A, 0, R, None, A, big, stream=0) == md.MOE_E_ARG
+    assert c(d, 1, [lw] * 65, A, A, 0, R, None, A, big, stream=0) == md.MOE_E_UNSUPPORTED
+    assert c(d, 1, [md.moe_layer_weights(A, 0, A)], A, A, 0, R, None, A, big,
+             stream=0) == md.MOE_E_ARG
+    assert c(d, 1, [md.moe_layer_weights(BAD, A, A)], A, A, 0, R, None, A, big,
+             stream=0) == md.MOE_E_ALIGN
+    assert c(d, 1, [lw], A, A, 0, R, A + 2, A, big, stream=0) == md.MOE_E_ALIGN
+    rc, need = md.moe_workspace_size(d, 6, 16)
+    assert c(d, 6, [lw] * 16, A, A, 0, R, None, A, need - 256, stream=0) == md.MOE_E_WORKSPACE
+
+
+def test_lmhead_validation():
+    f = md.lmhead_argmax
+    big = 1 << 30
+    assert f(0, 2560, 100, A, A, A, None, A, big, stream=0) == md.MOE_E_ARG
+    assert f(9, 2560, 100, A, A, A, None, A, big, stream=0) == md.MOE_E_UNSUPPORTED
+    assert f(1, 2560, 0, A, A, A, None, A, big, stream=0) == md.MOE_E_ARG
+    assert f(1, 2560, 100, None, A, A, None, A, big, stream=0) == md.MOE_E_ARG
+    assert f(1, 2560, 100, A, A, A, None, None, big, stream=0) == md.MOE_E_WORKSPACE
+    assert f(1, 2560, 100, A, A, A, None, A, 100, stream=0) == md.MOE_E_WORKSPACE
+    assert f(1, 2560, 100, BAD, A, A, None, A, big, stream=0) == md.MOE_E_ALIGN
+    assert f(1, 2500, 100, A, A, A, None, A, big, stream=0) == md.MOE_E_UNSUPPORTED
+
+
+def test_workspace_calls_validate_before_touching_the_device():
+    assert md.moe_workspace_init(None, 1 << 20, stream=0) == md.MOE_E_WORKSPACE
+    assert md.moe_workspace_init(BAD, 1 << 20, stream=0) == md.MOE_E_ALIGN
+    assert md.moe_workspace_init(A, 16, stream=0) == md.MOE_E_WORKSPACE
+    assert md.moe_last_device_status(None, 1 << 20, stream=0) == md.MOE_E_WORKSPACE
+    assert md.moe_workspace_debug(A, 0, 16, stream=0, ws_bytes=16) == md.MOE_E_WORKSPACE
+    assert md.moe_workspace_debug(A, 0, 50_000_000, ws_bytes=1 << 20,
+                                  stream=0) == md.MOE_E_ARG

@@ -1,0 +1,382 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: expert indices and argmax tokens bit-exact (inputs are tie-free: the
+oracle's K-th and (K+1)-th logits, and its top two lm_head logits, are at
+least 1e-3 apart); bf16 outputs within a norm-wise relative error of 1e-2
+(max |gpu - oracle| / max |oracle|); fp32 partial outputs within 1e-3 of the
+same norm; logits within twice the fp32 summation bound of either order.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import moe_decode_amd as md
+import oracle
+from oracle import runner
+from datagen import workloads as W
+from datagen import device as D
+
+from gpu_support import (f32, frac_beyond_one_ulp, order_agrees, rel_err_normwise, same_sets,
+                         say, tiefree_attempts, x_tiefree)
+
+pytestmark = pytest.mark.gpu
+
+U32 = 2.0 ** -24
+
+
+def _dims(wl, **kw):
+    a = dict(hidden=wl.H, n_experts=wl.E, top_k=wl.K, inter=wl.I, n_shared=wl.S)
+    a.update(kw)
+    return md.dims(**a)
+
+
+def _lw(L):
+    return md.layer_weights(L.w_router, L.w_gate_up, L.w_down)
+
+
+def _empty(shape, dtype, dev):
+    import torch
+    return torch.empty(shape, dtype=dtype, device=dev)
+
+
+def _layer_gpu(wl, dw, gpu, x, ws=None, out_f32=None):
+    """One layer through moe_layer_chain(LAYER_ONLY): returns (idx [M][K], out)."""
+    import torch
+    M = x.shape[0]
+    d = _dims(wl)
+    L = dw.layer(wl, 0)
+    ws = md.new_workspace(d, M, 1) if ws is None else ws
+    out_f32 = wl.out_f32 if out_f32 is None else out_f32
+    out = _empty((M, wl.H), torch.float32 if out_f32 else torch.int16, gpu)
+    idx = _empty((M, wl.K), torch.int32, gpu)
+    say("layer_chain LAYER_ONLY %s M=%d" % (wl.name, M))
+    md.check(md.moe_layer_chain(d, M, [_lw(L)], D.to_device(x), out,
+                                md.MOE_OUT_F32 if out_f32 else md.MOE_OUT_BF16,
+                                md.MOE_CHAIN_LAYER_ONLY, idx, ws))
+    md.check(md.moe_last_device_status(ws))
+    o = out.cpu().numpy()
+    return idx.cpu().numpy(), (o if out_f32 else o.view(np.uint16))
+
+
+def _check_layer(wl, x, idx_g, out_g):
+    ref = runner.layer(wl, x)
+    assert same_sets(idx_g, ref["idx"]), (idx_g, ref["idx"])
+    assert order_agrees(idx_g, ref["idx"], ref["logits"])
+    if wl.out_f32:
+        err = rel_err_normwise(out_g, ref["acc"])
+        assert err <= 1e-3, err
+    else:
+        ref_out = runner.layer_output(wl, ref)
+        err = rel_err_normwise(f32(out_g), f32(ref_out))
+        assert err <= 1e-2, err
+        assert frac_beyond_one_ulp(out_g, ref_out) <= 0.01
+    return err
+
+
+# ------------------------------------------------------------------ generator
+
+def test_device_generator_matches_host(gpu, dw):
+    say("datagen device vs host")
+    for wl in (W.C1, W.C3, W.C4):
+        L = dw.layer(wl, 0)
+        e = 7 if wl.E > 7 else 0
+        assert np.array_equal(D.from_device_bf16(L.w_router), W.router(wl, 0))
+        assert np.array_equal(D.from_device_bf16(L.w_gate_up[e]), W.expert_gate_up(wl, 0, e))
+        assert np.array_equal(D.from_device_bf16(L.w_down[wl.E]), W.expert_down(wl, 0, wl.E))
+
+
+# ------------------------------------------------------------------ router
+
+@pytest.mark.parametrize("wl,M", [(W.C1, 1), (W.C1, 5), (W.C1, 8), (W.C2, 1), (W.C3, 6),
+                                  (W.C2, 8)])
+def test_router_topk(gpu, dw, wl, M):
+    import torch
+    x = x_tiefree(wl, M)
+    d = _dims(wl)
+    L = dw.layer(wl, 0)
+    ws = md.new_workspace(d, M, 1)
+    idx = _empty((M, wl.K), torch.int32, gpu)
+    gate = _empty((M, wl.K), torch.float32, gpu)
+    lg = _empty((M, wl.E), torch.float32, gpu)
+    say("router_topk %s M=%d" % (wl.name, M))
+    md.check(md.moe_router_topk(d, M, D.to_device(x), L.w_router, idx, gate, lg, ws))
+    md.check(md.moe_last_device_status(ws))
+    ri, rg, rl = oracle.router_topk(x, W.router(wl, 0), wl.K)
+    gi, gg, gl = idx.cpu().numpy(), gate.cpu().numpy(), lg.cpu().numpy()
+    xf, wf = f32(x).astype(np.float64), f32(W.router(wl, 0)).astype(np.float64)
+    bound = 2 * wl.H * U32 * (np.abs(xf) @ np.abs(wf).T)
+    assert np.all(np.abs(gl.astype(np.float64) - rl) <= bound + 1e-30)
+    assert np.array_equal(gi, ri) or (same_sets(gi, ri) and order_agrees(gi, ri, rl))
+    for m in range(M):
+        ref = dict(zip(ri[m], rg[m]))
+        for k in range(wl.K):
+            assert abs(gg[m, k] - ref[gi[m, k]]) <= 1e-5 * ref[gi[m, k]]
+        assert abs(gg[m].astype(np.float64).sum() - 1.0) <= 1e-6
+
+
+def test_router_exact_on_dyadic_inputs(gpu):
+    """Dyadic inputs make every partial sum exact: logits must match bit for bit."""
+    import torch
+    rng = np.random.default_rng(3)
+    H, E, K, M = 256, 16, 2, 3
+    x = (rng.integers(-8, 9, (M, H)) / 8.0)
+    w = (rng.integers(-8, 9, (E, H)) / 8.0)
+    xb = oracle.f32_to_bf16(x.astype(np.float32)).reshape(M, H)
+    wb = oracle.f32_to_bf16(w.astype(np.float32)).reshape(E, H)
+    d = md.dims(H, E, K, 64, 0)
+    ws = md.new_workspace(d, M, 1)
+    idx = _empty((M, K), torch.int32, gpu)
+    gate = _empty((M, K), torch.float32, gpu)
+    lg = _empty((M, E), torch.float32, gpu)
+    say("router_topk dyadic exact")
+    md.check(md.moe_router_topk(d, M, D.to_device(xb), D.to_device(wb), idx, gate, lg, ws))
+    ri, _, rl = oracle.router_topk(xb, wb, K)
+    assert np.array_equal(lg.cpu().numpy(), rl)
+    assert np.array_equal(idx.cpu().numpy(), ri)   # exact logits: ties resolved identically
+
+
+# ------------------------------------------------------------------ one layer
+
+@pytest.mark.parametrize("M", [1, 2, 3, 6, 8])
+def test_layer_tiny_all_row_counts(gpu, dw, M):
+    wl = W.C1
+    x = x_tiefree(wl, M)
+    idx, out = _layer_gpu(wl, dw, gpu, x)
+    _check_layer(wl, x, idx, out)
+
+
+def test_layer_ling_m1(gpu, dw):
+    wl = W.C2
+    x = x_tiefree(wl, 1)
+    idx, out = _layer_gpu(wl, dw, gpu, x)
+    _check_layer(wl, x, idx, out)
+
+
+def test_layer_ling_m6(gpu, dw):
+    wl = W.C3
+    x = x_tiefree(wl, 6)
+    idx, out = _layer_gpu(wl, dw, gpu, x)
+    _check_layer(wl, x, idx, out)
+
+
+def test_layer_ling_max_rows(gpu, dw):
+    wl = replace(W.C2, M=8)
+    x = x_tiefree(W.C2, 8)
+    idx, out = _layer_gpu(wl, dw, gpu, x)
+    _check_layer(wl, x, idx, out)
+
+
+def test_layer_tp4_shard_fp32_partial(gpu, dw):
+    wl = W.C4
+    x = x_tiefree(wl, 6)
+    idx, out = _layer_gpu(wl, dw, gpu, x)
+    _check_layer(wl, x, idx, out)
+
+
+def test_zero_input_routes_to_lowest_indices(gpu, dw):
+    wl = W.C1
+    x = np.zeros((2, wl.H), np.uint16)
+    idx, out = _layer_gpu(wl, dw, gpu, x)
+    assert np.array_equal(idx, np.tile(np.arange(wl.K, dtype=np.int32), (2, 1)))
+    assert np.all((out == 0) | (out == 0x8000))
+
+
+def test_no_shared_expert(gpu, dw):
+    wl = replace(W.C1, S=0)
+    x = x_tiefree(W.C1, 3)
+    import torch
+    d = _dims(wl)
+    L = dw.layer(W.C1, 0)
+    ws = md.new_workspace(d, 3, 1)
+    out = _empty((3, wl.H), torch.int16, gpu)
+    idx = _empty((3, wl.K), torch.int32, gpu)
+    say("layer_chain no shared expert")
+    md.check(md.moe_layer_chain(d, 3, [_lw(L)], D.to_device(x), out, md.MOE_OUT_BF16,
+                                md.MOE_CHAIN_LAYER_ONLY, idx, ws))
+    ref = runner.layer(wl, x)
+    assert same_sets(idx.cpu().numpy(), ref["idx"])
+    err = rel_err_normwise(f32(out.cpu().numpy().view(np.uint16)),
+                           f32(runner.layer_output(wl, ref)))
+    assert err <= 1e-2
+
+
+# ------------------------------------------------------------------ experts only
+
+def _experts_gpu(wl, dw, gpu, x, idx, gate, out_f32=False, ws=None):
+    import torch
+    M = x.shape[0]
+    d = _dims(wl)
+    L = dw.layer(wl, 0)
+    ws = md.new_workspace(d, M, 1) if ws is None else ws
+    out = _empty((M, wl.H), torch.float32 if out_f32 else torch.int16, gpu)
+    say("experts_fused %s M=%d" % (wl.name, M))
+    rc = md.moe_experts_fused(d, M, D.to_device(x), D.to_device(idx.astype(np.int32)),
+                              D.to_device(gate.astype(np.float32)),
+                              md.layer_weights(None, L.w_gate_up, L.w_down), out,
+                              md.MOE_OUT_F32 if out_f32 else md.MOE_OUT_BF16, ws)
+    md.check(rc)
+    st = md.moe_last_device_status(ws)
+    o = out.cpu().numpy()
+    return st, (o if out_f32 else o.view(np.uint16))
+
+
+@pytest.mark.parametrize("wl", [W.C3, W.C4])
+def test_experts_fused_with_oracle_routing(gpu, dw, wl):
+    x = x_tiefree(wl, 6)
+    ref = runner.layer(wl, x)
+    st, out = _experts_gpu(wl, dw, gpu, x, ref["idx"], ref["gate"], out_f32=wl.out_f32)
+    assert st == md.MOE_OK
+    if wl.out_f32:
+        assert rel_err_normwise(out, ref["acc"]) <= 1e-3
+    else:
+        assert rel_err_normwise(f32(out), f32(runner.layer_output(wl, ref))) <= 1e-2
+
+
+def test_experts_fused_duplicate_and_invalid_indices(gpu, dw):
+    wl = W.C1
+    x = x_tiefree(wl, 3)
+    idx = np.array([[3, 3], [5, 9], [0, 15]], np.int32)          # a duplicate in row 0
+    gate = np.array([[0.25, 0.75], [0.6, 0.4], [0.5, 0.5]], np.float32)
+    gu = {e: W.expert_gate_up(wl, 0, e) for e in range(wl.E + 1)}
+    dn = {e: W.expert_down(wl, 0, e) for e in range(wl.E + 1)}
+    ref = oracle.experts_combine(x, idx, gate, gu, dn, wl.E, 1)
+    st, out = _experts_gpu(wl, dw, gpu, x, idx, gate, out_f32=True)
+    assert st == md.MOE_OK
+    assert rel_err_normwise(out, ref) <= 1e-3
+    # an out-of-range index is skipped and reported
+    bad = idx.copy()
+    bad[1, 1] = wl.E
+    ref_skip = oracle.experts_combine(x[1:2], bad[1:2, :1], gate[1:2, :1], gu, dn, wl.E, 1)
+    st, out = _experts_gpu(wl, dw, gpu, x, bad, gate, out_f32=True)
+    assert st == md.MOE_E_INDEX
+    assert rel_err_normwise(out[1:2], ref_skip) <= 1e-3
+
+
+# ------------------------------------------------------------------ chains
+
+def _chain_gpu(wl, dw, gpu, x, n_layers, mode, ws=None, inplace=False):
+    import torch
+    M = x.shape[0]
+    d = _dims(wl)
+    layers = [_lw(dw.layer(wl, l)) for l in range(n_layers)]
+    ws = md.new_workspace(d, M, n_layers) if ws is None else ws
+    xin = D.to_device(x)
+    out = xin if inplace else _empty((M, wl.H), torch.int16, gpu)
+    idx = _empty((n_layers, M, wl.K), torch.int32, gpu)
+    say("layer_chain mode=%d %s L=%d M=%d inplace=%s" % (mode, wl.name, n_layers, M, inplace))
+    md.check(md.moe_layer_chain(d, M, layers, xin, out, md.MOE_OUT_BF16, mode, idx, ws))
+    md.check(md.moe_last_device_status(ws))
+    return idx.cpu().numpy(), out.cpu().numpy().view(np.uint16)
+
+
+def test_chain_residual_tiny(gpu, dw):
+    wl = W.C1
+    x = x_tiefree(wl, 4)
+    idx, h = _chain_gpu(wl, dw, gpu, x, 3, md.MOE_CHAIN_RESIDUAL)
+    href, per = runner.chain(wl, x, n_layers=3, prenorm=False)
+    for l in range(3):
+        assert same_sets(idx[l], per[l]["idx"]), l
+    assert rel_err_normwise(f32(h), f32(href)) <= 1e-2
+
+
+def test_chain_prenorm_tiny_inplace_matches_out_of_place(gpu, dw):
+    wl = W.C1
+    x = x_tiefree(wl, 8)
+    idx_a, h_a = _chain_gpu(wl, dw, gpu, x, 4, md.MOE_CHAIN_PRENORM_RESIDUAL)
+    idx_b, h_b = _chain_gpu(wl, dw, gpu, x, 4, md.MOE_CHAIN_PRENORM_RESIDUAL, inplace=True)
+    assert np.array_equal(idx_a, idx_b) and np.array_equal(h_a, h_b)
+    href, per = runner.chain(wl, x, n_layers=4, prenorm=True)
+    for l in range(4):
+        assert same_sets(idx_a[l], per[l]["idx"]), l
+    assert rel_err_normwise(f32(h_a), f32(href)) <= 1e-2
+
+
+def test_chain16_lmhead_full_size(gpu, dw):
+    """The 16-layer Ling chain at M=6 with the pre-norm residual, then the
+    157184-row lm_head argmax: every layer's expert sets and the tokens exact."""
+    import torch
+    wl = W.C5
+    x = x_tiefree(wl, 6)
+    idx, h = _chain_gpu(wl, dw, gpu, x, wl.n_layers, md.MOE_CHAIN_PRENORM_RESIDUAL)
+    routers = [W.router(wl, l) for l in range(wl.n_layers)]
+    href, per = runner.chain(wl, x, routers=routers)
+    for l in range(wl.n_layers):
+        assert same_sets(idx[l], per[l]["idx"]), l
+    assert rel_err_normwise(f32(h), f32(href)) <= 1e-2
+    lm = dw.lmhead(wl)
+    ws = md.new_workspace(_dims(wl), 6, 1)
+    tok = _empty((6,), torch.int32, gpu)
+    mx = _empty((6,), torch.float32, gpu)
+    say("lmhead_argmax V=%d M=6 on the chain output" % wl.V)
+    md.check(md.lmhead_argmax(6, wl.H, wl.V, D.to_device(href), lm, tok, mx, ws))
+    t_ref, m_ref = oracle.lmhead_argmax(href, D.from_device_bf16(lm))
+    assert np.array_equal(tok.cpu().numpy(), t_ref)
+    assert np.all(np.abs(mx.cpu().numpy() - m_ref) <= 1e-4 * np.abs(m_ref) + 1e-5)
+
+
+# ------------------------------------------------------------------ lm_head
+
+@pytest.mark.parametrize("M,V", [(1, 1), (3, 4097), (8, 20000)])
+def test_lmhead_ragged_and_planted_ties(gpu, M, V):
+    import torch
+    wl = W.C5
+    h = W.x_rows(wl, list(range(M)))
+    w = W.lmhead_rows(wl, 0, V).copy()
+    if V > 10:
+        z = f32(h[0]).astype(np.float64) @ f32(w).astype(np.float64).T
+        best = int(np.argmax(z))
+        w[V - 1] = w[best]          # exact duplicate of row 0's winner at a higher index
+    dev_w = D.to_device(w)
+    ws = md.new_workspace(_dims(wl), M, 1)
+    tok = _empty((M,), torch.int32, gpu)
+    mx = _empty((M,), torch.float32, gpu)
+    say("lmhead_argmax M=%d V=%d" % (M, V))
+    md.check(md.lmhead_argmax(M, wl.H, V, D.to_device(h), dev_w, tok, mx, ws))
+    t_ref, m_ref = oracle.lmhead_argmax(h, w)
+    zf = f32(h).astype(np.float64) @ f32(w).astype(np.float64).T
+    srt = -np.sort(-zf, axis=1)
+    got = tok.cpu().numpy()
+    for m in range(M):
+        if V == 1 or srt[m, 0] - srt[m, 1] >= 1e-4 or (m == 0 and V > 10):
+            assert got[m] == t_ref[m], (m, got[m], t_ref[m])
+    # a second call on the same workspace sees freshly reset argmax keys
+    md.check(md.lmhead_argmax(M, wl.H, V, D.to_device(h), dev_w, tok, mx, ws))
+    assert np.array_equal(tok.cpu().numpy(), got)
+
+
+# ------------------------------------------------------------------ workspace state
+
+def test_state_is_clean_across_calls_and_call_types(gpu, dw):
+    """Re-running after other calls on the same workspace gives bit-identical
+    results (no stale tags, counters or argmax keys leak between calls)."""
+    wl = W.C3
+    x = x_tiefree(wl, 6)
+    d = _dims(wl)
+    ws = md.new_workspace(d, 8, 16)
+    idx1, out1 = _layer_gpu(wl, dw, gpu, x, ws=ws)
+    _layer_gpu(W.C2, dw, gpu, x_tiefree(W.C2, 1), ws=ws)
+    _chain_gpu(wl, dw, gpu, x[:2], 3, md.MOE_CHAIN_PRENORM_RESIDUAL, ws=ws)
+    idx2, out2 = _layer_gpu(wl, dw, gpu, x, ws=ws)
+    assert np.array_equal(idx1, idx2) and np.array_equal(out1, out2)
+
+
+def test_missed_deadline_is_reported_and_recovers(gpu, dw):
+    """Force every wait to miss its deadline from the host (the router never
+    publishes; 2 ms budget): the call ends, reports MOE_E_TIMEOUT, and the next
+    normal call on the same workspace is correct."""
+    wl = W.C1
+    x = x_tiefree(wl, 2)
+    d = _dims(wl)
+    ws = md.new_workspace(d, 2, 1)
+    md.check(md.moe_workspace_debug(ws, md.DBG_NO_ROUTER_PUBLISH, 2000))
+    say("forced deadline miss (router unpublished, 2 ms)")
+    import torch
+    out = _empty((2, wl.H), torch.int16, gpu)
+    md.check(md.moe_layer_chain(d, 2, [_lw(dw.layer(wl, 0))], D.to_device(x), out,
+                                md.MOE_OUT_BF16, md.MOE_CHAIN_LAYER_ONLY, None, ws))
+    assert md.moe_last_device_status(ws) == md.MOE_E_TIMEOUT
+    assert md.moe_last_device_status(ws) == md.MOE_OK       # read clears it
+    md.check(md.moe_workspace_debug(ws, 0, 0))
+    idx, out = _layer_gpu(wl, dw, gpu, x, ws=ws)
+    _check_layer(wl, x, idx, out)
