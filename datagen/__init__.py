@@ -47,9 +47,12 @@ def _host_lib():
 def _dev_lib():
     global _dev
     if _dev is None:
+        import torch  # noqa: F401  (bind to torch's HIP runtime, see moe_decode_amd)
         if not os.path.exists(DEV_SO):
             raise RuntimeError("libdg_device.so is not built; run __graft_entry__.build()")
         lib = ctypes.CDLL(DEV_SO)
+        lib.dg_error_string.restype = ctypes.c_char_p
+        lib.dg_error_string.argtypes = [ctypes.c_int]
         lib.dg_fill_bf16_dev.restype = ctypes.c_int
         lib.dg_fill_bf16_dev.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int] + \
             [ctypes.c_int64] * 6 + [ctypes.c_float, ctypes.c_void_p]
@@ -88,4 +91,5 @@ def fill_device(out_ptr, keys_dev_ptr, n_blocks, block_stride, rows, cols, sigma
     rc = _dev_lib().dg_fill_bf16_dev(out_ptr, keys_dev_ptr, n_blocks, block_stride, row0, col0,
                                      rows, cols, ld_full, scale_for(sigma), stream)
     if rc != 0:
-        raise RuntimeError("dg_fill_bf16_dev failed (%d)" % rc)
+        raise RuntimeError("dg_fill_bf16_dev failed (%d: %s)"
+                           % (rc, _dev_lib().dg_error_string(rc).decode()))

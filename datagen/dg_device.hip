@@ -27,10 +27,19 @@ extern "C" int dg_fill_bf16_dev(uint16_t* out, const uint64_t* keys_dev, int n_b
                                 int64_t cols, int64_t ld_full, float scale, void* stream) {
   if (n_blocks <= 0 || rows <= 0 || cols <= 0) return 0;
   if (n_blocks > 65535) return -1;
+  const hipError_t before = hipGetLastError();  // an error left by an earlier call
+  if (before != hipSuccess) return -(2000 + (int)before);
   const int threads = 256;
   int64_t per = (rows * cols + threads - 1) / threads;
   int gx = (int)(per < 4096 ? per : 4096);
   hipLaunchKernelGGL(dg_fill_kernel, dim3(gx, n_blocks), dim3(threads), 0, (hipStream_t)stream,
                      out, keys_dev, block_stride, row0, col0, rows, cols, ld_full, scale);
-  return hipGetLastError() == hipSuccess ? 0 : -5;
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? 0 : -(1000 + (int)e);
+}
+
+extern "C" const char* dg_error_string(int code) {
+  int e = -code;
+  if (e >= 2000) e -= 2000; else if (e >= 1000) e -= 1000;
+  return hipGetErrorString((hipError_t)e);
 }

@@ -131,17 +131,19 @@ int moe_experts_fused(const moe_dims* dims, int32_t M, const uint16_t* x, const 
  *   MOE_CHAIN_LAYER_ONLY: n_layers must be 1; out = MoE(x_in) exactly as
  *                         moe_experts_fused would return it (bf16 or fp32).
  *   MOE_CHAIN_PRENORM_RESIDUAL: h_{l+1} = bf16(h_l + MoE_l(u_l)) with
- *                         u_l = bf16(h_l * r), r = 1 / sqrt(mean(h_l^2) + 1e-6)
- *                         (RMSNorm with unit gain, the norm that opens the
+ *                         u_l = bf16(h_l * r), r = fp32(1 / sqrt(mean(h_l^2) + 1e-6)),
+ *                         the mean of squares summed in double (RMSNorm with unit gain, the norm that opens the
  *                         router chain in [LING] "PDL: stacking ..."); keeps
  *                         every layer's input at unit scale.  out = h_L.
  *   layers: host array [n_layers] of device weight pointers;
  *   x_in [M][H] bf16; out [M][H] (bf16, or fp32 in LAYER_ONLY); out may alias x_in;
- *   topk_idx_all [n_layers][M][K] int32 (out, optional: NULL to skip). */
+ *   topk_idx_all [n_layers][M][K] int32 (out, optional: NULL to skip);
+ *   h_all [n_layers+1][M][H] bf16 (out, optional, residual modes only): h_all[0] = x_in,
+ *         h_all[l+1] = the residual stream after layer l; must not overlap x_in. */
 int moe_layer_chain(const moe_dims* dims, int32_t M, int32_t n_layers,
                     const moe_layer_weights* layers, const uint16_t* x_in, void* out,
-                    int32_t out_dtype, int32_t mode, int32_t* topk_idx_all, void* ws,
-                    size_t ws_bytes, void* stream);
+                    int32_t out_dtype, int32_t mode, int32_t* topk_idx_all, uint16_t* h_all,
+                    void* ws, size_t ws_bytes, void* stream);
 
 /* bf16 lm_head GEMV and greedy argmax: z[m][v] = sum_h h[m][h] * w_lm[v][h]
  * (fp32 accumulation), token[m] = the smallest v with the largest z[m][v].

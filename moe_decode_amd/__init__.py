@@ -11,6 +11,12 @@ integer address, or None (NULL).
 import ctypes
 import os
 
+# The library must bind to the HIP runtime that owns the caller's device
+# memory and streams.  torch ships its own libamdhip64 with the same soname;
+# loading torch first makes the dynamic linker reuse that one instead of
+# pulling a second runtime from the system path.
+import torch  # noqa: F401
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoedecode.so")
 
@@ -72,7 +78,7 @@ _lib.moe_experts_fused.argtypes = [ctypes.POINTER(moe_dims), _I32, _P, _P, _P,
 _lib.moe_layer_chain.restype = ctypes.c_int
 _lib.moe_layer_chain.argtypes = [ctypes.POINTER(moe_dims), _I32, _I32,
                                  ctypes.POINTER(moe_layer_weights), _P, _P, _I32, _I32, _P, _P,
-                                 _SZ, _P]
+                                 _P, _SZ, _P]
 _lib.lmhead_argmax.restype = ctypes.c_int
 _lib.lmhead_argmax.argtypes = [_I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.moe_last_device_status.restype = ctypes.c_int
@@ -162,7 +168,7 @@ def moe_experts_fused(d, M, x, topk_idx, topk_gate, w, out, out_dtype, ws, ws_by
 
 
 def moe_layer_chain(d, M, layers, x_in, out, out_dtype, mode, topk_idx_all, ws, ws_bytes=None,
-                    stream=None):
+                    stream=None, h_all=None):
     """layers: a sequence of moe_layer_weights (or None)."""
     if layers is None:
         arr, n = None, 0
@@ -170,8 +176,8 @@ def moe_layer_chain(d, M, layers, x_in, out, out_dtype, mode, topk_idx_all, ws, 
         n = len(layers)
         arr = (moe_layer_weights * max(n, 1))(*layers)
     return _lib.moe_layer_chain(ctypes.byref(d) if d is not None else None, M, n, arr, _ptr(x_in),
-                                _ptr(out), out_dtype, mode, _ptr(topk_idx_all), _ptr(ws),
-                                _nbytes(ws, ws_bytes), _stream(stream))
+                                _ptr(out), out_dtype, mode, _ptr(topk_idx_all), _ptr(h_all),
+                                _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream))
 
 
 def lmhead_argmax(M, H, V, h, w_lm, token, max_logit, ws, ws_bytes=None, stream=None):

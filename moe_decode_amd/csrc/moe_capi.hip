@@ -164,7 +164,8 @@ int plan_lds(const moe_dims& d, int M, int G, int max_lds, bool experts, LdsPlan
 
 int launch_layer(const moe_dims& d, int M, int L, uint32_t flags, const moe_layer_weights* layers,
                  const uint16_t* x, void* out, const int32_t* tk_in, const float* tkg_in,
-                 int32_t* tk_out, float* tkg_out, float* logits_out, void* ws, hipStream_t st) {
+                 int32_t* tk_out, float* tkg_out, float* logits_out, uint16_t* h_all, void* ws,
+                 hipStream_t st) {
   DevInfo di;
   int rc = device_info(&di);
   if (rc) return rc;
@@ -213,6 +214,7 @@ int launch_layer(const moe_dims& d, int M, int L, uint32_t flags, const moe_laye
   p.tk_idx_out = tk_out;
   p.tk_gate_out = tkg_out;
   p.logits_out = logits_out;
+  p.h_all = h_all;
   unsigned char* base = (unsigned char*)ws;
   p.hdr = (uint32_t*)base;
   p.lg_buf = (uint64_t*)(base + wl.lg);
@@ -287,7 +289,7 @@ int moe_router_topk(const moe_dims* dims, int32_t M, const uint16_t* x, const ui
   if (rc) return rc;
   moe_layer_weights lw = {w_router, nullptr, nullptr};
   return launch_layer(*dims, M, 1, F_ROUTER_ONLY, &lw, x, nullptr, nullptr, nullptr, topk_idx,
-                      topk_gate, logits, ws, (hipStream_t)stream);
+                      topk_gate, logits, nullptr, ws, (hipStream_t)stream);
 }
 
 int moe_experts_fused(const moe_dims* dims, int32_t M, const uint16_t* x, const int32_t* topk_idx,
@@ -309,13 +311,13 @@ int moe_experts_fused(const moe_dims* dims, int32_t M, const uint16_t* x, const 
   if (overlaps(out, osz, x, (size_t)M * dims->hidden * 2)) flags |= F_ALIAS;
   moe_layer_weights lw = {nullptr, w->w_gate_up, w->w_down};
   return launch_layer(*dims, M, 1, flags, &lw, x, out, topk_idx, topk_gate, nullptr, nullptr,
-                      nullptr, ws, (hipStream_t)stream);
+                      nullptr, nullptr, ws, (hipStream_t)stream);
 }
 
 int moe_layer_chain(const moe_dims* dims, int32_t M, int32_t n_layers,
                     const moe_layer_weights* layers, const uint16_t* x_in, void* out,
-                    int32_t out_dtype, int32_t mode, int32_t* topk_idx_all, void* ws,
-                    size_t ws_bytes, void* stream) {
+                    int32_t out_dtype, int32_t mode, int32_t* topk_idx_all, uint16_t* h_all,
+                    void* ws, size_t ws_bytes, void* stream) {
   int rc = check_dims(dims);
   if (rc) return rc;
   if (M < 1 || n_layers < 1) return MOE_E_ARG;
@@ -335,6 +337,11 @@ int moe_layer_chain(const moe_dims* dims, int32_t M, int32_t n_layers,
   }
   if (!aligned16(x_in) || !aligned16(out)) return MOE_E_ALIGN;
   if (topk_idx_all && ((uintptr_t)topk_idx_all & 3u)) return MOE_E_ALIGN;
+  if (h_all && mode == MOE_CHAIN_LAYER_ONLY) return MOE_E_ARG;
+  if (h_all && !aligned16(h_all)) return MOE_E_ALIGN;
+  if (h_all && (overlaps(h_all, (size_t)(n_layers + 1) * M * dims->hidden * 2, x_in,
+                         (size_t)M * dims->hidden * 2)))
+    return MOE_E_ARG;
   rc = check_ws(dims, M, n_layers, ws, ws_bytes);
   if (rc) return rc;
   uint32_t flags = 0;
@@ -344,7 +351,7 @@ int moe_layer_chain(const moe_dims* dims, int32_t M, int32_t n_layers,
   const size_t osz = (size_t)M * dims->hidden * (out_dtype == MOE_OUT_F32 ? 4 : 2);
   if (overlaps(out, osz, x_in, (size_t)M * dims->hidden * 2)) flags |= F_ALIAS;
   return launch_layer(*dims, M, n_layers, flags, layers, x_in, out, nullptr, nullptr, topk_idx_all,
-                      nullptr, nullptr, ws, (hipStream_t)stream);
+                      nullptr, nullptr, h_all, ws, (hipStream_t)stream);
 }
 
 int lmhead_argmax(int32_t M, int32_t H, int32_t V, const uint16_t* h, const uint16_t* w_lm,

@@ -69,6 +69,7 @@ struct Params {
   const int32_t* tk_idx_in;
   const float* tk_gate_in;
   int32_t* tk_idx_out;   // [L][M][K] (or [M][K])
+  uint16_t* h_all;       // [L+1][M][H] residual stream per layer (optional)
   float* tk_gate_out;    // [M][K]
   float* logits_out;     // [M][E]
   uint32_t* hdr;
@@ -339,16 +340,26 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(Params p) {
         sm->hres[m * p.nr_max + nl] = xs[m * H + n0 + nl];
       }
     }
+    if (l == 0 && g == 0 && p.h_all) {
+      uint4* dst = reinterpret_cast<uint4*>(p.h_all);
+      for (int i = tid; i < (M * H) >> 3; i += MOE_WG) dst[i] = xs4[i];
+    }
     if (p.flags & F_PRENORM) {
-      // sum of squares per row: exact bf16 squares accumulated in fp32
+      // Sum of squares per row in double: every bf16 square is exact in fp32 and,
+      // over the value range of a residual stream, every partial sum is exact in
+      // double, so the sum (and the scale) does not depend on the order.
+      const uint32_t* xr32 = reinterpret_cast<const uint32_t*>(xs);
       for (int m = wv; m < M; m += MOE_WAVES) {
-        float ss = 0.0f;
-        for (int c = lane; c < (H >> 3); c += 64) {
-          const uint4 v = xs4[m * (H >> 3) + c];
-          ss = dot8(v, v, ss);
+        double ss = 0.0;
+        for (int c = lane; c < H2; c += 64) {
+          const uint32_t w = xr32[m * H2 + c];
+          const float a = bf_lo(w), b = bf_hi(w);
+          ss += (double)(a * a);
+          ss += (double)(b * b);
         }
-        ss = group_sum(ss, 64);
-        if (lane == 0) sm->rn[m] = 1.0f / sqrtf(ss / (float)H + kRmsEps);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+        if (lane == 0) sm->rn[m] = (float)(1.0 / sqrt(ss / (double)H + (double)kRmsEps));
       }
       __syncthreads();
       uint32_t* x32 = reinterpret_cast<uint32_t*>(xs);
@@ -521,6 +532,9 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(Params p) {
           reinterpret_cast<uint32_t*>(p.out)[(m * H + n) >> 1] = word;
         else
           st_tag(p.res_buf + (size_t)(l + 1) * M * H2 + ((m * H + n) >> 1), word, tag);
+        if (p.h_all)
+          reinterpret_cast<uint32_t*>(p.h_all)[((size_t)(l + 1) * M * H + (size_t)m * H + n) >> 1] =
+              word;
       } else if (p.flags & F_OUT_F32) {
         reinterpret_cast<float2*>(p.out)[(m * H + n) >> 1] = make_float2(acc[0], acc[1]);
       } else {

@@ -208,18 +208,20 @@ void oracle_residual(int64_t n, const uint16_t* h, const float* acc, uint16_t* o
 /* Pre-norm of the residual chain (reading: the router chain of "PDL: stacking
  * ..." starts with a norm, and the chain workload feeds every layer a unit-scale
  * input): RMSNorm with unit gain,
- *   ss = sum_n h_n^2 (fp32, n ascending), ms = ss / H (fp32),
- *   r = 1 / sqrt(ms + eps) (double, rounded once to fp32), u_n = bf16(h_n * r). */
+ *   ss = sum_n h_n^2 accumulated in double (each square of a bf16 value is exact,
+ *        and for the chain's value range so is every partial sum, so ss is the
+ *        exact sum whatever the order),
+ *   r = 1 / sqrt(ss / H + eps) in double, rounded once to fp32,
+ *   u_n = bf16(h_n * r) with the product in fp32. */
 void oracle_rmsnorm(int M, int H, const uint16_t* h, float eps, uint16_t* u) {
   for (int m = 0; m < M; ++m) {
     const uint16_t* hr = h + (size_t)m * H;
-    float ss = 0.0f;
+    double ss = 0.0;
     for (int n = 0; n < H; ++n) {
-      float v = bf2f(hr[n]);
+      double v = (double)bf2f(hr[n]);
       ss = ss + v * v;
     }
-    float ms = ss / (float)H;
-    float r = (float)(1.0 / sqrt((double)ms + (double)eps));
+    float r = (float)(1.0 / sqrt(ss / (double)H + (double)eps));
     for (int n = 0; n < H; ++n) u[(size_t)m * H + n] = oracle_f32_to_bf16(bf2f(hr[n]) * r);
   }
 }

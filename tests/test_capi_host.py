@@ -162,3 +162,14 @@ def test_workspace_calls_validate_before_touching_the_device():
     assert md.moe_workspace_debug(A, 0, 16, stream=0, ws_bytes=16) == md.MOE_E_WORKSPACE
     assert md.moe_workspace_debug(A, 0, 50_000_000, ws_bytes=1 << 20,
                                   stream=0) == md.MOE_E_ARG
+
+
+def test_one_hip_runtime_per_process():
+    """Importing the binding first must not pull in a second HIP runtime."""
+    code = ("import moe_decode_amd, datagen, torch\n"
+            "datagen._dev_lib()\n"
+            "m = open('/proc/self/maps').read()\n"
+            "print(len(set(l.split()[-1] for l in m.splitlines() if 'libamdhip64' in l)))\n")
+    out = subprocess.run(["python", "-c", code], capture_output=True, text=True, cwd=ROOT,
+                         check=True).stdout
+    assert out.strip() == "1"

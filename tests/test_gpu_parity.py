@@ -254,6 +254,15 @@ def test_experts_fused_duplicate_and_invalid_indices(gpu, dw):
 
 
 # ------------------------------------------------------------------ chains
+#
+# A chain of layers amplifies legitimate rounding differences (one bf16 flip
+# in an expert's SwiGLU output shifts that expert's whole output vector), so
+# the GPU chain is not compared with a free-running oracle chain.  Instead the
+# chain exports its residual stream h_l per layer and every layer's decisions
+# are checked against the oracle run on the GPU's own input to that layer
+# (teacher forcing): expert sets exactly wherever the K-th/(K+1)-th margin on
+# that input is >= 1e-3, validity of the choice below that, the layer output
+# within the bf16 bar.
 
 def _chain_gpu(wl, dw, gpu, x, n_layers, mode, ws=None, inplace=False):
     import torch
@@ -264,54 +273,91 @@ def _chain_gpu(wl, dw, gpu, x, n_layers, mode, ws=None, inplace=False):
     xin = D.to_device(x)
     out = xin if inplace else _empty((M, wl.H), torch.int16, gpu)
     idx = _empty((n_layers, M, wl.K), torch.int32, gpu)
+    h_all = None if inplace else _empty((n_layers + 1, M, wl.H), torch.int16, gpu)
     say("layer_chain mode=%d %s L=%d M=%d inplace=%s" % (mode, wl.name, n_layers, M, inplace))
-    md.check(md.moe_layer_chain(d, M, layers, xin, out, md.MOE_OUT_BF16, mode, idx, ws))
+    md.check(md.moe_layer_chain(d, M, layers, xin, out, md.MOE_OUT_BF16, mode, idx, ws,
+                                h_all=h_all))
     md.check(md.moe_last_device_status(ws))
-    return idx.cpu().numpy(), out.cpu().numpy().view(np.uint16)
+    hs = None if h_all is None else h_all.cpu().numpy().view(np.uint16)
+    return idx.cpu().numpy(), out.cpu().numpy().view(np.uint16), hs
+
+
+def _valid_selection(sel, logits, K, tol=1e-3):
+    """A selection is valid if it holds every expert clearly above the K-th logit
+    and only experts within tol of it."""
+    srt = -np.sort(-logits.astype(np.float64))
+    kth = srt[K - 1]
+    must = set(np.nonzero(logits > kth + tol)[0].tolist())
+    may = set(np.nonzero(logits >= kth - tol)[0].tolist())
+    s = set(int(e) for e in sel)
+    return len(s) == K and must <= s <= may
+
+
+def _check_chain_teacher_forced(wl, x, idx, out, hs, n_layers, prenorm, routers=None):
+    assert np.array_equal(hs[0], x)
+    assert np.array_equal(hs[n_layers], out)
+    cache = runner.ExpertCache(wl)
+    exact = 0
+    for l in range(n_layers):
+        u = oracle.rmsnorm(hs[l]) if prenorm else hs[l]
+        r = runner.layer(wl, u, l, cache, w_router=None if routers is None else routers[l])
+        marg = runner.router_margin(r["logits"], wl.K)
+        clear = marg >= 1e-3
+        for m in range(x.shape[0]):
+            if clear[m]:
+                assert set(idx[l, m]) == set(r["idx"][m]), (l, m)
+                exact += 1
+            else:
+                assert _valid_selection(idx[l, m], r["logits"][m], wl.K), (l, m)
+        ref_next = oracle.residual(hs[l], r["acc"])
+        rows = np.nonzero(clear)[0]
+        err = rel_err_normwise(f32(hs[l + 1][rows]), f32(ref_next[rows]))
+        assert err <= 1e-2, (l, err)
+        cache.drop_layer(l)
+    return exact
 
 
 def test_chain_residual_tiny(gpu, dw):
     wl = W.C1
     x = x_tiefree(wl, 4)
-    idx, h = _chain_gpu(wl, dw, gpu, x, 3, md.MOE_CHAIN_RESIDUAL)
-    href, per = runner.chain(wl, x, n_layers=3, prenorm=False)
-    for l in range(3):
-        assert same_sets(idx[l], per[l]["idx"]), l
-    assert rel_err_normwise(f32(h), f32(href)) <= 1e-2
+    idx, h, hs = _chain_gpu(wl, dw, gpu, x, 3, md.MOE_CHAIN_RESIDUAL)
+    assert _check_chain_teacher_forced(wl, x, idx, h, hs, 3, prenorm=False) == 12
 
 
 def test_chain_prenorm_tiny_inplace_matches_out_of_place(gpu, dw):
     wl = W.C1
     x = x_tiefree(wl, 8)
-    idx_a, h_a = _chain_gpu(wl, dw, gpu, x, 4, md.MOE_CHAIN_PRENORM_RESIDUAL)
-    idx_b, h_b = _chain_gpu(wl, dw, gpu, x, 4, md.MOE_CHAIN_PRENORM_RESIDUAL, inplace=True)
+    idx_a, h_a, hs = _chain_gpu(wl, dw, gpu, x, 4, md.MOE_CHAIN_PRENORM_RESIDUAL)
+    idx_b, h_b, _ = _chain_gpu(wl, dw, gpu, x, 4, md.MOE_CHAIN_PRENORM_RESIDUAL, inplace=True)
     assert np.array_equal(idx_a, idx_b) and np.array_equal(h_a, h_b)
-    href, per = runner.chain(wl, x, n_layers=4, prenorm=True)
-    for l in range(4):
-        assert same_sets(idx_a[l], per[l]["idx"]), l
-    assert rel_err_normwise(f32(h_a), f32(href)) <= 1e-2
+    assert _check_chain_teacher_forced(wl, x, idx_a, h_a, hs, 4, prenorm=True) >= 30
 
 
 def test_chain16_lmhead_full_size(gpu, dw):
     """The 16-layer Ling chain at M=6 with the pre-norm residual, then the
-    157184-row lm_head argmax: every layer's expert sets and the tokens exact."""
+    157184-row lm_head argmax on its output: teacher-forced per-layer parity,
+    and the tokens exactly the oracle's argmax of the GPU's final hidden state."""
     import torch
     wl = W.C5
     x = x_tiefree(wl, 6)
-    idx, h = _chain_gpu(wl, dw, gpu, x, wl.n_layers, md.MOE_CHAIN_PRENORM_RESIDUAL)
+    idx, h, hs = _chain_gpu(wl, dw, gpu, x, wl.n_layers, md.MOE_CHAIN_PRENORM_RESIDUAL)
     routers = [W.router(wl, l) for l in range(wl.n_layers)]
-    href, per = runner.chain(wl, x, routers=routers)
-    for l in range(wl.n_layers):
-        assert same_sets(idx[l], per[l]["idx"]), l
-    assert rel_err_normwise(f32(h), f32(href)) <= 1e-2
+    exact = _check_chain_teacher_forced(wl, x, idx, h, hs, wl.n_layers, prenorm=True,
+                                        routers=routers)
+    assert exact >= 0.9 * wl.n_layers * 6
     lm = dw.lmhead(wl)
     ws = md.new_workspace(_dims(wl), 6, 1)
     tok = _empty((6,), torch.int32, gpu)
     mx = _empty((6,), torch.float32, gpu)
     say("lmhead_argmax V=%d M=6 on the chain output" % wl.V)
-    md.check(md.lmhead_argmax(6, wl.H, wl.V, D.to_device(href), lm, tok, mx, ws))
-    t_ref, m_ref = oracle.lmhead_argmax(href, D.from_device_bf16(lm))
-    assert np.array_equal(tok.cpu().numpy(), t_ref)
+    md.check(md.lmhead_argmax(6, wl.H, wl.V, D.to_device(h), lm, tok, mx, ws))
+    w_host = D.from_device_bf16(lm)
+    t_ref, m_ref = oracle.lmhead_argmax(h, w_host)
+    marg = runner.lmhead_margin(h, w_host)
+    got = tok.cpu().numpy()
+    for m in range(6):
+        if marg[m] >= 1e-4:
+            assert got[m] == t_ref[m], (m, got[m], t_ref[m])
     assert np.all(np.abs(mx.cpu().numpy() - m_ref) <= 1e-4 * np.abs(m_ref) + 1e-5)
 
 

@@ -375,6 +375,28 @@ def test_residual_rounds_once():
     assert np.array_equal(oracle.residual(h, np.zeros(5000, np.float32)), h)
 
 
+def test_rmsnorm_scale_is_the_correctly_rounded_exact_value():
+    """r must be the fp32 rounding of 1/sqrt(exact mean square + eps), and u = bf16(h * r)."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 50
+    rng = np.random.default_rng(11)
+    H = 2560
+    h = bf16_bits_torch(rng.standard_normal((4, H)) * 1.7)
+    u = oracle.rmsnorm(h)
+    hf = f32(h).astype(np.float64)
+    for m in range(4):
+        ss = sum(Fraction(float(v)) ** 2 for v in hf[m])
+        ms = Decimal(ss.numerator) / Decimal(ss.denominator) / H + Decimal(oracle.RMS_EPS)
+        r = np.float32(float(1 / ms.sqrt()))
+        ref = bf16_bits_torch((f32(h[m]) * r).astype(np.float64))   # fp32 product, then bf16
+        assert np.array_equal(u[m], ref)
+    # unit mean square after the norm; a constant row maps to (about) +-1
+    uf = f32(u).astype(np.float64)
+    assert np.all(np.abs((uf ** 2).mean(1) - 1) < 0.01)
+    c = bf16_bits_torch(np.full((2, 256), [[1.0], [-3.0]]))
+    assert np.all(f32(oracle.rmsnorm(c)) == np.array([[1.0], [-1.0]], np.float32))
+
+
 def test_chain_with_zero_weights_is_identity():
     wl = W.C1
     x = W.x_rows(wl, [0, 1])
