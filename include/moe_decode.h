@@ -157,9 +157,18 @@ int lmhead_argmax(int32_t M, int32_t H, int32_t V, const uint16_t* h, const uint
  * workspace (MOE_OK, MOE_E_TIMEOUT or MOE_E_INDEX) and clear it. */
 int moe_last_device_status(void* ws, size_t ws_bytes, void* stream);
 
-/* Test hook: set the wait deadline (microseconds, 0 = default 200 ms) and
- * debug flags (bit 0: the router never publishes its logits, so every wait on
- * them ends at the deadline) for later calls on this workspace. */
+/* Test and measurement hook: set the wait deadline (microseconds, 0 = default
+ * 200 ms) and debug flags for later calls on this workspace.
+ *   bit 0: the router never publishes its logits, so every wait on them ends at
+ *          the deadline (exercises the timeout path);
+ *   bit 1: phase stamps.  The fused kernel records the 100 MHz global clock at
+ *          its phase boundaries into the workspace at byte offset 4096, as
+ *          uint64 [256 workgroups][32 slots]: slots 10*s + e for layer slot
+ *          s (0: first layer, 1: second, 2: last) and event e (0 layer start,
+ *          1 input staged, 2 router and shared gate/up rows done, 3 logits
+ *          received, 4 top-k and union built, 5 routed gate/up done, 6 first h
+ *          group staged, 7 down projection done, 8 combine done); slot 31 is
+ *          the end of the call. */
 int moe_workspace_debug(void* ws, size_t ws_bytes, uint32_t flags, uint32_t deadline_us,
                         void* stream);
 

@@ -13,7 +13,8 @@
 #include <mutex>
 
 #include "../../include/moe_decode.h"
-#include "moe_kernels.hpp"
+#include "moe_layer.hpp"
+#include "moe_lmhead.hpp"
 
 using namespace moe;
 
@@ -21,7 +22,7 @@ static_assert(MOE_MAX_LAYERS == 64, "layer table size must match the header");
 
 namespace {
 
-constexpr size_t kHdrBytes = (size_t)HDR_WORDS * 4;
+constexpr size_t kHdrBytes = (size_t)HDR_BYTES;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -66,26 +67,28 @@ bool plan_h_rows(int H, RowPlan* rp) {
   return true;
 }
 
+// Down-projection rows are split over 8 lanes each (I/64 loads per lane);
+// several 8-row blocks go in flight together when rows are short.
 bool plan_i_rows(int I, RowPlan* rp) {
   if (I % 64) return false;
-  const int c = I / 8;
-  for (int lpr : {32, 16, 8}) {
-    if (c % lpr == 0) {
-      rp->lpr = lpr;
-      rp->cpl = c / lpr;
-      return true;
-    }
-  }
-  return false;
+  rp->lpr = 8;
+  rp->cpl = I / 64;
+  return true;
 }
 
-// Compiled (CPLH, CPLI) variants of the layer kernel.
+int down_blocks(int cpli) {
+  const int b = 10 / cpli;
+  return b < 1 ? 1 : (b > 4 ? 4 : b);
+}
+
+// Compiled (CPLH, CPLI) variants of the layer kernel: hidden size 256 * CPLH,
+// intermediate size 64 * CPLI.
 typedef void (*LayerKern)(Params);
 LayerKern pick_layer_kernel(int cplh, int cpli) {
 #define MOE_K(a, b) \
-  if (cplh == a && cpli == b) return moe_layer_kernel<a, b>;
-  MOE_K(1, 1) MOE_K(1, 3) MOE_K(10, 1) MOE_K(10, 3) MOE_K(10, 2) MOE_K(10, 4)
-  MOE_K(8, 3) MOE_K(4, 3) MOE_K(2, 1)
+  if (cplh == a && cpli == b) return moe_layer_kernel<a, b, (10 / b < 1 ? 1 : (10 / b > 4 ? 4 : 10 / b))>;
+  MOE_K(1, 1) MOE_K(10, 12) MOE_K(10, 3) MOE_K(10, 1) MOE_K(10, 4) MOE_K(8, 12) MOE_K(8, 3)
+  MOE_K(4, 4) MOE_K(2, 2)
 #undef MOE_K
   return nullptr;
 }
@@ -114,52 +117,56 @@ int check_dims(const moe_dims* d) {
   return MOE_OK;
 }
 
+// Workspace regions after the header (all tagged 64-bit words):
+//   lg  [L][M][E]        router logits
+//   hs  [L][M][I/2]      shared expert SwiGLU output (bf16 pairs)
+//   hr  [L][M*K][I/2]    routed (expert, row) SwiGLU outputs (bf16 pairs)
+//   y   [L][M*K][H]      routed (expert, row) down-projection outputs (fp32)
+//   res [L+1][M][H/2]    residual stream between chained layers (bf16 pairs)
 struct WsLayout {
-  size_t lg, hb, res, total;
-  int pmax;
+  size_t lg, hs, hr, y, res, total;
 };
 
 WsLayout ws_layout(const moe_dims& d, int M, int L) {
   WsLayout w;
   const size_t E = (size_t)d.n_experts, H = (size_t)d.hidden, I = (size_t)d.inter;
-  w.pmax = M * (d.top_k + d.n_shared);
+  const size_t MK = (size_t)M * d.top_k;
   w.lg = kHdrBytes;
-  w.hb = align_up(w.lg + (size_t)L * M * E * 8, 256);
-  w.res = align_up(w.hb + (size_t)L * w.pmax * (I / 2) * 8, 256);
+  w.hs = align_up(w.lg + (size_t)L * M * E * 8, 256);
+  w.hr = align_up(w.hs + (size_t)L * M * (I / 2) * 8, 256);
+  w.y = align_up(w.hr + (size_t)L * MK * (I / 2) * 8, 256);
+  w.res = align_up(w.y + (size_t)L * MK * H * 8, 256);
   w.total = align_up(w.res + (size_t)(L + 1) * M * (H / 2) * 8, 256);
   return w;
 }
 
 struct LdsPlan {
-  int xs, r, ys, small, total, hb_pairs, nr_max;
+  int xs, lg, hs, ysh, ysr, small, total, nr_max;
 };
 
-int plan_lds(const moe_dims& d, int M, int G, int max_lds, bool experts, LdsPlan* lp) {
-  const int H = d.hidden, E = d.n_experts, K = d.top_k, I = d.inter, S = d.n_shared;
-  const int pmax = M * (K + S);
+// LDS of the layer kernel: x [M][H] bf16, logits [M][E] fp32, the SwiGLU rows
+// of the shared expert and of up to two routed slice pieces [3][M][I] bf16, the shared expert's outputs for the owned rows
+// [M][nr_max] fp32, the routed (expert, row) outputs of the owned rows
+// [M*K][nr_max] fp32, and the small tables.
+int plan_lds(const moe_dims& d, int M, int G, int max_lds, LdsPlan* lp) {
+  const int H = d.hidden, E = d.n_experts, I = d.inter;
   lp->nr_max = 2 * (((H / 2) + G - 1) / G);
   if (lp->nr_max > 64) return MOE_E_UNSUPPORTED;  // residual rows kept in LDS
-  const int umax = M * K + S;
-  lp->xs = 0;
-  const int sx = (int)align_up((size_t)M * H * 2, 16);
-  const int sy = experts ? (int)align_up((size_t)umax * lp->nr_max * M * 4, 16) : 0;
-  const int ssm = (int)align_up(sizeof(Small), 16);
-  const int slg = (int)align_up((size_t)M * E * 4, 16);
-  const int avail = max_lds - sx - sy - ssm;
-  if (avail < slg) return MOE_E_UNSUPPORTED;
-  int hb = 0;
-  if (experts) {
-    hb = avail / (I * 2);
-    if (hb > pmax) hb = pmax;
-    if (hb < M) return MOE_E_UNSUPPORTED;
-  }
-  const int sr = (int)align_up((size_t)(hb * I * 2 > slg ? hb * I * 2 : slg), 16);
-  lp->r = sx;
-  lp->ys = sx + sr;
-  lp->small = lp->ys + sy;
-  lp->total = lp->small + ssm;
-  lp->hb_pairs = hb > 0 ? hb : M;
-  return lp->total <= max_lds ? MOE_OK : MOE_E_UNSUPPORTED;
+  size_t o = 0;
+  lp->xs = (int)o;
+  o = align_up(o + (size_t)M * H * 2, 16);
+  lp->lg = (int)o;
+  o = align_up(o + (size_t)M * E * 4, 16);
+  lp->hs = (int)o;  // SwiGLU rows of the down tasks: shared | first piece | second piece
+  o = align_up(o + (size_t)3 * M * I * 2, 16);
+  lp->ysh = (int)o;
+  o = align_up(o + (size_t)M * lp->nr_max * 4, 16);
+  lp->ysr = (int)o;
+  o = align_up(o + (size_t)M * d.top_k * lp->nr_max * 4, 16);
+  lp->small = (int)o;
+  o = align_up(o + sizeof(Small), 16);
+  lp->total = (int)o;
+  return o <= (size_t)max_lds ? MOE_OK : MOE_E_UNSUPPORTED;
 }
 
 int launch_layer(const moe_dims& d, int M, int L, uint32_t flags, const moe_layer_weights* layers,
@@ -175,9 +182,8 @@ int launch_layer(const moe_dims& d, int M, int L, uint32_t flags, const moe_laye
   LayerKern kern = pick_layer_kernel(ph.cpl, pi.cpl);
   if (!kern) return MOE_E_UNSUPPORTED;
   const int G = di.num_cu;
-  const bool experts = !(flags & F_ROUTER_ONLY);
   LdsPlan lp;
-  rc = plan_lds(d, M, G, di.max_lds, experts, &lp);
+  rc = plan_lds(d, M, G, di.max_lds, &lp);
   if (rc) return rc;
   if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                           lp.total) != hipSuccess)
@@ -199,13 +205,12 @@ int launch_layer(const moe_dims& d, int M, int L, uint32_t flags, const moe_laye
   p.M = M;
   p.L = L;
   p.flags = flags;
-  p.lpr_i = pi.lpr;
-  p.hb_pairs = lp.hb_pairs;
   p.nr_max = lp.nr_max;
-  p.pmax = wl.pmax;
   p.lds_xs = lp.xs;
-  p.lds_r = lp.r;
-  p.lds_ys = lp.ys;
+  p.lds_lg = lp.lg;
+  p.lds_hs = lp.hs;
+  p.lds_ysh = lp.ysh;
+  p.lds_ysr = lp.ysr;
   p.lds_small = lp.small;
   p.x_in = x;
   p.out = out;
@@ -218,7 +223,9 @@ int launch_layer(const moe_dims& d, int M, int L, uint32_t flags, const moe_laye
   unsigned char* base = (unsigned char*)ws;
   p.hdr = (uint32_t*)base;
   p.lg_buf = (uint64_t*)(base + wl.lg);
-  p.h_buf = (uint64_t*)(base + wl.hb);
+  p.hs_buf = (uint64_t*)(base + wl.hs);
+  p.hr_buf = (uint64_t*)(base + wl.hr);
+  p.y_buf = (uint64_t*)(base + wl.y);
   p.res_buf = (uint64_t*)(base + wl.res);
   for (int l = 0; l < L; ++l) {
     p.lw[l].wr = layers[l].w_router;

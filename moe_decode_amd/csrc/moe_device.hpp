@@ -32,10 +32,14 @@ enum : int {
   HDR_DEADLINE = 129,   // wait budget in 100 MHz ticks (0 = default)
   HDR_LM_DONE = 160,    // lm_head: workgroups finished
   HDR_LM_KEYS = 192,    // lm_head: MOE_MAXM packed (logit, index) keys, u64 each
-  HDR_WORDS = 1024      // header size: 4 KiB
+  HDR_WORDS = 1024,     // control words: 4 KiB
+  HDR_STAMPS = 1024,    // phase stamps: [256 workgroups][32] u64 after the control words
+  STAMP_WG = 256,
+  STAMP_SLOTS = 32,
+  HDR_BYTES = HDR_WORDS * 4 + STAMP_WG * STAMP_SLOTS * 8
 };
 
-enum : uint32_t { DBG_NO_ROUTER_PUBLISH = 1u };
+enum : uint32_t { DBG_NO_ROUTER_PUBLISH = 1u, DBG_STAMPS = 2u };
 
 constexpr uint32_t kDefaultDeadlineTicks = 20000000u;  // 200 ms at 100 MHz
 
@@ -105,16 +109,18 @@ __device__ __forceinline__ float group_sum(float v, int lpr) {
   return v;
 }
 
-// Wave-wide maximum of an unsigned key; the result is wave-uniform.
+// Wave-wide maximum of an unsigned key; the result is wave-uniform.  All in
+// DPP (quad swaps, half-row and row mirrors, then the row broadcasts that
+// carry row 0 into row 1, row 2 into row 3 and rows 0-1 into rows 2-3), so lane
+// 63 ends with the maximum; one readlane makes it uniform.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, dpp_u<0xB1>(v));
   v = max(v, dpp_u<0x4E>(v));
   v = max(v, dpp_u<0x141>(v));
   v = max(v, dpp_u<0x140>(v));
-  v = max(v, swz16_u(v));
-  uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
-  uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
-  return max(a, b);
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Order-preserving map of an fp32 value to an unsigned key (-0 maps as +0).

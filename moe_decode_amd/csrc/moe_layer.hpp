@@ -1,0 +1,901 @@
+// The fused MoE layer / chain kernel for gfx950.
+//
+// One persistent launch runs one or several MoE layers; one workgroup per CU,
+// all resident for the whole call.  Per layer:
+//
+//   P0  stage the layer input x [M][H] in LDS (layer 0 from the caller's
+//       buffer, later layers from step-tagged residual words); under the
+//       pre-norm chain keep this workgroup's rows of h_l for the residual and
+//       replace x by bf16(RMSNorm(h_l)).
+//   P1  router GEMV rows and the shared expert's gate/up rows, spread over every
+//       wave of the GPU.  The shared expert does not depend on routing, so its
+//       weights stream while the logits travel ("weights that do not depend on
+//       routing load before their inputs arrive", SGLang Low-Latency Mode, AMD
+//       Low-Latency Kernels).  Logits and the shared expert's SwiGLU output are
+//       published as step-tagged words.
+//   P4  every workgroup reads all logits and computes the softmax top-k
+//       itself, so no second device-wide hop is needed.
+//   P5  union of the rows' choices: a bitmap over experts plus population
+//       counts gives each selected expert its slot with no scan over experts or
+//       sort (SGLang Low-Latency Mode, item 3: at most eight rows).
+//   P6  routed experts, in teams: the routed work (every expert's gate/up rows
+//       plus its down rows, the same amount per expert) is laid on a line and
+//       cut into one equal slice per workgroup.  A slice covers a fraction of at
+//       most two experts; for each it computes the matching share of the
+//       intermediate dimension (gate/up GEMV + SwiGLU, published as tagged bf16
+//       pairs) ...
+//   P7  ... and, once the team has published the expert's whole SwiGLU output,
+//       the same share of the expert's down-projection rows, published as
+//       tagged fp32 values.  The shared expert's down rows are done first by the
+//       owners of those output rows, while the teams finish.
+//   P8  each workgroup owns a slice of output rows and combines
+//       y_shared + sum_k g_k y_k in fp32 in rank order, then rounds once (or adds
+//       the residual with one rounding, or writes the fp32 partial).
+//
+// Every selected expert's weights stream from HBM exactly once per call, for
+// all the token rows that chose it; no workgroup reads another's weights.
+#pragma once
+
+#include "moe_device.hpp"
+
+namespace moe {
+
+#ifndef MOE_MAX_LAYERS
+#define MOE_MAX_LAYERS 64
+#endif
+
+constexpr int kMaxPK = MOE_MAXM * 16;  // max (routed expert, row) pairs = M * K
+
+struct LayerW {
+  const uint16_t* wr;   // [E][H]
+  const uint16_t* wgu;  // [E+S][2I][H]
+  const uint16_t* wd;   // [E+S][H][I]
+};
+
+enum : uint32_t {
+  F_RESIDUAL = 1u,     // chain: h_{l+1} = bf16(h_l + acc)
+  F_OUT_F32 = 2u,      // write the unrounded fp32 acc
+  F_TOPK_IN = 4u,      // routing comes from the caller (experts only)
+  F_ROUTER_ONLY = 8u,  // router + top-k only
+  F_ALIAS = 16u,       // out overlaps x_in: wait until every workgroup has read x_in
+  F_PRENORM = 32u,     // chain: each layer's MoE input is bf16(RMSNorm(h_l)), unit gain
+};
+
+constexpr float kRmsEps = 1e-6f;
+
+struct Params {
+  int H, E, K, I, S, M, L;
+  uint32_t flags;
+  int nr_max;         // output rows owned by one workgroup, at most
+  // LDS byte offsets
+  int lds_xs, lds_lg, lds_hs, lds_ysh, lds_ysr, lds_small;  // lds_hs: [3*M][I] bf16
+  const uint16_t* x_in;
+  void* out;
+  const int32_t* tk_idx_in;
+  const float* tk_gate_in;
+  int32_t* tk_idx_out;   // [L][M][K] (or [M][K])
+  float* tk_gate_out;    // [M][K]
+  float* logits_out;     // [M][E]
+  uint16_t* h_all;       // [L+1][M][H] residual stream per layer (optional)
+  uint32_t* hdr;
+  uint64_t* lg_buf;      // [L][M][E]       tagged fp32 logits
+  uint64_t* hs_buf;      // [L][M][I/2]     tagged bf16 pairs, shared expert
+  uint64_t* hr_buf;      // [L][M*K][I/2]   tagged bf16 pairs, routed (expert, row) pairs
+  uint64_t* y_buf;       // [L][M*K][H]     tagged fp32 down outputs of routed pairs
+  uint64_t* res_buf;     // [L+1][M][H/2]   tagged bf16 pairs, residual stream
+  LayerW lw[MOE_MAX_LAYERS];
+};
+
+struct Small {
+  int nU, nP, abort_flag, pad;
+  int tk_idx[kMaxPK];
+  float tk_gate[kMaxPK];
+  int upos[kMaxPK];          // routed slot of (row, rank), -1 if skipped
+  int uexp[kMaxPK];          // expert id of routed slot r
+  uint32_t umask[kMaxPK];    // rows that chose routed slot r
+  int pbase[kMaxPK + 1];     // first (slot, row) pair of slot r
+  uint32_t bm[32];           // expert bitmap (E <= 1024)
+  int bpre[32];              // population-count prefix per bitmap word
+  float rn[MOE_MAXM];        // RMSNorm scale per token row
+  alignas(16) uint32_t gmax[MOE_MAXM * MOE_WAVES];  // top-k: group maxima per row
+  int ccount[MOE_MAXM];                 // top-k: candidates per row
+  alignas(16) uint64_t cand[MOE_MAXM * 64];  // top-k: (key << 32 | ~expert) candidates
+  uint16_t hres[MOE_MAXM * 64];  // residual input h_l of this workgroup's output rows
+};
+
+__device__ __forceinline__ float swiglu(float a, float b) {
+  const float s = a / (1.0f + expf(-a));
+  return s * b;
+}
+
+// Inclusive prefix sum over the 64 lanes, all in DPP: shifts by 1, 2, 4 and
+// 8 inside each 16-lane row, then row 0's total broadcast into row 1 (and row
+// 2's into row 3), then row 1's running total into rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
+// Copy n tagged words into LDS (low 32 bits) once each carries `tag`.  Each
+// thread requests a whole batch of B independent words before checking any,
+// and re-requests every word of the batch still carrying an older tag together,
+// so a stage costs about one load latency per poll round rather than one per
+// word.  addr(i) gives the source word of element i.  Returns false on a
+// missed deadline (recorded in the workspace status).
+template <int B, typename Addr>
+__device__ __forceinline__ bool stage_tagged(int n, uint32_t* dst32, uint32_t tag,
+                                             const Waiter& wt, int tid, Addr addr) {
+  const uint64_t ready = (uint64_t)tag << 32;
+  for (int base = tid; base < n; base += B * MOE_WG) {
+    uint64_t v[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int i = base + b * MOE_WG;
+      v[b] = i < n ? ld_tag(addr(i)) : ready;
+    }
+    for (;;) {
+      bool all = true;
+#pragma unroll
+      for (int b = 0; b < B; ++b) all = all && (uint32_t)(v[b] >> 32) == tag;
+      if (all) break;
+      if (wt.expired()) {
+        record_status(wt.hdr, -6 /* MOE_E_TIMEOUT */);
+        return false;
+      }
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+        if ((uint32_t)(v[b] >> 32) != tag) v[b] = ld_tag(addr(base + b * MOE_WG));
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int i = base + b * MOE_WG;
+      if (i < n) dst32[i] = (uint32_t)v[b];
+    }
+  }
+  return true;
+}
+
+// ---------------------------------------------------------------- streaming units
+//
+// A row unit is two weight rows of H bf16 values, the first on lanes 0-31 and
+// the second on lanes 32-63, CPLH 16-byte loads per lane.  A down unit is
+// DBLK blocks of 8 down-projection rows (8 lanes per row, CPLI loads per lane).
+// Every task requests all its weights before using any, and the first task of
+// a phase is requested before the phase waits on its inputs.
+
+template <int CPLH>
+struct RowRegs {
+  uint4 w[CPLH];
+};
+
+template <int CPLH>
+__device__ __forceinline__ void load_rows(RowRegs<CPLH>& r, const uint16_t* row0,
+                                          const uint16_t* row1, int lane) {
+  const uint4* src = reinterpret_cast<const uint4*>((lane >> 5) ? row1 : row0);
+  const int li = lane & 31;
+#pragma unroll
+  for (int q = 0; q < CPLH; ++q) r.w[q] = src[li + 32 * q];
+}
+
+// Dot product of each half-wave's row with token row m (all lanes of a half
+// receive the sum).
+template <int CPLH>
+__device__ __forceinline__ float dot_rows(const RowRegs<CPLH>& r, const uint4* xs4, int H8, int m,
+                                          int lane) {
+  const int li = lane & 31;
+  float acc = 0.0f;
+#pragma unroll
+  for (int q = 0; q < CPLH; ++q) acc = dot8(r.w[q], xs4[m * H8 + li + 32 * q], acc);
+  return group_sum(acc, 32);
+}
+
+// P1 item `it`: router rows (it < NRI) or a shared-expert gate/up row pair.
+// The first unit goes to A; a gate/up item's second unit goes to B when
+// `second` is set.
+template <int CPLH>
+__device__ __forceinline__ void p1_load(const Params& p, int l, int it, int NRI,
+                                        RowRegs<CPLH>& A, RowRegs<CPLH>& B, int lane,
+                                        bool second) {
+  // Row pointers are chosen first and the loads issued unconditionally after,
+  // so the two register buffers never meet in one pointer (which would force
+  // them out of registers).
+  const size_t H = (size_t)p.H, I = (size_t)p.I;
+  const uint16_t *a0, *a1, *b0, *b1;
+  const bool router = it < NRI;
+  if (router) {
+    const int e0 = 2 * it, e1 = (2 * it + 1 < p.E) ? 2 * it + 1 : 2 * it;
+    a0 = p.lw[l].wr + (size_t)e0 * H;
+    a1 = p.lw[l].wr + (size_t)e1 * H;
+    b0 = a0;
+    b1 = a1;
+  } else {
+    const size_t j0 = 2 * (size_t)(it - NRI);
+    const uint16_t* base = p.lw[l].wgu + (size_t)p.E * (2 * I) * H;
+    a0 = base + j0 * H;
+    a1 = base + (I + j0) * H;
+    b0 = base + (j0 + 1) * H;
+    b1 = base + (I + j0 + 1) * H;
+  }
+  load_rows<CPLH>(A, a0, a1, lane);
+  if (!router && second) load_rows<CPLH>(B, b0, b1, lane);
+}
+
+template <int CPLH>
+__device__ __forceinline__ void p1_load_second(const Params& p, int l, int it, int NRI,
+                                               RowRegs<CPLH>& B, int lane) {
+  const size_t H = (size_t)p.H, I = (size_t)p.I;
+  const size_t j1 = 2 * (size_t)(it - NRI) + 1;
+  const uint16_t* base = p.lw[l].wgu + (size_t)p.E * (2 * I) * H;
+  load_rows<CPLH>(B, base + j1 * H, base + (I + j1) * H, lane);
+}
+
+template <int CPLH>
+__device__ __forceinline__ void p1_compute(const Params& p, int l, int it, int NRI,
+                                           const RowRegs<CPLH>& A, const RowRegs<CPLH>& B,
+                                           const uint4* xs4, uint32_t tag, int lane,
+                                           uint32_t dbg) {
+  const int H8 = p.H >> 3;
+  if (it < NRI) {
+    const int e = 2 * it + (lane >> 5);
+    const bool publish =
+        e < p.E && (lane & 31) == 0 && !(dbg & DBG_NO_ROUTER_PUBLISH);
+#pragma unroll 1
+    for (int m = 0; m < p.M; ++m) {
+      const float acc = dot_rows<CPLH>(A, xs4, H8, m, lane);
+      if (publish) st_tag(p.lg_buf + ((size_t)l * p.M + m) * p.E + e, __float_as_uint(acc), tag);
+    }
+  } else {
+    const int jp = it - NRI, I2 = p.I >> 1;
+    uint64_t* dst = p.hs_buf + (size_t)l * p.M * I2 + jp;
+#pragma unroll 1
+    for (int m = 0; m < p.M; ++m) {
+      const float a0 = dot_rows<CPLH>(A, xs4, H8, m, lane);
+      const float a1 = dot_rows<CPLH>(B, xs4, H8, m, lane);
+      const uint32_t word = f_to_bf(swiglu(readlane_f(a0, 0), readlane_f(a0, 32))) |
+                            (f_to_bf(swiglu(readlane_f(a1, 0), readlane_f(a1, 32))) << 16);
+      if (lane == 0) st_tag(dst + (size_t)m * I2, word, tag);
+    }
+  }
+}
+
+template <int CPLI, int DBLK>
+struct DownRegs {
+  uint4 w[DBLK][CPLI];
+};
+
+// Down rows [n, min(n + 8*DBLK, n_end)) of expert e: row n + 8b + (lane >> 3)
+// on the 8-lane group of lane in block b.
+template <int CPLI, int DBLK>
+__device__ __forceinline__ void load_down(DownRegs<CPLI, DBLK>& r, const Params& p, int l, int e,
+                                          int n, int n_end, int lane) {
+  const int gl = lane >> 3, li = lane & 7;
+#pragma unroll
+  for (int b = 0; b < DBLK; ++b) {
+    const int row = n + 8 * b + gl;
+    const uint4* src = reinterpret_cast<const uint4*>(
+        p.lw[l].wd + ((size_t)e * p.H + (row < n_end ? row : n)) * p.I);
+#pragma unroll
+    for (int q = 0; q < CPLI; ++q) r.w[b][q] = src[li + 8 * q];
+  }
+}
+
+// y(t, row) = sum_j h_t[j] * W[row][j] for the nrows token rows whose SwiGLU
+// outputs sit in LDS at hv4 (row t at hv4 + t * I8); emit(t, row, y).
+template <int CPLI, int DBLK, typename Emit>
+__device__ __forceinline__ void compute_down(const DownRegs<CPLI, DBLK>& r, int I8, int n,
+                                             int n_end, int nrows, const uint4* hv4, int lane,
+                                             Emit emit) {
+  const int gl = lane >> 3, li = lane & 7;
+#pragma unroll 1
+  for (int t = 0; t < nrows; ++t) {
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int q = 0; q < CPLI; ++q) acc = dot8(r.w[b][q], hv4[t * I8 + li + 8 * q], acc);
+      acc = group_sum(acc, 8);
+      const int row = n + 8 * b + gl;
+      if (li == 0 && row < n_end) emit(t, row, acc);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- P4 / P5
+
+// Softmax top-k ("softmax top-k with renormalised gates", Low-Latency MoE
+// Decode, routing step).  The selection order is: larger logit first, lower
+// expert index first among equal logits.
+//
+// Fast path (E <= 512 experts, one per thread, and K no larger than the number
+// of 64-expert groups): every wave takes the maximum of its group of 64
+// experts for each row; the smallest of a row's group maxima, tau, has at
+// least (groups) >= K experts at or above it, so the row's K winners are among
+// the experts with key >= tau.  Those candidates (typically 10-20 of 512) are
+// compacted into LDS and each one's rank is counted directly against the
+// others; ranks below K are the selection.  No step is a serial round over K.
+// A row with more than 64 candidates, and every row outside the fast path's
+// shapes, takes the plain method: K rounds of a wave-wide maximum.
+//
+// K rounds over one row held by one wave, PER keys per lane in lane-major
+// blocks (lane L holds experts L*PER .. L*PER+PER-1); key 0 marks "no expert".
+template <int PER>
+__device__ __forceinline__ void select_rounds(const float* lr, int E, int K, int* out, int lane) {
+  uint32_t keys[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane * PER + i;
+    keys[i] = e < E ? f_key(lr[e]) : 0u;
+  }
+#pragma unroll 1
+  for (int k = 0; k < K; ++k) {
+    uint32_t lb = 0u;
+    int li = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (keys[i] > lb) { lb = keys[i]; li = i; }
+    const uint32_t wmax = wave_max_u32(lb);
+    const uint64_t ball = __ballot(lb == wmax && lb != 0u);
+    const int wl = ball ? (int)__builtin_ctzll(ball) : 0;
+    const int wi = __builtin_amdgcn_readlane(li, wl);
+    if (lane == wl) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (i == wi) keys[i] = 0u;
+    }
+    if (lane == 0) out[k] = wmax ? wl * PER + wi : -1;
+  }
+}
+
+__device__ __forceinline__ void select_row_plain(const float* lr, int E, int K, int* out,
+                                                 int lane) {
+  const int per = (E + 63) >> 6;
+  if (per <= 1) select_rounds<1>(lr, E, K, out, lane);
+  else if (per <= 2) select_rounds<2>(lr, E, K, out, lane);
+  else if (per <= 4) select_rounds<4>(lr, E, K, out, lane);
+  else if (per <= 8) select_rounds<8>(lr, E, K, out, lane);
+  else select_rounds<16>(lr, E, K, out, lane);
+}
+
+// Gates of row m from its K selected experts (tk_idx written by this wave):
+// p_k = exp(l_k - l_max) renormalised over the K (the full softmax
+// denominator cancels in the renormalisation); lane k holds rank k.
+__device__ __forceinline__ void gates_from_idx(const float* lr, int K, Small* sm, int m,
+                                               int lane) {
+  const int ek = lane < K ? sm->tk_idx[m * K + lane] : 0;
+  const float v0 = lr[sm->tk_idx[m * K]];
+  const float pk = lane < K ? expf(lr[ek] - v0) : 0.0f;
+  const float s = group_sum(pk, 64);
+  if (lane < K) sm->tk_gate[m * K + lane] = pk / s;
+}
+
+// Fast path for exactly MM token rows (see above).
+template <int MM>
+__device__ __forceinline__ void topk_fast(const float* lgs, Small* sm, int E, int K, int nW,
+                                          int tid, int wv, int lane) {
+  // (a) every wave: its group maximum, for every row
+  uint32_t key[MM];
+#pragma unroll
+  for (int m = 0; m < MM; ++m) key[m] = tid < E ? f_key(lgs[m * E + tid]) : 0u;
+  uint32_t mine = 0u;
+#pragma unroll
+  for (int m = 0; m < MM; ++m) {
+    const uint32_t gm = wave_max_u32(key[m]);
+    mine = lane == m ? gm : mine;
+  }
+  if (lane < MM) sm->gmax[lane * MOE_WAVES + wv] = mine;
+  if (tid < MOE_MAXM) sm->ccount[tid] = 0;
+  __syncthreads();
+  // (b) lane m: tau of row m = its smallest group maximum; every row's
+  //     candidates (key >= tau) are packed as (key << 32 | ~expert), so that
+  //     one unsigned 64-bit comparison orders them as the selection does
+  uint32_t tau_l = 0u;
+  if (lane < MM) {
+    const uint4 ga = *reinterpret_cast<const uint4*>(sm->gmax + lane * MOE_WAVES);
+    const uint4 gb = *reinterpret_cast<const uint4*>(sm->gmax + lane * MOE_WAVES + 4);
+    const uint32_t g8[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+    tau_l = g8[0];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) tau_l = w < nW ? min(tau_l, g8[w]) : tau_l;
+  }
+  uint64_t ball[MM];
+  int cnt = 0;
+#pragma unroll
+  for (int m = 0; m < MM; ++m) {
+    const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)tau_l, m);
+    ball[m] = __ballot(key[m] != 0u && key[m] >= tau);
+    cnt = lane == m ? (int)__builtin_popcountll(ball[m]) : cnt;
+  }
+  const int base = lane < MM ? atomicAdd(&sm->ccount[lane], cnt) : 0;
+#pragma unroll
+  for (int m = 0; m < MM; ++m) {
+    const int pos = __builtin_amdgcn_readlane(base, m) +
+                    (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(ball[m] >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)ball[m], 0u));
+    if (((ball[m] >> lane) & 1ull) && pos < 64)
+      sm->cand[m * 64 + pos] = ((uint64_t)key[m] << 32) | (uint64_t)(uint32_t)~tid;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void topk_rows(const Params& p, const float* lgs, Small* sm, int tid,
+                                          int wv, int lane) {
+  const int M = p.M, E = p.E, K = p.K;
+  const int nW = (E + 63) >> 6;
+  const bool fast = E <= MOE_WG && K <= nW;
+  if (fast) {
+    switch (M) {
+      case 1: topk_fast<1>(lgs, sm, E, K, nW, tid, wv, lane); break;
+      case 2: topk_fast<2>(lgs, sm, E, K, nW, tid, wv, lane); break;
+      case 3: topk_fast<3>(lgs, sm, E, K, nW, tid, wv, lane); break;
+      case 4: topk_fast<4>(lgs, sm, E, K, nW, tid, wv, lane); break;
+      case 5: topk_fast<5>(lgs, sm, E, K, nW, tid, wv, lane); break;
+      case 6: topk_fast<6>(lgs, sm, E, K, nW, tid, wv, lane); break;
+      case 7: topk_fast<7>(lgs, sm, E, K, nW, tid, wv, lane); break;
+      default: topk_fast<8>(lgs, sm, E, K, nW, tid, wv, lane); break;
+    }
+  }
+  // (c) one wave per row: rank the candidates, or K plain rounds
+  for (int m = wv; m < M; m += MOE_WAVES) {
+    const int n = fast ? sm->ccount[m] : 0;
+    if (n >= K && n <= 64) {
+      const uint64_t* cr = sm->cand + m * 64;
+      const uint64_t mine = lane < n ? cr[lane] : 0ull;
+      int rank = 0;
+#pragma unroll 1
+      for (int j = 0; j < n; j += 8) {
+        const ulonglong2 c0 = *reinterpret_cast<const ulonglong2*>(cr + j);
+        const ulonglong2 c1 = *reinterpret_cast<const ulonglong2*>(cr + j + 2);
+        const ulonglong2 c2 = *reinterpret_cast<const ulonglong2*>(cr + j + 4);
+        const ulonglong2 c3 = *reinterpret_cast<const ulonglong2*>(cr + j + 6);
+        const uint64_t c8[8] = {c0.x, c0.y, c1.x, c1.y, c2.x, c2.y, c3.x, c3.y};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) rank += (j + q < n && c8[q] > mine) ? 1 : 0;
+      }
+      const bool sel = lane < n && rank < K;
+      // the row maximum is the rank-0 candidate's key
+      const uint32_t kmax = wave_max_u32(lane < n ? (uint32_t)(mine >> 32) : 0u);
+      const float pk = sel ? expf(key_f((uint32_t)(mine >> 32)) - key_f(kmax)) : 0.0f;
+      const float s = group_sum(pk, 64);
+      if (sel) {
+        sm->tk_idx[m * K + rank] = (int)~(uint32_t)mine;
+        sm->tk_gate[m * K + rank] = pk / s;
+      }
+    } else {
+      select_row_plain(lgs + m * E, E, K, sm->tk_idx + m * K, lane);
+      gates_from_idx(lgs + m * E, K, sm, m, lane);
+    }
+  }
+}
+
+// Routed slots in ascending expert order, their row masks and pair numbering.
+// Built by wave 0 alone (its LDS operations execute in order), then one
+// workgroup barrier publishes the tables.
+__device__ __forceinline__ void build_union(const Params& p, Small* sm, int wv, int lane) {
+  if (wv == 0) {
+    const int MK = p.M * p.K;  // <= 128: entries (row, rank) i = lane and lane + 64
+    if (lane < 32) sm->bm[lane] = 0u;
+    sm->umask[lane] = 0u;
+    sm->umask[lane + 64] = 0u;
+    const int ea = lane < MK ? sm->tk_idx[lane] : -1;
+    const int eb = lane + 64 < MK ? sm->tk_idx[lane + 64] : -1;
+    if (ea >= 0) atomicOr(&sm->bm[ea >> 5], 1u << (ea & 31));
+    if (eb >= 0) atomicOr(&sm->bm[eb >> 5], 1u << (eb & 31));
+    const uint32_t w = lane < 32 ? sm->bm[lane] : 0u;
+    const int c = __builtin_popcount(w);
+    const int incl = wave_incl_scan(c);
+    const int U = __builtin_amdgcn_readlane(incl, 63);
+    if (lane < 32) sm->bpre[lane] = incl - c;
+    if (lane == 0) sm->nU = U;
+    // routed slot of each entry = number of selected experts below it
+    int ra = -1, rb = -1;
+    if (ea >= 0) {
+      ra = sm->bpre[ea >> 5] + __builtin_popcount(sm->bm[ea >> 5] & ((1u << (ea & 31)) - 1u));
+      sm->uexp[ra] = ea;
+      atomicOr(&sm->umask[ra], 1u << (lane / p.K));
+    }
+    if (eb >= 0) {
+      rb = sm->bpre[eb >> 5] + __builtin_popcount(sm->bm[eb >> 5] & ((1u << (eb & 31)) - 1u));
+      sm->uexp[rb] = eb;
+      atomicOr(&sm->umask[rb], 1u << ((lane + 64) / p.K));
+    }
+    if (lane < MK) sm->upos[lane] = ra;
+    if (lane + 64 < MK) sm->upos[lane + 64] = rb;
+    // first (slot, row) pair of every slot
+    const int c0 = lane < U ? __builtin_popcount(sm->umask[lane]) : 0;
+    const int c1 = lane + 64 < U ? __builtin_popcount(sm->umask[lane + 64]) : 0;
+    const int i0 = wave_incl_scan(c0);
+    const int t0 = __builtin_amdgcn_readlane(i0, 63);
+    const int i1 = wave_incl_scan(c1);
+    sm->pbase[lane] = i0 - c0;
+    sm->pbase[lane + 64] = t0 + i1 - c1;
+    if (lane == 63) {
+      sm->nP = t0 + i1;
+      sm->pbase[kMaxPK] = t0 + i1;
+    }
+  }
+  __syncthreads();
+}
+
+// Piece q (0 or 1) of this workgroup's slice of the routed work: expert slot r,
+// intermediate range [j0, j1) and down rows [n0, n1).  Returns false if none.
+struct Piece {
+  int r, j0, j1, n0, n1;
+};
+
+__device__ __forceinline__ bool slice_piece(int g, int G, int U, int I, int H, int q, Piece& pc) {
+  if (U <= 0) return false;
+  const long long s0 = (long long)g * U, s1 = (long long)(g + 1) * U;  // in units of 1/G
+  const int r = (int)(s0 / G) + q;
+  if ((long long)r * G >= s1 || r >= U) return false;
+  long long a = s0 - (long long)r * G, b = s1 - (long long)r * G;
+  if (a < 0) a = 0;
+  if (b > G) b = G;
+  if (b <= a) return false;
+  const int I2 = I >> 1, H2 = H >> 1;
+  pc.r = r;
+  pc.j0 = 2 * (int)((a * I2 + G / 2) / G);
+  pc.j1 = 2 * (int)((b * I2 + G / 2) / G);
+  pc.n0 = 2 * (int)((a * H2 + G / 2) / G);
+  pc.n1 = 2 * (int)((b * H2 + G / 2) / G);
+  return true;
+}
+
+// ---------------------------------------------------------------- the kernel
+
+template <int CPLH, int CPLI, int DBLK>
+__global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(Params p) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  uint16_t* xs = reinterpret_cast<uint16_t*>(lds + p.lds_xs);
+  const uint4* xs4 = reinterpret_cast<const uint4*>(xs);
+  float* lgs = reinterpret_cast<float*>(lds + p.lds_lg);
+  uint32_t* hs32 = reinterpret_cast<uint32_t*>(lds + p.lds_hs);
+  const uint4* hs4 = reinterpret_cast<const uint4*>(lds + p.lds_hs);
+  float* ysh = reinterpret_cast<float*>(lds + p.lds_ysh);
+  float* ysr = reinterpret_cast<float*>(lds + p.lds_ysr);
+  Small* sm = reinterpret_cast<Small*>(lds + p.lds_small);
+
+  const int G = gridDim.x, g = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int NW = G * MOE_WAVES;
+  const int gw = wv * G + g;  // consecutive wave ids land on different CUs
+  const uint32_t tag = ld_u32(p.hdr + HDR_EPOCH) + 1u;
+  const uint32_t dbg = ld_u32(p.hdr + HDR_FLAGS);
+  const uint32_t budget = ld_u32(p.hdr + HDR_DEADLINE);
+  Waiter wt{p.hdr, now_ticks() + (budget ? budget : kDefaultDeadlineTicks)};
+  const int M = p.M, H = p.H, I = p.I, K = p.K, S = p.S, E = p.E;
+  const int I2 = I >> 1, H2 = H >> 1, I8 = I >> 3;
+  const int MK = M * K;
+  const bool router_only = (p.flags & F_ROUTER_ONLY) != 0u;
+  const bool topk_in = (p.flags & F_TOPK_IN) != 0u;
+
+  if (tid == 0) sm->abort_flag = 0;
+  uint64_t* stamps = ((dbg & DBG_STAMPS) && g < STAMP_WG)
+                         ? reinterpret_cast<uint64_t*>(p.hdr + HDR_STAMPS) + (size_t)g * STAMP_SLOTS
+                         : nullptr;
+  int sbase = 0;
+#define MOE_STAMP(ev)                                                          \
+  do {                                                                         \
+    if (stamps && tid == 0 && sbase >= 0) stamps[sbase + (ev)] = now_ticks(); \
+  } while (0)
+
+  // output rows owned by this workgroup (whole row pairs)
+  const int r0 = (int)(((long long)g * H2) / G), r1 = (int)(((long long)(g + 1) * H2) / G);
+  const int n0 = 2 * r0, NR = 2 * (r1 - r0);
+
+  for (int l = 0; l < p.L; ++l) {
+    sbase = l == 0 ? 0 : (l == 1 ? 10 : (l == p.L - 1 ? 20 : -1));
+    MOE_STAMP(0);
+    // ---------------- P1 prefetch: this wave's first router / shared gate-up rows
+    // do not depend on x, so their loads fly while x is staged
+    const int NRI = topk_in ? 0 : (E + 1) >> 1;
+    const int NSI = (router_only || !S) ? 0 : I2;
+    RowRegs<CPLH> A, B;
+    if (gw < NRI + NSI) p1_load<CPLH>(p, l, gw, NRI, A, B, lane, false);
+
+    // ---------------- P0: layer input -> LDS
+    if (l == 0) {
+      const uint4* src = reinterpret_cast<const uint4*>(p.x_in);
+      uint4* dst = reinterpret_cast<uint4*>(xs);
+      for (int i = tid; i < (M * H) >> 3; i += MOE_WG) dst[i] = src[i];
+    } else {
+      const uint64_t* src = p.res_buf + (size_t)l * M * H2;
+      if (!stage_tagged<8>(M * H2, reinterpret_cast<uint32_t*>(xs), tag, wt, tid,
+                           [&](int i) { return src + i; }))
+        sm->abort_flag = 1;
+    }
+    __syncthreads();
+    if (l == 0 && tid == 0 && (p.flags & F_ALIAS)) add_u32(p.hdr + HDR_XREAD, 1u);
+    if (sm->abort_flag) break;
+    if (p.flags & F_RESIDUAL) {
+      for (int i = tid; i < M * NR; i += MOE_WG) {
+        const int m = i / NR, nl = i - m * NR;
+        sm->hres[m * p.nr_max + nl] = xs[m * H + n0 + nl];
+      }
+    }
+    if (l == 0 && g == 0 && p.h_all) {
+      uint4* dst = reinterpret_cast<uint4*>(p.h_all);
+      for (int i = tid; i < (M * H) >> 3; i += MOE_WG) dst[i] = xs4[i];
+    }
+    if (p.flags & F_PRENORM) {
+      // Sum of squares per row in double: every bf16 square is exact in fp32 and,
+      // over the value range of a residual stream, every partial sum is exact in
+      // double, so the sum (and the scale) does not depend on the order.
+      const uint32_t* xr32 = reinterpret_cast<const uint32_t*>(xs);
+      for (int m = wv; m < M; m += MOE_WAVES) {
+        double ss = 0.0;
+        for (int c = lane; c < H2; c += 64) {
+          const uint32_t w = xr32[m * H2 + c];
+          const float a = bf_lo(w), b = bf_hi(w);
+          ss += (double)(a * a);
+          ss += (double)(b * b);
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+        if (lane == 0) sm->rn[m] = (float)(1.0 / sqrt(ss / (double)H + (double)kRmsEps));
+      }
+      __syncthreads();
+      uint32_t* x32 = reinterpret_cast<uint32_t*>(xs);
+      for (int i = tid; i < M * H2; i += MOE_WG) {
+        const float r = sm->rn[i / H2];
+        const uint32_t w = x32[i];
+        x32[i] = f_to_bf(bf_lo(w) * r) | (f_to_bf(bf_hi(w) * r) << 16);
+      }
+    }
+    __syncthreads();
+    MOE_STAMP(1);
+
+    // ---------------- P1: router rows + shared expert gate/up rows
+    for (int it = gw; it < NRI + NSI; it += NW) {
+      if (it != gw)
+        p1_load<CPLH>(p, l, it, NRI, A, B, lane, true);
+      else if (it >= NRI)  // the prefetched gate/up item still needs its second row
+        p1_load_second<CPLH>(p, l, it, NRI, B, lane);
+      p1_compute<CPLH>(p, l, it, NRI, A, B, xs4, tag, lane, dbg);
+    }
+    MOE_STAMP(2);
+
+    if (router_only) {
+      // the last workgroup to finish its rows computes the top-k
+      __syncthreads();
+      if (tid == 0) {
+        const uint32_t old = add_u32(p.hdr + HDR_DONE, 1u);
+        sm->abort_flag = (old == (uint32_t)(G - 1)) ? 2 : 3;
+      }
+      __syncthreads();
+      if (sm->abort_flag != 2) return;
+    }
+
+    // ---------------- P4: routing
+    if (topk_in) {
+      for (int i = tid; i < MK; i += MOE_WG) {
+        int e = p.tk_idx_in[i];
+        if (e < 0 || e >= E) {
+          record_status(p.hdr, -7 /* MOE_E_INDEX */);
+          e = -1;
+        }
+        sm->tk_idx[i] = e;
+        sm->tk_gate[i] = p.tk_gate_in[i];
+      }
+      __syncthreads();
+    } else {
+      const uint64_t* src = p.lg_buf + (size_t)l * M * E;
+      if (!stage_tagged<8>(M * E, reinterpret_cast<uint32_t*>(lgs), tag, wt, tid,
+                           [&](int i) { return src + i; }))
+        sm->abort_flag = 1;
+      __syncthreads();
+      MOE_STAMP(3);
+      if (sm->abort_flag == 1) break;
+      topk_rows(p, lgs, sm, tid, wv, lane);
+      __syncthreads();
+      MOE_STAMP(9);
+      if (g == 0 || router_only) {
+        int32_t* oi = p.tk_idx_out ? p.tk_idx_out + (size_t)l * MK : nullptr;
+        for (int i = tid; i < MK; i += MOE_WG) {
+          if (oi) oi[i] = sm->tk_idx[i];
+          if (p.tk_gate_out && l == 0) p.tk_gate_out[i] = sm->tk_gate[i];
+        }
+        if (p.logits_out && l == 0)
+          for (int i = tid; i < M * E; i += MOE_WG) p.logits_out[i] = lgs[i];
+      }
+      if (router_only) break;
+    }
+
+    // ---------------- P5: routed slots
+    build_union(p, sm, wv, lane);
+    const int U = sm->nU;
+    MOE_STAMP(4);
+
+    // ---------------- P6: this workgroup's slice of the routed gate/up rows
+    // Task f over the slice's intermediate pairs (wave wv takes f = wv,
+    // wv + WAVES, ...): gate/up rows j = 2jp (unit A) and 2jp + 1 (unit B) are
+    // both requested before either is used.
+    uint64_t* hr_l = p.hr_buf + (size_t)l * MK * I2;
+    Piece pc0, pc1;
+    const bool has0 = slice_piece(g, G, U, I, H, 0, pc0);
+    const bool has1 = slice_piece(g, G, U, I, H, 1, pc1);
+    const int F0 = has0 ? (pc0.j1 - pc0.j0) >> 1 : 0;
+    const int F1 = has1 ? (pc1.j1 - pc1.j0) >> 1 : 0;
+    {
+      const int r0s = has0 ? pc0.r : 0, r1s = has1 ? pc1.r : 0;
+      const int jb0 = has0 ? pc0.j0 >> 1 : 0, jb1 = has1 ? (pc1.j0 >> 1) - F0 : 0;
+      const int H8 = H >> 3;
+      for (int f = wv; f < F0 + F1; f += MOE_WAVES) {
+        const int jp = f + (f < F0 ? jb0 : jb1);
+        const int rr = f < F0 ? r0s : r1s;
+        const uint16_t* base = p.lw[l].wgu + (size_t)sm->uexp[rr] * (2 * (size_t)I) * H;
+        const size_t j0 = 2 * (size_t)jp;
+        load_rows<CPLH>(A, base + j0 * H, base + ((size_t)I + j0) * H, lane);
+        load_rows<CPLH>(B, base + (j0 + 1) * H, base + ((size_t)I + j0 + 1) * H, lane);
+        const uint32_t mask = sm->umask[rr];
+        uint64_t* dst = hr_l + (size_t)sm->pbase[rr] * I2 + jp;
+        uint32_t bits = mask;
+        int t = 0;
+#pragma unroll 1
+        while (bits) {
+          const int m = __builtin_ctz(bits);
+          bits &= bits - 1u;
+          const float a0 = dot_rows<CPLH>(A, xs4, H8, m, lane);
+          const float a1 = dot_rows<CPLH>(B, xs4, H8, m, lane);
+          const uint32_t word = f_to_bf(swiglu(readlane_f(a0, 0), readlane_f(a0, 32))) |
+                                (f_to_bf(swiglu(readlane_f(a1, 0), readlane_f(a1, 32))) << 16);
+          if (lane == 0) st_tag(dst + (size_t)t * I2, word, tag);
+          ++t;
+        }
+      }
+    }
+    MOE_STAMP(5);
+
+    // ---------------- P7: down projection
+    // This workgroup's down tasks: the shared expert's blocks of its own output
+    // rows, then its slice's blocks of the routed experts, after the SwiGLU
+    // inputs of all of them are staged in LDS with one batched wait.
+    uint64_t* y_l = p.y_buf + (size_t)l * MK * H;
+    {
+      const int BR = 8 * DBLK;
+      const int nbs = (S && NR > 0) ? (NR + BR - 1) / BR : 0;
+      const int nb0 = has0 ? (pc0.n1 - pc0.n0 + BR - 1) / BR : 0;
+      const int nb1 = has1 ? (pc1.n1 - pc1.n0 + BR - 1) / BR : 0;
+      const int nrow0 = has0 ? __builtin_popcount(sm->umask[pc0.r]) : 0;
+      const int nrow1 = has1 ? __builtin_popcount(sm->umask[pc1.r]) : 0;
+      const int ntask = nbs + nb0 + nb1;
+      // task f -> (expert, first row, end row, h rows in LDS, rows, emit kind)
+      auto task = [&](int f, int& e, int& n, int& n_end, int& kind) __attribute__((always_inline)) {
+        if (f < nbs) {
+          e = E; n = n0 + f * BR; n_end = n0 + NR; kind = 0;
+        } else if (f < nbs + nb0) {
+          e = sm->uexp[pc0.r]; n = pc0.n0 + (f - nbs) * BR; n_end = pc0.n1; kind = 1;
+        } else {
+          e = sm->uexp[pc1.r]; n = pc1.n0 + (f - nbs - nb0) * BR; n_end = pc1.n1; kind = 2;
+        }
+      };
+      DownRegs<CPLI, DBLK> DA;
+      int e, n, n_end, kind;
+      // SwiGLU inputs of all this workgroup's down tasks -> LDS: shared | piece 0 | piece 1
+      const int ws0 = nbs ? M * I2 : 0;
+      const int ws1 = nb0 ? nrow0 * I2 : 0;
+      const int ws2 = nb1 ? nrow1 * I2 : 0;
+      const uint64_t* hsrc = p.hs_buf + (size_t)l * M * I2;
+      const uint64_t* r0src = hr_l + (size_t)(has0 ? sm->pbase[pc0.r] : 0) * I2;
+      const uint64_t* r1src = hr_l + (size_t)(has1 ? sm->pbase[pc1.r] : 0) * I2;
+      if (!stage_tagged<4>(ws0 + ws1 + ws2, hs32, tag, wt, tid, [&](int i) {
+            return i < ws0 ? hsrc + i : (i < ws0 + ws1 ? r0src + (i - ws0) : r1src + (i - ws0 - ws1));
+          }))
+        sm->abort_flag = 1;
+      __syncthreads();
+      MOE_STAMP(6);
+      if (sm->abort_flag == 1) break;
+      const int pb0 = has0 ? sm->pbase[pc0.r] : 0, pb1 = has1 ? sm->pbase[pc1.r] : 0;
+      auto run = [&](int f, const DownRegs<CPLI, DBLK>& R) __attribute__((always_inline)) {
+        int e2, nn, ne, kd;
+        task(f, e2, nn, ne, kd);
+        if (kd == 0) {
+          compute_down<CPLI, DBLK>(R, I8, nn, ne, M, hs4, lane, [&](int m, int row, float y) {
+            ysh[m * p.nr_max + (row - n0)] = y;
+          });
+        } else {
+          const uint4* hv = hs4 + (size_t)(ws0 + (kd == 2 ? ws1 : 0)) / 4;
+          const int pb = kd == 1 ? pb0 : pb1;
+          compute_down<CPLI, DBLK>(R, I8, nn, ne, kd == 1 ? nrow0 : nrow1, hv, lane,
+                                   [&](int t, int row, float y) {
+                                     st_tag(y_l + (size_t)(pb + t) * H + row, __float_as_uint(y),
+                                            tag);
+                                   });
+        }
+      };
+      for (int f = wv; f < ntask; f += MOE_WAVES) {
+        task(f, e, n, n_end, kind);
+        load_down<CPLI, DBLK>(DA, p, l, e, n, n_end, lane);
+        run(f, DA);
+      }
+      __syncthreads();
+    }
+    MOE_STAMP(7);
+
+    // ---------------- P8: combine (+ residual) and hand off
+    const bool last = (l == p.L - 1);
+    if (last && (p.flags & F_ALIAS)) {
+      if (tid == 0) {
+        for (;;) {
+          if (ld_u32(p.hdr + HDR_XREAD) >= (uint32_t)G) break;
+          if (wt.expired()) { record_status(p.hdr, -6); sm->abort_flag = 1; break; }
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      __syncthreads();
+      if (sm->abort_flag == 1) break;
+    }
+    if (NR > 0) {
+      // this workgroup's rows of every routed (expert, row) output -> LDS
+      const int nP = sm->nP;
+      if (!stage_tagged<4>(nP * NR, reinterpret_cast<uint32_t*>(ysr), tag, wt, tid,
+                           [&](int i) {
+                             const int pr = i / NR;
+                             return y_l + (size_t)pr * H + n0 + (i - pr * NR);
+                           }))
+        sm->abort_flag = 1;
+    }
+    __syncthreads();
+    if (sm->abort_flag == 1) break;
+    {
+      for (int i = tid; i < (NR >> 1) * M; i += MOE_WG) {
+        const int np = i / M, m = i - np * M;
+        const int nl = 2 * np, n = n0 + nl;
+        float a0 = S ? ysh[m * p.nr_max + nl] : 0.0f;
+        float a1 = S ? ysh[m * p.nr_max + nl + 1] : 0.0f;
+        for (int k = 0; k < K; ++k) {
+          const int r = sm->upos[m * K + k];
+          if (r < 0) continue;
+          const int pr = sm->pbase[r] + __builtin_popcount(sm->umask[r] & ((1u << m) - 1u));
+          const float gk = sm->tk_gate[m * K + k];
+          const float t0 = gk * ysr[pr * NR + nl];
+          const float t1 = gk * ysr[pr * NR + nl + 1];
+          a0 = a0 + t0;
+          a1 = a1 + t1;
+        }
+        if (p.flags & F_RESIDUAL) {
+          const float h0 = bf_to_f(sm->hres[m * p.nr_max + nl]);
+          const float h1 = bf_to_f(sm->hres[m * p.nr_max + nl + 1]);
+          const uint32_t word = f_to_bf(h0 + a0) | (f_to_bf(h1 + a1) << 16);
+          if (last)
+            reinterpret_cast<uint32_t*>(p.out)[(m * H + n) >> 1] = word;
+          else
+            st_tag(p.res_buf + (size_t)(l + 1) * M * H2 + ((m * H + n) >> 1), word, tag);
+          if (p.h_all)
+            reinterpret_cast<uint32_t*>(p.h_all)[((size_t)(l + 1) * M * H + (size_t)m * H + n) >> 1] =
+                word;
+        } else if (p.flags & F_OUT_F32) {
+          reinterpret_cast<float2*>(p.out)[(m * H + n) >> 1] = make_float2(a0, a1);
+        } else {
+          reinterpret_cast<uint32_t*>(p.out)[(m * H + n) >> 1] = f_to_bf(a0) | (f_to_bf(a1) << 16);
+        }
+      }
+    }
+    __syncthreads();
+    MOE_STAMP(8);
+    if (sm->abort_flag == 1) break;
+  }
+
+  // ---------------- end of call: the last workgroup advances the step
+  __syncthreads();
+  sbase = 0;
+  MOE_STAMP(31);
+#undef MOE_STAMP
+  if (tid == 0) {
+    const bool counted = router_only;  // router-only already counted itself
+    uint32_t old = 0;
+    if (!counted) old = add_u32(p.hdr + HDR_DONE, 1u);
+    if (counted || old == (uint32_t)(G - 1)) {
+      st_u32(p.hdr + HDR_DONE, 0u);
+      st_u32(p.hdr + HDR_XREAD, 0u);
+      st_u32(p.hdr + HDR_EPOCH, tag);
+    }
+  }
+}
+
+}  // namespace moe

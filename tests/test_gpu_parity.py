@@ -136,6 +136,57 @@ def test_router_exact_on_dyadic_inputs(gpu):
     assert np.array_equal(idx.cpu().numpy(), ri)   # exact logits: ties resolved identically
 
 
+def _planted_logits(rng, M, E):
+    """Per-row logit patterns that exercise every branch of the selection:
+    all equal (every expert ties), one dense 128-expert block far above the
+    rest, a few coarse dyadic levels (many ties at the K-th place), and
+    distinct values."""
+    rows = []
+    for m in range(M):
+        kind = m % 4
+        if kind == 0:
+            v = np.full(E, 0.5)
+        elif kind == 1:
+            v = rng.integers(-8, 0, E) / 8.0
+            v[128:256] = rng.integers(8, 64, 128) / 8.0
+        elif kind == 2:
+            v = rng.integers(-4, 5, E) / 4.0
+        else:
+            v = rng.permutation(E) / 64.0 - 4.0
+        rows.append(v)
+    return np.array(rows)
+
+
+@pytest.mark.parametrize("M", [1, 4, 6, 8])
+def test_router_topk_planted_ties(gpu, M):
+    """Exact dyadic logits with planted ties and dense blocks: the selection
+    (larger logit first, lower index among equals) matches the oracle bit for
+    bit in every row, whichever internal path the row takes."""
+    import torch
+    rng = np.random.default_rng(11 + M)
+    H, E, K = 256, 512, 8
+    lgt = _planted_logits(rng, M, E)
+    x = np.zeros((M, H))
+    w = np.zeros((E, H))
+    for m in range(M):
+        x[m, m] = 1.0
+        w[:, m] = lgt[m]
+    xb = oracle.f32_to_bf16(x.astype(np.float32)).reshape(M, H)
+    wb = oracle.f32_to_bf16(w.astype(np.float32)).reshape(E, H)
+    d = md.dims(H, E, K, 64, 0)
+    ws = md.new_workspace(d, M, 1)
+    idx = _empty((M, K), torch.int32, gpu)
+    gate = _empty((M, K), torch.float32, gpu)
+    lg = _empty((M, E), torch.float32, gpu)
+    say("router_topk planted ties M=%d" % M)
+    md.check(md.moe_router_topk(d, M, D.to_device(xb), D.to_device(wb), idx, gate, lg, ws))
+    md.check(md.moe_last_device_status(ws))
+    ri, rg, rl = oracle.router_topk(xb, wb, K)
+    assert np.array_equal(lg.cpu().numpy(), rl)
+    assert np.array_equal(idx.cpu().numpy(), ri)
+    assert np.allclose(gate.cpu().numpy(), rg, rtol=1e-5, atol=0)
+
+
 # ------------------------------------------------------------------ one layer
 
 @pytest.mark.parametrize("M", [1, 2, 3, 6, 8])
