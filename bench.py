@@ -91,26 +91,37 @@ def main():
         for i in range(warmup):
             md.check(call(i))
         torch.cuda.synchronize()
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        # timed region: exactly `steps` back-to-back launches between two events
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t_start = time.perf_counter()
-        evs[0].record()
+        e0.record()
         for i in range(steps):
             md.check(call(warmup + i))
-            evs[i + 1].record()
+        e1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_start
         md.check(md.moe_last_device_status(ws))
-        per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]) * 1e3  # us
+        us_per = e0.elapsed_time(e1) * 1e3 / steps
+        # spread: a separate, untimed pass with an event after every launch
+        # (each event adds its own small cost, so these sit a little above us_per)
+        ne = min(steps, 50)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(ne + 1)]
+        evs[0].record()
+        for i in range(ne):
+            md.check(call(warmup + i))
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(ne)]) * 1e3
         ids = idx.cpu().numpy()[warmup:]
         U = np.array([len(np.unique(ids[i])) for i in range(steps)])
         bytes_per = wl.router_bytes() + (U + wl.S) * wl.expert_bytes()
-        gbs = bytes_per.sum() / (per.sum() * 1e-6) / 1e9
+        gbs = bytes_per.mean() / (us_per * 1e-6) / 1e9
         return {
-            "us_per_layer": float(per.mean()),
-            "us_median": float(np.median(per)),
-            "us_p10": float(np.percentile(per, 10)),
-            "us_p90": float(np.percentile(per, 90)),
+            "us_per_layer": float(us_per),
+            "per_call_event_us_median": float(np.median(per)),
+            "per_call_event_us_p10": float(np.percentile(per, 10)),
+            "per_call_event_us_p90": float(np.percentile(per, 90)),
             "wall_ms_per_step": wall * 1e3 / steps,
             "effective_gbs": float(gbs),
             "pct_of_hbm_peak": float(100.0 * gbs / HBM_PEAK_GBS),
