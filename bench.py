@@ -42,15 +42,34 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="rocprofv3 FETCH/WRITE_SIZE summary for the roofline traffic field")
+    ap.add_argument("--profile-run", choices=sorted(PROFILE_WORKLOADS),
+                    help="untimed launches of one workload for rocprofv3 (after one known-size "
+                         "reference copy); prints no JSON")
+    ap.add_argument("--ingest-profiles", metavar="DIR",
+                    help="read rocprofv3 CSV output under DIR and write the summaries in profiles/")
     return ap.parse_args()
+
+
+# Workloads of --profile-run: (workload name, rows, fp32 partial output)
+PROFILE_WORKLOADS = {"m1": ("ling_moe_layer_m1", 1, False),
+                     "m6": ("ling_moe_layer_m6", 6, False),
+                     "tp4": ("ling_tp4_shard_moe_layer_m6", 6, True)}
+COPY_BYTES = 256 << 20   # reference copy for the counter scale
+PROFILE_CALLS = 64
 
 
 def main():
     args = parse()
+    if args.ingest_profiles:
+        ingest_profiles(args.ingest_profiles)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.profile_run:
+        profile_run(args.profile_run)
+        return
 
     import numpy as np
     import torch
@@ -162,7 +181,7 @@ def main():
         with open(args.traffic) as f:
             tj = json.load(f)
         if tj.get("kernel_source_sha") == kernel_source_sha():
-            traffic = tj.get("bytes_per_launch")
+            traffic = tj.get("workloads", {}).get(W.C2.name, {}).get("bytes_per_launch")
 
     cpu = None
     if not args.no_cpu:
@@ -255,6 +274,143 @@ def time_chain(md, D, W, np, torch, dev, lw, steps, warmup):
         "floor_us_at_peak": float(floor_us),
         "ratio_to_floor": float(tot_us / floor_us),
     }
+
+
+def profile_run(key):
+    """One reference copy of COPY_BYTES, then PROFILE_CALLS cold layer launches of
+    one workload (rotating over 16 distinct layers), for rocprofv3."""
+    import torch
+
+    import benchsupport as bs
+    import moe_decode_amd as md
+    from datagen import device as D
+    from datagen import workloads as W
+
+    name, M, f32 = PROFILE_WORKLOADS[key]
+    wl = {w.name: w for w in (W.C2, W.C3, W.C4)}[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layers = [D.make_layer(wl, l) for l in range(N_LAYERS)]
+    lws = [md.layer_weights(L.w_router, L.w_gate_up, L.w_down) for L in layers]
+    d = md.dims(wl.H, wl.E, wl.K, wl.I, wl.S)
+    ws = md.new_workspace(d, M, 1)
+    xs = torch.stack([D.to_device(W.x_rows(wl, [s * M + m for m in range(M)]))
+                      for s in range(PROFILE_CALLS)])
+    out = torch.empty((M, wl.H), dtype=torch.float32 if f32 else torch.int16, device=dev)
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream().cuda_stream
+    bs.copy(src, dst, 2048, st)
+    idx = torch.empty((PROFILE_CALLS, M, wl.K), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    for i in range(PROFILE_CALLS):
+        md.check(md.moe_layer_chain(d, M, [lws[i % N_LAYERS]], xs[i], out,
+                                    md.MOE_OUT_F32 if f32 else md.MOE_OUT_BF16,
+                                    md.MOE_CHAIN_LAYER_ONLY, idx[i], ws))
+    torch.cuda.synchronize()
+    md.check(md.moe_last_device_status(ws))
+    ids = idx.cpu().numpy()
+    U = [len(set(ids[i].ravel().tolist())) for i in range(PROFILE_CALLS)]
+    alg = wl.router_bytes() + (sum(U) / len(U) + wl.S) * wl.expert_bytes()
+    print("profile run %s: 1 copy of %d bytes, %d layer launches" % (key, COPY_BYTES,
+                                                                      PROFILE_CALLS))
+    print("algorithmic bytes per launch: %.0f (mean union %.2f experts)" % (alg, sum(U) / len(U)),
+          flush=True)
+
+
+def _csv_rows(root, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(root, "**", "*" + suffix), recursive=True))
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return files, rows
+
+
+def ingest_profiles(root):
+    """rocprofv3 output of the profile runs -> profiles/*.txt and profiles/traffic.json.
+
+    Expected layout under root: kt_<key>/ (--kernel-trace --stats), pmc_fetch_<key>/
+    (--pmc FETCH_SIZE) and pmc_write_<key>/ (--pmc WRITE_SIZE) for each key of
+    PROFILE_WORKLOADS that was run.  FETCH_SIZE and WRITE_SIZE are KiB per dispatch;
+    each is scaled to bytes by what it reads for the reference copy of COPY_BYTES."""
+    import numpy as np
+    out_dir = os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    traffic = {"kernel_source_sha": kernel_source_sha(), "copy_bytes": COPY_BYTES,
+               "workloads": {}}
+    for key, (name, M, _) in sorted(PROFILE_WORKLOADS.items()):
+        cmd_kt = ("rocprofv3 --kernel-trace --stats --output-format csv -d %s/kt_%s -o kt "
+                  "-- python3 bench.py --profile-run %s" % (root, key, key))
+        alg = None
+        logf = os.path.join(root, "kt_%s.log" % key)
+        if os.path.exists(logf):
+            for ln in open(logf):
+                if ln.startswith("algorithmic bytes per launch:"):
+                    alg = float(ln.split(":")[1].split()[0])
+        kt_files, kt = _csv_rows(os.path.join(root, "kt_" + key), "kernel_trace.csv")
+        st_files, stats = _csv_rows(os.path.join(root, "kt_" + key), "kernel_stats.csv")
+        if not kt_files:
+            continue
+        lay = [r for r in kt if "moe_layer_kernel" in r.get("Kernel_Name", "")]
+        durs = np.array([int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in lay],
+                        dtype=np.float64) * 1e-3
+        lines = ["# %s: moe_layer_kernel, %d cold single-layer launches" % (name, len(durs)),
+                 "command: %s" % cmd_kt,
+                 "per-launch kernel duration (us, kernel_trace.csv): mean %.2f  median %.2f  "
+                 "min %.2f  max %.2f" % (durs.mean(), np.median(durs), durs.min(), durs.max()),
+                 "", "kernel_stats.csv:"]
+        for r in stats:
+            lines.append("  %-60s calls %5s  avg %10.0f ns  total %12s ns  %6s %%"
+                         % (r["Name"][:60], r["Calls"], float(r["AverageNs"]),
+                            r["TotalDurationNs"], r["Percentage"]))
+        w = {"mean_kernel_us": float(durs.mean()), "median_kernel_us": float(np.median(durs))}
+        for ctr, tag in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+            files, rows = _csv_rows(os.path.join(root, "pmc_%s_%s" % (tag, key)),
+                                    "counter_collection.csv")
+            if not files:
+                continue
+            ref = [float(r["Counter_Value"]) for r in rows
+                   if "bs_copy" in r["Kernel_Name"] and r["Counter_Name"] == ctr]
+            vals = [float(r["Counter_Value"]) for r in rows
+                    if "moe_layer_kernel" in r["Kernel_Name"] and r["Counter_Name"] == ctr]
+            if not ref or not vals:
+                continue
+            scale = COPY_BYTES / ref[0]          # bytes per counter unit
+            per = float(np.mean(vals)) * scale
+            w[tag + "_bytes_per_launch"] = per
+            w[tag + "_counter_per_launch"] = float(np.mean(vals))
+            w[tag + "_scale_bytes_per_unit"] = scale
+            lines.append("")
+            lines.append("%s: command: rocprofv3 --pmc %s --output-format csv -d %s/pmc_%s_%s "
+                         "-o pmc -- python3 bench.py --profile-run %s" % (ctr, ctr, root, tag, key,
+                                                                          key))
+            lines.append("  reference copy of %d bytes (read once, written once): %.1f units "
+                         "-> %.2f bytes per unit" % (COPY_BYTES, ref[0], scale))
+            lines.append("  layer kernel: %.1f units per launch (mean of %d) = %.3f MB per launch"
+                         % (np.mean(vals), len(vals), per / 1e6))
+        if "fetch_bytes_per_launch" in w:
+            w["bytes_per_launch"] = w["fetch_bytes_per_launch"] + w.get("write_bytes_per_launch", 0.0)
+        if alg:
+            w["algorithmic_bytes_per_launch"] = alg
+            lines.append("")
+            lines.append("algorithmic bytes per launch (router + union + shared expert, each once): "
+                         "%.3f MB" % (alg / 1e6))
+            if "bytes_per_launch" in w:
+                lines.append("measured HBM traffic / algorithmic bytes: %.4f"
+                             % (w["bytes_per_launch"] / alg))
+            lines.append("achieved at the mean kernel duration: %.0f GB/s (%.1f %% of 8 TB/s)"
+                         % (alg / (durs.mean() * 1e-6) / 1e9,
+                            100 * alg / (durs.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS))
+        traffic["workloads"][name] = w
+        with open(os.path.join(out_dir, "moe_layer_kernel_%s.txt" % name), "w") as f:
+            f.write("\n".join(lines) + "\n")
+    with open(os.path.join(out_dir, "traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+    print(json.dumps(traffic, indent=1))
 
 
 def kernel_source_sha():

@@ -166,8 +166,9 @@ int moe_last_device_status(void* ws, size_t ws_bytes, void* stream);
  *          uint64 [256 workgroups][32 slots]: slots 10*s + e for layer slot
  *          s (0: first layer, 1: second, 2: last) and event e (0 layer start,
  *          1 input staged, 2 router and shared gate/up rows done, 3 logits
- *          received, 4 top-k and union built, 5 routed gate/up done, 6 first h
- *          group staged, 7 down projection done, 8 combine done); slot 31 is
+ *          received, 9 top-k done, 4 expert union built, 5 routed gate/up
+ *          done, 6 down inputs staged, 7 down projection done, 8 combine
+ *          done); slot 31 is
  *          the end of the call. */
 int moe_workspace_debug(void* ws, size_t ws_bytes, uint32_t flags, uint32_t deadline_us,
                         void* stream);
