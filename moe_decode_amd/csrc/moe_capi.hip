@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <vector>
 
 #include "../../include/moe_decode.h"
 #include "moe_layer.hpp"
@@ -82,15 +83,48 @@ int down_blocks(int cpli) {
 }
 
 // Compiled (CPLH, CPLI) variants of the layer kernel: hidden size 256 * CPLH,
-// intermediate size 64 * CPLI.
-typedef void (*LayerKern)(Params);
-LayerKern pick_layer_kernel(int cplh, int cpli) {
-#define MOE_K(a, b) \
-  if (cplh == a && cpli == b) return moe_layer_kernel<a, b, (10 / b < 1 ? 1 : (10 / b > 4 ? 4 : 10 / b))>;
+// intermediate size 64 * CPLI; NL layer weight slots in the kernel arguments.
+template <int NL>
+using LayerKern = void (*)(ParamsT<NL>);
+
+template <int NL>
+LayerKern<NL> pick_layer_kernel(int cplh, int cpli) {
+#define MOE_K(a, b)              \
+  if (cplh == a && cpli == b)   \
+    return moe_layer_kernel<a, b, (10 / b < 1 ? 1 : (10 / b > 4 ? 4 : 10 / b)), NL>;
   MOE_K(1, 1) MOE_K(10, 12) MOE_K(10, 3) MOE_K(10, 1) MOE_K(10, 4) MOE_K(8, 12) MOE_K(8, 3)
   MOE_K(4, 4) MOE_K(2, 2)
 #undef MOE_K
   return nullptr;
+}
+
+// Per-process record of the kernels whose dynamic-LDS limit was raised and
+// whose co-residency was checked, so repeated calls skip both runtime queries.
+struct KernelReady {
+  const void* fn;
+  int lds;
+  int device;
+};
+std::mutex g_ready_mu;
+std::vector<KernelReady> g_ready;
+
+int prepare_kernel(const void* fn, int lds, int block) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_E_HIP;
+  {
+    std::lock_guard<std::mutex> lk(g_ready_mu);
+    for (const KernelReady& r : g_ready)
+      if (r.fn == fn && r.lds >= lds && r.device == dev) return MOE_OK;
+  }
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+    return MOE_E_HIP;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, block, lds) != hipSuccess)
+    return MOE_E_HIP;
+  if (nb < 1) return MOE_E_UNSUPPORTED;  // the persistent grid would not be co-resident
+  std::lock_guard<std::mutex> lk(g_ready_mu);
+  g_ready.push_back(KernelReady{fn, lds, dev});
+  return MOE_OK;
 }
 
 typedef void (*LmKern)(LmParams);
@@ -169,33 +203,28 @@ int plan_lds(const moe_dims& d, int M, int G, int max_lds, LdsPlan* lp) {
   return o <= (size_t)max_lds ? MOE_OK : MOE_E_UNSUPPORTED;
 }
 
-int launch_layer(const moe_dims& d, int M, int L, uint32_t flags, const moe_layer_weights* layers,
-                 const uint16_t* x, void* out, const int32_t* tk_in, const float* tkg_in,
-                 int32_t* tk_out, float* tkg_out, float* logits_out, uint16_t* h_all, void* ws,
-                 hipStream_t st) {
+template <int NL>
+int launch_layer_nl(const moe_dims& d, int M, int L, uint32_t flags,
+                    const moe_layer_weights* layers, const uint16_t* x, void* out,
+                    const int32_t* tk_in, const float* tkg_in, int32_t* tk_out, float* tkg_out,
+                    float* logits_out, uint16_t* h_all, void* ws, hipStream_t st) {
   DevInfo di;
   int rc = device_info(&di);
   if (rc) return rc;
   RowPlan ph, pi;
   plan_h_rows(d.hidden, &ph);
   plan_i_rows(d.inter, &pi);
-  LayerKern kern = pick_layer_kernel(ph.cpl, pi.cpl);
+  LayerKern<NL> kern = pick_layer_kernel<NL>(ph.cpl, pi.cpl);
   if (!kern) return MOE_E_UNSUPPORTED;
   const int G = di.num_cu;
   LdsPlan lp;
   rc = plan_lds(d, M, G, di.max_lds, &lp);
   if (rc) return rc;
-  if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          lp.total) != hipSuccess)
-    return MOE_E_HIP;
-  int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, (const void*)kern, MOE_WG, lp.total) !=
-      hipSuccess)
-    return MOE_E_HIP;
-  if (nb < 1) return MOE_E_UNSUPPORTED;  // the persistent grid would not be co-resident
+  rc = prepare_kernel((const void*)kern, lp.total, MOE_WG);
+  if (rc) return rc;
 
   const WsLayout wl = ws_layout(d, M, L);
-  Params p;
+  ParamsT<NL> p;
   memset(&p, 0, sizeof(p));
   p.H = d.hidden;
   p.E = d.n_experts;
@@ -234,6 +263,19 @@ int launch_layer(const moe_dims& d, int M, int L, uint32_t flags, const moe_laye
   }
   hipLaunchKernelGGL(kern, dim3(G), dim3(MOE_WG), lp.total, st, p);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
+// Single-layer calls carry one weight slot in their (smaller, faster to
+// launch) argument block; chains carry MOE_MAX_LAYERS.
+int launch_layer(const moe_dims& d, int M, int L, uint32_t flags, const moe_layer_weights* layers,
+                 const uint16_t* x, void* out, const int32_t* tk_in, const float* tkg_in,
+                 int32_t* tk_out, float* tkg_out, float* logits_out, uint16_t* h_all, void* ws,
+                 hipStream_t st) {
+  if (L == 1)
+    return launch_layer_nl<1>(d, M, L, flags, layers, x, out, tk_in, tkg_in, tk_out, tkg_out,
+                              logits_out, h_all, ws, st);
+  return launch_layer_nl<MOE_MAX_LAYERS>(d, M, L, flags, layers, x, out, tk_in, tkg_in, tk_out,
+                                         tkg_out, logits_out, h_all, ws, st);
 }
 
 int check_ws(const moe_dims* d, int M, int L, void* ws, size_t ws_bytes) {
@@ -379,9 +421,8 @@ int lmhead_argmax(int32_t M, int32_t H, int32_t V, const uint16_t* h, const uint
   if (rc) return rc;
   const int lds = (int)align_up((size_t)M * H * 2, 16) + (MOE_LM_WG / 64) * MOE_MAXM * 8;
   if (lds > di.max_lds) return MOE_E_UNSUPPORTED;
-  if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) !=
-      hipSuccess)
-    return MOE_E_HIP;
+  rc = prepare_kernel((const void*)kern, lds, MOE_LM_WG);
+  if (rc) return rc;
   LmParams p;
   p.M = M;
   p.H = H;

@@ -63,7 +63,10 @@ enum : uint32_t {
 
 constexpr float kRmsEps = 1e-6f;
 
-struct Params {
+// NL: layer weight slots carried in the kernel arguments (1 for single-layer
+// calls keeps the argument block small; the chain takes MOE_MAX_LAYERS).
+template <int NL>
+struct ParamsT {
   int H, E, K, I, S, M, L;
   uint32_t flags;
   int nr_max;         // output rows owned by one workgroup, at most
@@ -83,7 +86,7 @@ struct Params {
   uint64_t* hr_buf;      // [L][M*K][I/2]   tagged bf16 pairs, routed (expert, row) pairs
   uint64_t* y_buf;       // [L][M*K][H]     tagged fp32 down outputs of routed pairs
   uint64_t* res_buf;     // [L+1][M][H/2]   tagged bf16 pairs, residual stream
-  LayerW lw[MOE_MAX_LAYERS];
+  LayerW lw[NL];
 };
 
 struct Small {
@@ -198,8 +201,8 @@ __device__ __forceinline__ float dot_rows(const RowRegs<CPLH>& r, const uint4* x
 // P1 item `it`: router rows (it < NRI) or a shared-expert gate/up row pair.
 // The first unit goes to A; a gate/up item's second unit goes to B when
 // `second` is set.
-template <int CPLH>
-__device__ __forceinline__ void p1_load(const Params& p, int l, int it, int NRI,
+template <int CPLH, class P>
+__device__ __forceinline__ void p1_load(const P& p, int l, int it, int NRI,
                                         RowRegs<CPLH>& A, RowRegs<CPLH>& B, int lane,
                                         bool second) {
   // Row pointers are chosen first and the loads issued unconditionally after,
@@ -226,8 +229,8 @@ __device__ __forceinline__ void p1_load(const Params& p, int l, int it, int NRI,
   if (!router && second) load_rows<CPLH>(B, b0, b1, lane);
 }
 
-template <int CPLH>
-__device__ __forceinline__ void p1_load_second(const Params& p, int l, int it, int NRI,
+template <int CPLH, class P>
+__device__ __forceinline__ void p1_load_second(const P& p, int l, int it, int NRI,
                                                RowRegs<CPLH>& B, int lane) {
   const size_t H = (size_t)p.H, I = (size_t)p.I;
   const size_t j1 = 2 * (size_t)(it - NRI) + 1;
@@ -235,8 +238,8 @@ __device__ __forceinline__ void p1_load_second(const Params& p, int l, int it, i
   load_rows<CPLH>(B, base + j1 * H, base + (I + j1) * H, lane);
 }
 
-template <int CPLH>
-__device__ __forceinline__ void p1_compute(const Params& p, int l, int it, int NRI,
+template <int CPLH, class P>
+__device__ __forceinline__ void p1_compute(const P& p, int l, int it, int NRI,
                                            const RowRegs<CPLH>& A, const RowRegs<CPLH>& B,
                                            const uint4* xs4, uint32_t tag, int lane,
                                            uint32_t dbg) {
@@ -271,8 +274,8 @@ struct DownRegs {
 
 // Down rows [n, min(n + 8*DBLK, n_end)) of expert e: row n + 8b + (lane >> 3)
 // on the 8-lane group of lane in block b.
-template <int CPLI, int DBLK>
-__device__ __forceinline__ void load_down(DownRegs<CPLI, DBLK>& r, const Params& p, int l, int e,
+template <int CPLI, int DBLK, class P>
+__device__ __forceinline__ void load_down(DownRegs<CPLI, DBLK>& r, const P& p, int l, int e,
                                           int n, int n_end, int lane) {
   const int gl = lane >> 3, li = lane & 7;
 #pragma unroll
@@ -423,7 +426,8 @@ __device__ __forceinline__ void topk_fast(const float* lgs, Small* sm, int E, in
   __syncthreads();
 }
 
-__device__ __forceinline__ void topk_rows(const Params& p, const float* lgs, Small* sm, int tid,
+template <class P>
+__device__ __forceinline__ void topk_rows(const P& p, const float* lgs, Small* sm, int tid,
                                           int wv, int lane) {
   const int M = p.M, E = p.E, K = p.K;
   const int nW = (E + 63) >> 6;
@@ -476,7 +480,8 @@ __device__ __forceinline__ void topk_rows(const Params& p, const float* lgs, Sma
 // Routed slots in ascending expert order, their row masks and pair numbering.
 // Built by wave 0 alone (its LDS operations execute in order), then one
 // workgroup barrier publishes the tables.
-__device__ __forceinline__ void build_union(const Params& p, Small* sm, int wv, int lane) {
+template <class P>
+__device__ __forceinline__ void build_union(const P& p, Small* sm, int wv, int lane) {
   if (wv == 0) {
     const int MK = p.M * p.K;  // <= 128: entries (row, rank) i = lane and lane + 64
     if (lane < 32) sm->bm[lane] = 0u;
@@ -548,8 +553,8 @@ __device__ __forceinline__ bool slice_piece(int g, int G, int U, int I, int H, i
 
 // ---------------------------------------------------------------- the kernel
 
-template <int CPLH, int CPLI, int DBLK>
-__global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(Params p) {
+template <int CPLH, int CPLI, int DBLK, int NL>
+__global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
   extern __shared__ __align__(16) unsigned char lds[];
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds + p.lds_xs);
   const uint4* xs4 = reinterpret_cast<const uint4*>(xs);
