@@ -55,7 +55,7 @@ def _dev_lib():
         lib.dg_error_string.argtypes = [ctypes.c_int]
         lib.dg_fill_bf16_dev.restype = ctypes.c_int
         lib.dg_fill_bf16_dev.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int] + \
-            [ctypes.c_int64] * 6 + [ctypes.c_float, ctypes.c_void_p]
+            [ctypes.c_int64] * 6 + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
         _dev = lib
     return _dev
 
@@ -84,12 +84,14 @@ def fill_host(k, rows, cols, sigma, row0=0, col0=0, ld_full=None):
 
 
 def fill_device(out_ptr, keys_dev_ptr, n_blocks, block_stride, rows, cols, sigma,
-                row0=0, col0=0, ld_full=None, stream=0):
-    """Fill n_blocks device slices (block b at out_ptr + 2*b*block_stride bytes)."""
+                row0=0, col0=0, ld_full=None, stream=0, transposed=False):
+    """Fill n_blocks device slices (block b at out_ptr + 2*b*block_stride bytes), each the
+    rows x cols slice stored row-major, or column-major (its transpose) if `transposed`."""
     if ld_full is None:
         ld_full = cols
     rc = _dev_lib().dg_fill_bf16_dev(out_ptr, keys_dev_ptr, n_blocks, block_stride, row0, col0,
-                                     rows, cols, ld_full, scale_for(sigma), stream)
+                                     rows, cols, ld_full, scale_for(sigma), int(transposed),
+                                     stream)
     if rc != 0:
         raise RuntimeError("dg_fill_bf16_dev failed (%d: %s)"
                            % (rc, _dev_lib().dg_error_string(rc).decode()))
