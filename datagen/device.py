@@ -13,7 +13,7 @@ class DeviceLayer:
     def __init__(self, w_router, w_gate_up, w_down):
         self.w_router = w_router      # int16 [E][H]
         self.w_gate_up = w_gate_up    # int16 [E+S][2I][H]
-        self.w_down = w_down          # int16 [E+S][I][H]: each expert's down projection, transposed
+        self.w_down = w_down          # int16 [E+S][H][I]
 
 
 def _keys(keys, dev):
@@ -43,11 +43,10 @@ def make_layer(wl, layer, dev="cuda"):
                     row0=wl.shard * I, ld_full=H, stream=st)
         fill_device(gu.data_ptr() + I * H * 2, kg.data_ptr(), E + S, stride, I, H, SIGMA_W,
                     row0=wl.I_full + wl.shard * I, ld_full=H, stream=st)
-    # the down projection W_d [H][I] of each expert is stored transposed, [I][H]
-    dn = torch.empty((E + S, I, H), dtype=torch.int16, device=dev)
+    dn = torch.empty((E + S, H, I), dtype=torch.int16, device=dev)
     kd = _keys([key(WEIGHT_SEED, wl.family, layer, TENSOR_DOWN, e) for e in range(E + S)], dev)
     fill_device(dn.data_ptr(), kd.data_ptr(), E + S, H * I, H, I, SIGMA_W, col0=wl.shard * I,
-                ld_full=wl.I_full, stream=st, transposed=True)
+                ld_full=wl.I_full, stream=st)
     torch.cuda.synchronize()
     del kr, kg, kd
     return DeviceLayer(wr, gu, dn)

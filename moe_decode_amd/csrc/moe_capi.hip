@@ -68,25 +68,34 @@ bool plan_h_rows(int H, RowPlan* rp) {
   return true;
 }
 
-// Intermediate size: gate/up units are pairs of intermediate indices, and
-// transposed down-projection rows are H long (16-byte aligned when I % 8 == 0).
-bool plan_i_rows(int I) { return I > 0 && I % 8 == 0; }
+// Down-projection rows are split over 8 lanes each (I/64 loads per lane);
+// several 8-row blocks go in flight together when rows are short.
+bool plan_i_rows(int I, RowPlan* rp) {
+  if (I % 64) return false;
+  rp->lpr = 8;
+  rp->cpl = I / 64;
+  return true;
+}
 
-// Compiled variants of the layer kernel: hidden size 256 * CPLH; NL layer
-// weight slots in the kernel arguments.
+int down_blocks(int cpli) {
+  const int b = 10 / cpli;
+  return b < 1 ? 1 : (b > 4 ? 4 : b);
+}
+
+// Compiled (CPLH, CPLI) variants of the layer kernel: hidden size 256 * CPLH,
+// intermediate size 64 * CPLI; NL layer weight slots in the kernel arguments.
 template <int NL>
 using LayerKern = void (*)(ParamsT<NL>);
 
 template <int NL>
-LayerKern<NL> pick_layer_kernel(int cplh) {
-  switch (cplh) {
-    case 1: return moe_layer_kernel<1, NL>;
-    case 2: return moe_layer_kernel<2, NL>;
-    case 4: return moe_layer_kernel<4, NL>;
-    case 8: return moe_layer_kernel<8, NL>;
-    case 10: return moe_layer_kernel<10, NL>;
-    default: return nullptr;
-  }
+LayerKern<NL> pick_layer_kernel(int cplh, int cpli) {
+#define MOE_K(a, b)              \
+  if (cplh == a && cpli == b)   \
+    return moe_layer_kernel<a, b, (10 / b < 1 ? 1 : (10 / b > 4 ? 4 : 10 / b)), NL>;
+  MOE_K(1, 1) MOE_K(10, 12) MOE_K(10, 3) MOE_K(10, 1) MOE_K(10, 4) MOE_K(8, 12) MOE_K(8, 3)
+  MOE_K(4, 4) MOE_K(2, 2)
+#undef MOE_K
+  return nullptr;
 }
 
 // Per-process record of the kernels whose dynamic-LDS limit was raised and
@@ -136,68 +145,62 @@ int check_dims(const moe_dims* d) {
   if (d->n_shared != 0 && d->n_shared != 1) return MOE_E_ARG;
   if (d->top_k > d->n_experts) return MOE_E_ARG;
   if (d->n_experts > MOE_MAX_EXPERTS || d->top_k > MOE_MAX_TOPK) return MOE_E_UNSUPPORTED;
-  RowPlan a;
-  if (!plan_h_rows(d->hidden, &a) || !plan_i_rows(d->inter)) return MOE_E_UNSUPPORTED;
-  if (d->hidden / 8 > MOE_WG) return MOE_E_UNSUPPORTED;  // one down column block per thread
+  RowPlan a, b;
+  if (!plan_h_rows(d->hidden, &a) || !plan_i_rows(d->inter, &b)) return MOE_E_UNSUPPORTED;
   if (d->hidden > 16384 || d->inter > 16384) return MOE_E_UNSUPPORTED;
   return MOE_OK;
 }
 
 // Workspace regions after the header (all tagged 64-bit words):
-//   lg   [L][M][E]               router logits
-//   part [L][256][2][M][H]       per workgroup, piece and selecting row: the
-//                                gate-scaled partial down projection (fp32)
-//   res  [L+1][M][H/2]           residual stream between chained layers (bf16 pairs)
+//   lg  [L][M][E]        router logits
+//   hs  [L][M][I/2]      shared expert SwiGLU output (bf16 pairs)
+//   hr  [L][M*K][I/2]    routed (expert, row) SwiGLU outputs (bf16 pairs)
+//   y   [L][M*K][H]      routed (expert, row) down-projection outputs (fp32)
+//   res [L+1][M][H/2]    residual stream between chained layers (bf16 pairs)
 struct WsLayout {
-  size_t lg, part, res, total;
+  size_t lg, hs, hr, y, res, total;
 };
 
 WsLayout ws_layout(const moe_dims& d, int M, int L) {
   WsLayout w;
-  const size_t E = (size_t)d.n_experts, H = (size_t)d.hidden;
+  const size_t E = (size_t)d.n_experts, H = (size_t)d.hidden, I = (size_t)d.inter;
+  const size_t MK = (size_t)M * d.top_k;
   w.lg = kHdrBytes;
-  w.part = align_up(w.lg + (size_t)L * M * E * 8, 256);
-  w.res = align_up(w.part + (size_t)L * kMaxWG * 2 * M * H * 8, 256);
+  w.hs = align_up(w.lg + (size_t)L * M * E * 8, 256);
+  w.hr = align_up(w.hs + (size_t)L * M * (I / 2) * 8, 256);
+  w.y = align_up(w.hr + (size_t)L * MK * (I / 2) * 8, 256);
+  w.res = align_up(w.y + (size_t)L * MK * H * 8, 256);
   w.total = align_up(w.res + (size_t)(L + 1) * M * (H / 2) * 8, 256);
   return w;
 }
 
 struct LdsPlan {
-  int xs, lg, hw, z, small, total, nr_max, uw_max, zcap;
+  int xs, lg, hs, ysh, ysr, small, total, nr_max;
 };
 
-// LDS of the layer kernel: x [M][H] bf16, logits [M][E] fp32, this
-// workgroup's SwiGLU pairs [M][uw_max], the small tables, and as much room for
-// staged contributions [zcap][nr_max] fp32 as is left (at least one
-// workgroup's worth per token row).
+// LDS of the layer kernel: x [M][H] bf16, logits [M][E] fp32, the SwiGLU rows
+// of the shared expert and of up to two routed slice pieces [3][M][I] bf16, the shared expert's outputs for the owned rows
+// [M][nr_max] fp32, the routed (expert, row) outputs of the owned rows
+// [M*K][nr_max] fp32, and the small tables.
 int plan_lds(const moe_dims& d, int M, int G, int max_lds, LdsPlan* lp) {
   const int H = d.hidden, E = d.n_experts, I = d.inter;
-  if (G > kMaxWG) return MOE_E_UNSUPPORTED;
-  const int slots = M * d.top_k + d.n_shared;
-  if (slots > G) return MOE_E_UNSUPPORTED;  // a workgroup's units then span <= 2 slots
   lp->nr_max = 2 * (((H / 2) + G - 1) / G);
   if (lp->nr_max > 64) return MOE_E_UNSUPPORTED;  // residual rows kept in LDS
-  lp->uw_max = (int)(((long long)slots * (I / 2) + G - 1) / G) + 1;
   size_t o = 0;
   lp->xs = (int)o;
   o = align_up(o + (size_t)M * H * 2, 16);
   lp->lg = (int)o;
   o = align_up(o + (size_t)M * E * 4, 16);
-  lp->hw = (int)o;
-  o = align_up(o + (size_t)M * lp->uw_max * 4, 16);
+  lp->hs = (int)o;  // SwiGLU rows of the down tasks: shared | first piece | second piece
+  o = align_up(o + (size_t)3 * M * I * 2, 16);
+  lp->ysh = (int)o;
+  o = align_up(o + (size_t)M * lp->nr_max * 4, 16);
+  lp->ysr = (int)o;
+  o = align_up(o + (size_t)M * d.top_k * lp->nr_max * 4, 16);
   lp->small = (int)o;
   o = align_up(o + sizeof(Small), 16);
-  lp->z = (int)o;
-  const size_t zrow = (size_t)lp->nr_max * 4;
-  const size_t zmin = (size_t)M * 2 * zrow;  // any chunk holds a few contributions
-  if (o + zmin > (size_t)max_lds) return MOE_E_UNSUPPORTED;
-  size_t zcap = ((size_t)max_lds - o) / zrow;
-  const size_t zall = (size_t)G * 2 * M;  // every possible contribution
-  if (zcap > zall) zcap = zall;
-  lp->zcap = (int)zcap;
-  o = align_up(o + zcap * zrow, 16);
   lp->total = (int)o;
-  return MOE_OK;
+  return o <= (size_t)max_lds ? MOE_OK : MOE_E_UNSUPPORTED;
 }
 
 template <int NL>
@@ -208,9 +211,10 @@ int launch_layer_nl(const moe_dims& d, int M, int L, uint32_t flags,
   DevInfo di;
   int rc = device_info(&di);
   if (rc) return rc;
-  RowPlan ph;
+  RowPlan ph, pi;
   plan_h_rows(d.hidden, &ph);
-  LayerKern<NL> kern = pick_layer_kernel<NL>(ph.cpl);
+  plan_i_rows(d.inter, &pi);
+  LayerKern<NL> kern = pick_layer_kernel<NL>(ph.cpl, pi.cpl);
   if (!kern) return MOE_E_UNSUPPORTED;
   const int G = di.num_cu;
   LdsPlan lp;
@@ -231,12 +235,11 @@ int launch_layer_nl(const moe_dims& d, int M, int L, uint32_t flags,
   p.L = L;
   p.flags = flags;
   p.nr_max = lp.nr_max;
-  p.uw_max = lp.uw_max;
-  p.zcap = lp.zcap;
   p.lds_xs = lp.xs;
   p.lds_lg = lp.lg;
-  p.lds_hw = lp.hw;
-  p.lds_z = lp.z;
+  p.lds_hs = lp.hs;
+  p.lds_ysh = lp.ysh;
+  p.lds_ysr = lp.ysr;
   p.lds_small = lp.small;
   p.x_in = x;
   p.out = out;
@@ -249,7 +252,9 @@ int launch_layer_nl(const moe_dims& d, int M, int L, uint32_t flags,
   unsigned char* base = (unsigned char*)ws;
   p.hdr = (uint32_t*)base;
   p.lg_buf = (uint64_t*)(base + wl.lg);
-  p.part_buf = (uint64_t*)(base + wl.part);
+  p.hs_buf = (uint64_t*)(base + wl.hs);
+  p.hr_buf = (uint64_t*)(base + wl.hr);
+  p.y_buf = (uint64_t*)(base + wl.y);
   p.res_buf = (uint64_t*)(base + wl.res);
   for (int l = 0; l < L; ++l) {
     p.lw[l].wr = layers[l].w_router;

@@ -7,31 +7,33 @@
 //       buffer, later layers from step-tagged residual words); under the
 //       pre-norm chain keep this workgroup's rows of h_l for the residual and
 //       replace x by bf16(RMSNorm(h_l)).
-//   P1  router GEMV rows, spread over the waves of the GPU; logits are
-//       published as step-tagged words.  The first rows are requested before x
-//       arrives ("weights that do not depend on routing load before their
-//       inputs arrive", SGLang Low-Latency Mode, AMD Low-Latency Kernels).
+//   P1  router GEMV rows and the shared expert's gate/up rows, spread over every
+//       wave of the GPU.  The shared expert does not depend on routing, so its
+//       weights stream while the logits travel ("weights that do not depend on
+//       routing load before their inputs arrive", SGLang Low-Latency Mode, AMD
+//       Low-Latency Kernels).  Logits and the shared expert's SwiGLU output are
+//       published as step-tagged words.
 //   P4  every workgroup reads all logits and computes the softmax top-k
 //       itself, so no second device-wide hop is needed.
 //   P5  union of the rows' choices: a bitmap over experts plus population
 //       counts gives each selected expert its slot with no scan over experts or
-//       sort (SGLang Low-Latency Mode, item 3: at most eight rows); the shared
-//       expert joins as one more slot that every row selects with gate 1.
-//   P6  every slot's gate/up rows, cut into one equal, contiguous share of
-//       (slot, intermediate pair) units per workgroup: gate/up GEMV + SwiGLU,
-//       the results kept in LDS.
-//   P7  the same workgroup's share of the down projection: over its own
-//       intermediate indices, for all H outputs (split-K; the down weights are
-//       stored transposed so each intermediate index is one contiguous row),
-//       scaled by the row's gate and published as tagged fp32 partial sums.
-//       No SwiGLU value crosses workgroups, and each workgroup streams its
-//       gate/up and down weights back to back.
-//   P8  each workgroup owns a slice of output rows: it sums every partial for
-//       those rows in a fixed order and rounds once (or adds the residual with
-//       one rounding, or writes the fp32 partial).
+//       sort (SGLang Low-Latency Mode, item 3: at most eight rows).
+//   P6  routed experts, in teams: the routed work (every expert's gate/up rows
+//       plus its down rows, the same amount per expert) is laid on a line and
+//       cut into one equal slice per workgroup.  A slice covers a fraction of at
+//       most two experts; for each it computes the matching share of the
+//       intermediate dimension (gate/up GEMV + SwiGLU, published as tagged bf16
+//       pairs) ...
+//   P7  ... and, once the team has published the expert's whole SwiGLU output,
+//       the same share of the expert's down-projection rows, published as
+//       tagged fp32 values.  The shared expert's down rows are done first by the
+//       owners of those output rows, while the teams finish.
+//   P8  each workgroup owns a slice of output rows and combines
+//       y_shared + sum_k g_k y_k in fp32 in rank order, then rounds once (or adds
+//       the residual with one rounding, or writes the fp32 partial).
 //
 // Every selected expert's weights stream from HBM exactly once per call, for
-// all the token rows that chose it; no two workgroups read the same weights.
+// all the token rows that chose it; no workgroup reads another's weights.
 #pragma once
 
 #include "moe_device.hpp"
@@ -43,13 +45,11 @@ namespace moe {
 #endif
 
 constexpr int kMaxPK = MOE_MAXM * 16;  // max (routed expert, row) pairs = M * K
-constexpr int kMaxSlots = kMaxPK + 1;  // routed slots plus the shared expert
-constexpr int kMaxWG = 256;            // workgroups of the layer kernel, at most
 
 struct LayerW {
   const uint16_t* wr;   // [E][H]
   const uint16_t* wgu;  // [E+S][2I][H]
-  const uint16_t* wd;   // [E+S][I][H]: each expert's down projection, transposed
+  const uint16_t* wd;   // [E+S][H][I]
 };
 
 enum : uint32_t {
@@ -70,10 +70,8 @@ struct ParamsT {
   int H, E, K, I, S, M, L;
   uint32_t flags;
   int nr_max;         // output rows owned by one workgroup, at most
-  int uw_max;         // gate/up units of one workgroup, at most
-  int zcap;           // contributions staged in LDS per round
   // LDS byte offsets
-  int lds_xs, lds_lg, lds_hw, lds_z, lds_small;
+  int lds_xs, lds_lg, lds_hs, lds_ysh, lds_ysr, lds_small;  // lds_hs: [3*M][I] bf16
   const uint16_t* x_in;
   void* out;
   const int32_t* tk_idx_in;
@@ -83,30 +81,28 @@ struct ParamsT {
   float* logits_out;     // [M][E]
   uint16_t* h_all;       // [L+1][M][H] residual stream per layer (optional)
   uint32_t* hdr;
-  uint64_t* lg_buf;      // [L][M][E]              tagged fp32 logits
-  uint64_t* part_buf;    // [L][kMaxWG][2][M][H]   tagged fp32 gate-scaled partial down outputs
-  uint64_t* res_buf;     // [L+1][M][H/2]          tagged bf16 pairs, residual stream
+  uint64_t* lg_buf;      // [L][M][E]       tagged fp32 logits
+  uint64_t* hs_buf;      // [L][M][I/2]     tagged bf16 pairs, shared expert
+  uint64_t* hr_buf;      // [L][M*K][I/2]   tagged bf16 pairs, routed (expert, row) pairs
+  uint64_t* y_buf;       // [L][M*K][H]     tagged fp32 down outputs of routed pairs
+  uint64_t* res_buf;     // [L+1][M][H/2]   tagged bf16 pairs, residual stream
   LayerW lw[NL];
 };
 
 struct Small {
-  int nU, nP, abort_flag, ncontrib;
+  int nU, nP, abort_flag, pad;
   int tk_idx[kMaxPK];
   float tk_gate[kMaxPK];
   int upos[kMaxPK];          // routed slot of (row, rank), -1 if skipped
-  int uexp[kMaxSlots];       // expert id of slot r (slot U: the shared expert, id E)
-  uint32_t umask[kMaxSlots]; // rows that chose slot r
+  int uexp[kMaxPK];          // expert id of routed slot r
+  uint32_t umask[kMaxPK];    // rows that chose routed slot r
+  int pbase[kMaxPK + 1];     // first (slot, row) pair of slot r
   uint32_t bm[32];           // expert bitmap (E <= 1024)
   int bpre[32];              // population-count prefix per bitmap word
   float rn[MOE_MAXM];        // RMSNorm scale per token row
   alignas(16) uint32_t gmax[MOE_MAXM * MOE_WAVES];  // top-k: group maxima per row
   int ccount[MOE_MAXM];                 // top-k: candidates per row
   alignas(16) uint64_t cand[MOE_MAXM * 64];  // top-k: (key << 32 | ~expert) candidates
-  float slot_gate[kMaxSlots * MOE_MAXM];     // gate of (slot, token row); 1 for the shared expert
-  int wtot[MOE_WAVES * MOE_MAXM];            // contribution counts per wave and row
-  int cstart[MOE_MAXM + 1];                  // first contribution of each token row
-  uint16_t clist[kMaxWG * 2 * MOE_MAXM];     // contributions: workgroup << 4 | piece << 3 | row
-  float osum[MOE_MAXM * 64];                 // combined outputs of the owned rows
   uint16_t hres[MOE_MAXM * 64];  // residual input h_l of this workgroup's output rows
 };
 
@@ -171,9 +167,10 @@ __device__ __forceinline__ bool stage_tagged(int n, uint32_t* dst32, uint32_t ta
 // ---------------------------------------------------------------- streaming units
 //
 // A row unit is two weight rows of H bf16 values, the first on lanes 0-31 and
-// the second on lanes 32-63, CPLH 16-byte loads per lane; every unit requests
-// all its weights before using any, and the first router unit of a layer is
-// requested before the layer waits for its input.
+// the second on lanes 32-63, CPLH 16-byte loads per lane.  A down unit is
+// DBLK blocks of 8 down-projection rows (8 lanes per row, CPLI loads per lane).
+// Every task requests all its weights before using any, and the first task of
+// a phase is requested before the phase waits on its inputs.
 
 template <int CPLH>
 struct RowRegs {
@@ -201,38 +198,115 @@ __device__ __forceinline__ float dot_rows(const RowRegs<CPLH>& r, const uint4* x
   return group_sum(acc, 32);
 }
 
-// P1 item `it`: router rows 2it and 2it + 1 (the first on lanes 0-31, the
-// second on lanes 32-63).
+// P1 item `it`: router rows (it < NRI) or a shared-expert gate/up row pair.
+// The first unit goes to A; a gate/up item's second unit goes to B when
+// `second` is set.
 template <int CPLH, class P>
-__device__ __forceinline__ void p1_load(const P& p, int l, int it, RowRegs<CPLH>& A, int lane) {
-  const int e0 = 2 * it, e1 = (2 * it + 1 < p.E) ? 2 * it + 1 : 2 * it;
-  load_rows<CPLH>(A, p.lw[l].wr + (size_t)e0 * p.H, p.lw[l].wr + (size_t)e1 * p.H, lane);
+__device__ __forceinline__ void p1_load(const P& p, int l, int it, int NRI,
+                                        RowRegs<CPLH>& A, RowRegs<CPLH>& B, int lane,
+                                        bool second) {
+  // Row pointers are chosen first and the loads issued unconditionally after,
+  // so the two register buffers never meet in one pointer (which would force
+  // them out of registers).
+  const size_t H = (size_t)p.H, I = (size_t)p.I;
+  const uint16_t *a0, *a1, *b0, *b1;
+  const bool router = it < NRI;
+  if (router) {
+    const int e0 = 2 * it, e1 = (2 * it + 1 < p.E) ? 2 * it + 1 : 2 * it;
+    a0 = p.lw[l].wr + (size_t)e0 * H;
+    a1 = p.lw[l].wr + (size_t)e1 * H;
+    b0 = a0;
+    b1 = a1;
+  } else {
+    const size_t j0 = 2 * (size_t)(it - NRI);
+    const uint16_t* base = p.lw[l].wgu + (size_t)p.E * (2 * I) * H;
+    a0 = base + j0 * H;
+    a1 = base + (I + j0) * H;
+    b0 = base + (j0 + 1) * H;
+    b1 = base + (I + j0 + 1) * H;
+  }
+  load_rows<CPLH>(A, a0, a1, lane);
+  if (!router && second) load_rows<CPLH>(B, b0, b1, lane);
 }
 
 template <int CPLH, class P>
-__device__ __forceinline__ void p1_compute(const P& p, int l, int it, const RowRegs<CPLH>& A,
+__device__ __forceinline__ void p1_load_second(const P& p, int l, int it, int NRI,
+                                               RowRegs<CPLH>& B, int lane) {
+  const size_t H = (size_t)p.H, I = (size_t)p.I;
+  const size_t j1 = 2 * (size_t)(it - NRI) + 1;
+  const uint16_t* base = p.lw[l].wgu + (size_t)p.E * (2 * I) * H;
+  load_rows<CPLH>(B, base + j1 * H, base + (I + j1) * H, lane);
+}
+
+template <int CPLH, class P>
+__device__ __forceinline__ void p1_compute(const P& p, int l, int it, int NRI,
+                                           const RowRegs<CPLH>& A, const RowRegs<CPLH>& B,
                                            const uint4* xs4, uint32_t tag, int lane,
                                            uint32_t dbg) {
   const int H8 = p.H >> 3;
-  const int e = 2 * it + (lane >> 5);
-  const bool publish = e < p.E && (lane & 31) == 0 && !(dbg & DBG_NO_ROUTER_PUBLISH);
+  if (it < NRI) {
+    const int e = 2 * it + (lane >> 5);
+    const bool publish =
+        e < p.E && (lane & 31) == 0 && !(dbg & DBG_NO_ROUTER_PUBLISH);
 #pragma unroll 1
-  for (int m = 0; m < p.M; ++m) {
-    const float acc = dot_rows<CPLH>(A, xs4, H8, m, lane);
-    if (publish) st_tag(p.lg_buf + ((size_t)l * p.M + m) * p.E + e, __float_as_uint(acc), tag);
+    for (int m = 0; m < p.M; ++m) {
+      const float acc = dot_rows<CPLH>(A, xs4, H8, m, lane);
+      if (publish) st_tag(p.lg_buf + ((size_t)l * p.M + m) * p.E + e, __float_as_uint(acc), tag);
+    }
+  } else {
+    const int jp = it - NRI, I2 = p.I >> 1;
+    uint64_t* dst = p.hs_buf + (size_t)l * p.M * I2 + jp;
+#pragma unroll 1
+    for (int m = 0; m < p.M; ++m) {
+      const float a0 = dot_rows<CPLH>(A, xs4, H8, m, lane);
+      const float a1 = dot_rows<CPLH>(B, xs4, H8, m, lane);
+      const uint32_t word = f_to_bf(swiglu(readlane_f(a0, 0), readlane_f(a0, 32))) |
+                            (f_to_bf(swiglu(readlane_f(a1, 0), readlane_f(a1, 32))) << 16);
+      if (lane == 0) st_tag(dst + (size_t)m * I2, word, tag);
+    }
   }
 }
 
-// acc[k] += h * w_k for the eight bf16 values of w (each product exact in fp32).
-__device__ __forceinline__ void fma8(float* acc, const uint4& w, float h) {
-  acc[0] = __builtin_fmaf(h, bf_lo(w.x), acc[0]);
-  acc[1] = __builtin_fmaf(h, bf_hi(w.x), acc[1]);
-  acc[2] = __builtin_fmaf(h, bf_lo(w.y), acc[2]);
-  acc[3] = __builtin_fmaf(h, bf_hi(w.y), acc[3]);
-  acc[4] = __builtin_fmaf(h, bf_lo(w.z), acc[4]);
-  acc[5] = __builtin_fmaf(h, bf_hi(w.z), acc[5]);
-  acc[6] = __builtin_fmaf(h, bf_lo(w.w), acc[6]);
-  acc[7] = __builtin_fmaf(h, bf_hi(w.w), acc[7]);
+template <int CPLI, int DBLK>
+struct DownRegs {
+  uint4 w[DBLK][CPLI];
+};
+
+// Down rows [n, min(n + 8*DBLK, n_end)) of expert e: row n + 8b + (lane >> 3)
+// on the 8-lane group of lane in block b.
+template <int CPLI, int DBLK, class P>
+__device__ __forceinline__ void load_down(DownRegs<CPLI, DBLK>& r, const P& p, int l, int e,
+                                          int n, int n_end, int lane) {
+  const int gl = lane >> 3, li = lane & 7;
+#pragma unroll
+  for (int b = 0; b < DBLK; ++b) {
+    const int row = n + 8 * b + gl;
+    const uint4* src = reinterpret_cast<const uint4*>(
+        p.lw[l].wd + ((size_t)e * p.H + (row < n_end ? row : n)) * p.I);
+#pragma unroll
+    for (int q = 0; q < CPLI; ++q) r.w[b][q] = src[li + 8 * q];
+  }
+}
+
+// y(t, row) = sum_j h_t[j] * W[row][j] for the nrows token rows whose SwiGLU
+// outputs sit in LDS at hv4 (row t at hv4 + t * I8); emit(t, row, y).
+template <int CPLI, int DBLK, typename Emit>
+__device__ __forceinline__ void compute_down(const DownRegs<CPLI, DBLK>& r, int I8, int n,
+                                             int n_end, int nrows, const uint4* hv4, int lane,
+                                             Emit emit) {
+  const int gl = lane >> 3, li = lane & 7;
+#pragma unroll 1
+  for (int t = 0; t < nrows; ++t) {
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int q = 0; q < CPLI; ++q) acc = dot8(r.w[b][q], hv4[t * I8 + li + 8 * q], acc);
+      acc = group_sum(acc, 8);
+      const int row = n + 8 * b + gl;
+      if (li == 0 && row < n_end) emit(t, row, acc);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- P4 / P5
@@ -397,19 +471,16 @@ __device__ __forceinline__ void topk_rows(const P& p, const float* lgs, Small* s
   }
 }
 
-// Routed slots in ascending expert order and their row masks, then the shared
-// expert as slot U (every row), and the gate of every (slot, row).  Built by
-// wave 0 alone (its LDS operations execute in order), then one workgroup
-// barrier publishes the tables.
+// Routed slots in ascending expert order, their row masks and pair numbering.
+// Built by wave 0 alone (its LDS operations execute in order), then one
+// workgroup barrier publishes the tables.
 template <class P>
 __device__ __forceinline__ void build_union(const P& p, Small* sm, int wv, int lane) {
   if (wv == 0) {
-    const int M = p.M, K = p.K;
-    const int MK = M * K;  // <= 128: entries (row, rank) i = lane and lane + 64
+    const int MK = p.M * p.K;  // <= 128: entries (row, rank) i = lane and lane + 64
     if (lane < 32) sm->bm[lane] = 0u;
     sm->umask[lane] = 0u;
     sm->umask[lane + 64] = 0u;
-    if (lane == 0) sm->umask[kMaxPK] = 0u;
     const int ea = lane < MK ? sm->tk_idx[lane] : -1;
     const int eb = lane + 64 < MK ? sm->tk_idx[lane + 64] : -1;
     if (ea >= 0) atomicOr(&sm->bm[ea >> 5], 1u << (ea & 31));
@@ -422,128 +493,70 @@ __device__ __forceinline__ void build_union(const P& p, Small* sm, int wv, int l
     if (lane == 0) sm->nU = U;
     // routed slot of each entry = number of selected experts below it
     int ra = -1, rb = -1;
-    // gate of (slot, row): a row that lists one expert more than once (possible
-    // only for caller-provided routing) weights it by the sum of those gates,
-    // added in rank order by the entry that lists it first
-    auto row_gate = [&](int i, int e) __attribute__((always_inline)) -> float {
-      const int m0 = (i / K) * K;
-      for (int k = m0; k < i; ++k)
-        if (sm->tk_idx[k] == e) return -1.0f;  // not the first listing
-      float gsum = 0.0f;
-      for (int k = i; k < m0 + K; ++k)
-        if (sm->tk_idx[k] == e) gsum += sm->tk_gate[k];
-      return gsum;
-    };
     if (ea >= 0) {
       ra = sm->bpre[ea >> 5] + __builtin_popcount(sm->bm[ea >> 5] & ((1u << (ea & 31)) - 1u));
       sm->uexp[ra] = ea;
-      atomicOr(&sm->umask[ra], 1u << (lane / K));
-      const float gs = row_gate(lane, ea);
-      if (gs >= 0.0f) sm->slot_gate[ra * MOE_MAXM + lane / K] = gs;
+      atomicOr(&sm->umask[ra], 1u << (lane / p.K));
     }
     if (eb >= 0) {
       rb = sm->bpre[eb >> 5] + __builtin_popcount(sm->bm[eb >> 5] & ((1u << (eb & 31)) - 1u));
       sm->uexp[rb] = eb;
-      atomicOr(&sm->umask[rb], 1u << ((lane + 64) / K));
-      const float gs = row_gate(lane + 64, eb);
-      if (gs >= 0.0f) sm->slot_gate[rb * MOE_MAXM + (lane + 64) / K] = gs;
+      atomicOr(&sm->umask[rb], 1u << ((lane + 64) / p.K));
     }
     if (lane < MK) sm->upos[lane] = ra;
     if (lane + 64 < MK) sm->upos[lane + 64] = rb;
-    if (p.S) {
-      if (lane == 0) {
-        sm->uexp[U] = p.E;
-        sm->umask[U] = (1u << M) - 1u;
-      }
-      if (lane < M) sm->slot_gate[U * MOE_MAXM + lane] = 1.0f;
+    // first (slot, row) pair of every slot
+    const int c0 = lane < U ? __builtin_popcount(sm->umask[lane]) : 0;
+    const int c1 = lane + 64 < U ? __builtin_popcount(sm->umask[lane + 64]) : 0;
+    const int i0 = wave_incl_scan(c0);
+    const int t0 = __builtin_amdgcn_readlane(i0, 63);
+    const int i1 = wave_incl_scan(c1);
+    sm->pbase[lane] = i0 - c0;
+    sm->pbase[lane + 64] = t0 + i1 - c1;
+    if (lane == 63) {
+      sm->nP = t0 + i1;
+      sm->pbase[kMaxPK] = t0 + i1;
     }
   }
   __syncthreads();
 }
 
-// Piece q (0 or 1) of a workgroup's gate/up units [us0, us1): slot r and its
-// units [a, b).  A range of at most I/2 units spans at most two slots.
-__device__ __forceinline__ bool piece_of(int us0, int us1, int I2, int q, int& r, int& a,
-                                         int& b) {
-  if (us0 >= us1) return false;
-  const int r0 = us0 / I2, e0 = (r0 + 1) * I2;
-  if (q == 0) {
-    r = r0;
-    a = us0;
-    b = us1 < e0 ? us1 : e0;
-    return true;
-  }
-  if (us1 <= e0) return false;
-  r = r0 + 1;
-  a = e0;
-  b = us1;
+// Piece q (0 or 1) of this workgroup's slice of the routed work: expert slot r,
+// intermediate range [j0, j1) and down rows [n0, n1).  Returns false if none.
+struct Piece {
+  int r, j0, j1, n0, n1;
+};
+
+__device__ __forceinline__ bool slice_piece(int g, int G, int U, int I, int H, int q, Piece& pc) {
+  if (U <= 0) return false;
+  const long long s0 = (long long)g * U, s1 = (long long)(g + 1) * U;  // in units of 1/G
+  const int r = (int)(s0 / G) + q;
+  if ((long long)r * G >= s1 || r >= U) return false;
+  long long a = s0 - (long long)r * G, b = s1 - (long long)r * G;
+  if (a < 0) a = 0;
+  if (b > G) b = G;
+  if (b <= a) return false;
+  const int I2 = I >> 1, H2 = H >> 1;
+  pc.r = r;
+  pc.j0 = 2 * (int)((a * I2 + G / 2) / G);
+  pc.j1 = 2 * (int)((b * I2 + G / 2) / G);
+  pc.n0 = 2 * (int)((a * H2 + G / 2) / G);
+  pc.n1 = 2 * (int)((b * H2 + G / 2) / G);
   return true;
-}
-
-// The contribution list of the combine: for each token row m, in order of
-// workgroup g, piece q and row index t within the piece's slot, one entry
-// (g << 4 | q << 3 | t) for every piece whose slot row m selected.  Workgroup
-// g's units are the same equal share [g*NU/G, (g+1)*NU/G) the producer took.
-// Thread g describes workgroup g; per-wave ballots and one barrier place the
-// entries.
-__device__ __forceinline__ void build_contributions(Small* sm, int G, int NU, int I2, int M,
-                                                    int tid, int wv, int lane) {
-  const int gg = tid;
-  int r0 = 0, r1 = 0;
-  uint32_t m0 = 0u, m1 = 0u;  // rows of piece 0 / piece 1 of workgroup gg
-  if (gg < G) {
-    const int us0 = (int)(((long long)gg * NU) / G), us1 = (int)(((long long)(gg + 1) * NU) / G);
-    int a, b;
-    if (piece_of(us0, us1, I2, 0, r0, a, b)) m0 = sm->umask[r0];
-    if (piece_of(us0, us1, I2, 1, r1, a, b)) m1 = sm->umask[r1];
-  }
-  const uint64_t lt = (1ull << lane) - 1ull;
-  int pre[MOE_MAXM];
-#pragma unroll
-  for (int m = 0; m < MOE_MAXM; ++m) {
-    const uint64_t b0 = __ballot((m0 >> m) & 1u);
-    const uint64_t b1 = __ballot((m1 >> m) & 1u);
-    pre[m] = __builtin_popcountll(b0 & lt) + __builtin_popcountll(b1 & lt);
-    if (lane == 0 && m < M)
-      sm->wtot[wv * MOE_MAXM + m] = __builtin_popcountll(b0) + __builtin_popcountll(b1);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int m = 0; m < M; ++m) {
-      sm->cstart[m] = acc;
-      for (int w = 0; w < MOE_WAVES; ++w) acc += sm->wtot[w * MOE_MAXM + m];
-    }
-    sm->cstart[M] = acc;
-    sm->ncontrib = acc;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int m = 0; m < MOE_MAXM; ++m) {
-    if (m < M && (((m0 | m1) >> m) & 1u)) {
-      int pos = sm->cstart[m] + pre[m];
-      for (int w = 0; w < wv; ++w) pos += sm->wtot[w * MOE_MAXM + m];
-      if ((m0 >> m) & 1u)
-        sm->clist[pos++] = (uint16_t)((gg << 4) | (0 << 3) |
-                                      __builtin_popcount(m0 & ((1u << m) - 1u)));
-      if ((m1 >> m) & 1u)
-        sm->clist[pos] = (uint16_t)((gg << 4) | (1 << 3) |
-                                    __builtin_popcount(m1 & ((1u << m) - 1u)));
-    }
-  }
-  __syncthreads();
 }
 
 // ---------------------------------------------------------------- the kernel
 
-template <int CPLH, int NL>
+template <int CPLH, int CPLI, int DBLK, int NL>
 __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
   extern __shared__ __align__(16) unsigned char lds[];
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds + p.lds_xs);
   const uint4* xs4 = reinterpret_cast<const uint4*>(xs);
   float* lgs = reinterpret_cast<float*>(lds + p.lds_lg);
-  uint32_t* hw = reinterpret_cast<uint32_t*>(lds + p.lds_hw);  // [M][uw_max] SwiGLU pairs
-  float* zs = reinterpret_cast<float*>(lds + p.lds_z);         // [zcap][nr_max] contributions
+  uint32_t* hs32 = reinterpret_cast<uint32_t*>(lds + p.lds_hs);
+  const uint4* hs4 = reinterpret_cast<const uint4*>(lds + p.lds_hs);
+  float* ysh = reinterpret_cast<float*>(lds + p.lds_ysh);
+  float* ysr = reinterpret_cast<float*>(lds + p.lds_ysr);
   Small* sm = reinterpret_cast<Small*>(lds + p.lds_small);
 
   const int G = gridDim.x, g = blockIdx.x;
@@ -577,11 +590,12 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
   for (int l = 0; l < p.L; ++l) {
     sbase = l == 0 ? 0 : (l == 1 ? 10 : (l == p.L - 1 ? 20 : -1));
     MOE_STAMP(0);
-    // ---------------- P1 prefetch: this wave's first router rows do not
-    // depend on x, so their loads fly while x is staged
+    // ---------------- P1 prefetch: this wave's first router / shared gate-up rows
+    // do not depend on x, so their loads fly while x is staged
     const int NRI = topk_in ? 0 : (E + 1) >> 1;
+    const int NSI = (router_only || !S) ? 0 : I2;
     RowRegs<CPLH> A, B;
-    if (gw < NRI) p1_load<CPLH>(p, l, gw, A, lane);
+    if (gw < NRI + NSI) p1_load<CPLH>(p, l, gw, NRI, A, B, lane, false);
 
     // ---------------- P0: layer input -> LDS
     if (l == 0) {
@@ -635,10 +649,13 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     __syncthreads();
     MOE_STAMP(1);
 
-    // ---------------- P1: router rows
-    for (int it = gw; it < NRI; it += NW) {
-      if (it != gw) p1_load<CPLH>(p, l, it, A, lane);
-      p1_compute<CPLH>(p, l, it, A, xs4, tag, lane, dbg);
+    // ---------------- P1: router rows + shared expert gate/up rows
+    for (int it = gw; it < NRI + NSI; it += NW) {
+      if (it != gw)
+        p1_load<CPLH>(p, l, it, NRI, A, B, lane, true);
+      else if (it >= NRI)  // the prefetched gate/up item still needs its second row
+        p1_load_second<CPLH>(p, l, it, NRI, B, lane);
+      p1_compute<CPLH>(p, l, it, NRI, A, B, xs4, tag, lane, dbg);
     }
     MOE_STAMP(2);
 
@@ -688,30 +705,35 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       if (router_only) break;
     }
 
-    // ---------------- P5: routed slots (+ the shared expert as slot U)
+    // ---------------- P5: routed slots
     build_union(p, sm, wv, lane);
     const int U = sm->nU;
-    const int US = U + S;
     MOE_STAMP(4);
 
-    // ---------------- P6: this workgroup's gate/up units
-    // Units u = (slot r, intermediate pair jp), slot-major (u = r * I/2 + jp);
-    // the workgroup takes the contiguous range [us0, us1), an equal share of
-    // all units, which spans at most two slots ("pieces").  A wave's unit is
-    // gate/up rows 2jp and 2jp + 1 of slot r, all requested before any is
-    // used; the SwiGLU pair of every selecting row stays in LDS.
-    const int NU = US * I2;
-    const int us0 = (int)(((long long)g * NU) / G), us1 = (int)(((long long)(g + 1) * NU) / G);
-    const int UW = us1 - us0;
+    // ---------------- P6: this workgroup's slice of the routed gate/up rows
+    // Task f over the slice's intermediate pairs (wave wv takes f = wv,
+    // wv + WAVES, ...): gate/up rows j = 2jp (unit A) and 2jp + 1 (unit B) are
+    // both requested before either is used.
+    uint64_t* hr_l = p.hr_buf + (size_t)l * MK * I2;
+    Piece pc0, pc1;
+    const bool has0 = slice_piece(g, G, U, I, H, 0, pc0);
+    const bool has1 = slice_piece(g, G, U, I, H, 1, pc1);
+    const int F0 = has0 ? (pc0.j1 - pc0.j0) >> 1 : 0;
+    const int F1 = has1 ? (pc1.j1 - pc1.j0) >> 1 : 0;
     {
+      const int r0s = has0 ? pc0.r : 0, r1s = has1 ? pc1.r : 0;
+      const int jb0 = has0 ? pc0.j0 >> 1 : 0, jb1 = has1 ? (pc1.j0 >> 1) - F0 : 0;
       const int H8 = H >> 3;
-      for (int u = us0 + wv; u < us1; u += MOE_WAVES) {
-        const int rr = u / I2, jp = u - rr * I2;
+      for (int f = wv; f < F0 + F1; f += MOE_WAVES) {
+        const int jp = f + (f < F0 ? jb0 : jb1);
+        const int rr = f < F0 ? r0s : r1s;
         const uint16_t* base = p.lw[l].wgu + (size_t)sm->uexp[rr] * (2 * (size_t)I) * H;
         const size_t j0 = 2 * (size_t)jp;
         load_rows<CPLH>(A, base + j0 * H, base + ((size_t)I + j0) * H, lane);
         load_rows<CPLH>(B, base + (j0 + 1) * H, base + ((size_t)I + j0 + 1) * H, lane);
-        uint32_t bits = sm->umask[rr];
+        const uint32_t mask = sm->umask[rr];
+        uint64_t* dst = hr_l + (size_t)sm->pbase[rr] * I2 + jp;
+        uint32_t bits = mask;
         int t = 0;
 #pragma unroll 1
         while (bits) {
@@ -721,88 +743,80 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
           const float a1 = dot_rows<CPLH>(B, xs4, H8, m, lane);
           const uint32_t word = f_to_bf(swiglu(readlane_f(a0, 0), readlane_f(a0, 32))) |
                                 (f_to_bf(swiglu(readlane_f(a1, 0), readlane_f(a1, 32))) << 16);
-          if (lane == 0) hw[t * p.uw_max + (u - us0)] = word;
+          if (lane == 0) st_tag(dst + (size_t)t * I2, word, tag);
           ++t;
         }
       }
     }
-    __syncthreads();
     MOE_STAMP(5);
 
-    // ---------------- P7: down projection, split over the intermediate dim
-    // For each piece (slot r, units [a, b)) this workgroup computes the partial
-    // down projection over its own 2(b - a) intermediate indices for ALL H
-    // outputs, y_t[n] = sum_j h_t[j] * Wd[e][n][j] (Wd stored transposed, so
-    // row j is contiguous), scales it by the gate of the row, and publishes it
-    // as tagged fp32 words.  No SwiGLU value crosses workgroups.  Thread c
-    // owns output columns 8c .. 8c+7 and streams DB intermediate rows at a time.
-    uint64_t* part_l = p.part_buf + (size_t)l * kMaxWG * 2 * M * H;
+    // ---------------- P7: down projection
+    // This workgroup's down tasks: the shared expert's blocks of its own output
+    // rows, then its slice's blocks of the routed experts, after the SwiGLU
+    // inputs of all of them are staged in LDS with one batched wait.
+    uint64_t* y_l = p.y_buf + (size_t)l * MK * H;
     {
-      const int H8 = H >> 3;
-      const int c = tid;
-      for (int q = 0; q < 2; ++q) {
-        int r, a, b;
-        if (!piece_of(us0, us1, I2, q, r, a, b)) break;
-        const int e = sm->uexp[r];
-        const uint32_t mask = sm->umask[r];
-        const int nt = __builtin_popcount(mask);
-        float acc[MOE_MAXM][8];
-#pragma unroll
-        for (int t = 0; t < MOE_MAXM; ++t)
-#pragma unroll
-          for (int k = 0; k < 8; ++k) acc[t][k] = 0.0f;
-        const uint16_t* wd = p.lw[l].wd + (size_t)e * I * H;
-        constexpr int DB = 4;  // intermediate pairs per batch (2 rows each)
-        for (int u = a; u < b; u += DB) {
-          uint4 w[2 * DB];
-#pragma unroll
-          for (int k = 0; k < DB; ++k) {
-            const int uu = (u + k < b) ? u + k : u;
-            const size_t j = 2 * (size_t)(uu - r * I2);
-            const uint4* r0p = reinterpret_cast<const uint4*>(wd + j * H);
-            const uint4* r1p = reinterpret_cast<const uint4*>(wd + (j + 1) * H);
-            w[2 * k] = c < H8 ? r0p[c] : make_uint4(0, 0, 0, 0);
-            w[2 * k + 1] = c < H8 ? r1p[c] : make_uint4(0, 0, 0, 0);
-          }
-#pragma unroll
-          for (int k = 0; k < DB; ++k) {
-            if (u + k < b) {
-#pragma unroll
-              for (int t = 0; t < MOE_MAXM; ++t) {
-                if (t < nt) {
-                  const uint32_t hword = hw[t * p.uw_max + (u + k - us0)];
-                  const float h0 = bf_lo(hword), h1 = bf_hi(hword);
-                  fma8(acc[t], w[2 * k], h0);
-                  fma8(acc[t], w[2 * k + 1], h1);
-                }
-              }
-            }
-          }
+      const int BR = 8 * DBLK;
+      const int nbs = (S && NR > 0) ? (NR + BR - 1) / BR : 0;
+      const int nb0 = has0 ? (pc0.n1 - pc0.n0 + BR - 1) / BR : 0;
+      const int nb1 = has1 ? (pc1.n1 - pc1.n0 + BR - 1) / BR : 0;
+      const int nrow0 = has0 ? __builtin_popcount(sm->umask[pc0.r]) : 0;
+      const int nrow1 = has1 ? __builtin_popcount(sm->umask[pc1.r]) : 0;
+      const int ntask = nbs + nb0 + nb1;
+      // task f -> (expert, first row, end row, h rows in LDS, rows, emit kind)
+      auto task = [&](int f, int& e, int& n, int& n_end, int& kind) __attribute__((always_inline)) {
+        if (f < nbs) {
+          e = E; n = n0 + f * BR; n_end = n0 + NR; kind = 0;
+        } else if (f < nbs + nb0) {
+          e = sm->uexp[pc0.r]; n = pc0.n0 + (f - nbs) * BR; n_end = pc0.n1; kind = 1;
+        } else {
+          e = sm->uexp[pc1.r]; n = pc1.n0 + (f - nbs - nb0) * BR; n_end = pc1.n1; kind = 2;
         }
-        // publish gate * partial for each selecting row
-        if (c < H8) {
-          uint32_t bits = mask;
-#pragma unroll
-          for (int t = 0; t < MOE_MAXM; ++t) {
-            if (t < nt) {
-              const int m = __builtin_ctz(bits);
-              bits &= bits - 1u;
-              const float gt = sm->slot_gate[r * MOE_MAXM + m];
-              uint64_t* dst = part_l + (((size_t)g * 2 + q) * M + t) * H + 8 * c;
-#pragma unroll
-              for (int k = 0; k < 8; ++k) st_tag(dst + k, __float_as_uint(gt * acc[t][k]), tag);
-            }
-          }
+      };
+      DownRegs<CPLI, DBLK> DA;
+      int e, n, n_end, kind;
+      // SwiGLU inputs of all this workgroup's down tasks -> LDS: shared | piece 0 | piece 1
+      const int ws0 = nbs ? M * I2 : 0;
+      const int ws1 = nb0 ? nrow0 * I2 : 0;
+      const int ws2 = nb1 ? nrow1 * I2 : 0;
+      const uint64_t* hsrc = p.hs_buf + (size_t)l * M * I2;
+      const uint64_t* r0src = hr_l + (size_t)(has0 ? sm->pbase[pc0.r] : 0) * I2;
+      const uint64_t* r1src = hr_l + (size_t)(has1 ? sm->pbase[pc1.r] : 0) * I2;
+      if (!stage_tagged<4>(ws0 + ws1 + ws2, hs32, tag, wt, tid, [&](int i) {
+            return i < ws0 ? hsrc + i : (i < ws0 + ws1 ? r0src + (i - ws0) : r1src + (i - ws0 - ws1));
+          }))
+        sm->abort_flag = 1;
+      __syncthreads();
+      MOE_STAMP(6);
+      if (sm->abort_flag == 1) break;
+      const int pb0 = has0 ? sm->pbase[pc0.r] : 0, pb1 = has1 ? sm->pbase[pc1.r] : 0;
+      auto run = [&](int f, const DownRegs<CPLI, DBLK>& R) __attribute__((always_inline)) {
+        int e2, nn, ne, kd;
+        task(f, e2, nn, ne, kd);
+        if (kd == 0) {
+          compute_down<CPLI, DBLK>(R, I8, nn, ne, M, hs4, lane, [&](int m, int row, float y) {
+            ysh[m * p.nr_max + (row - n0)] = y;
+          });
+        } else {
+          const uint4* hv = hs4 + (size_t)(ws0 + (kd == 2 ? ws1 : 0)) / 4;
+          const int pb = kd == 1 ? pb0 : pb1;
+          compute_down<CPLI, DBLK>(R, I8, nn, ne, kd == 1 ? nrow0 : nrow1, hv, lane,
+                                   [&](int t, int row, float y) {
+                                     st_tag(y_l + (size_t)(pb + t) * H + row, __float_as_uint(y),
+                                            tag);
+                                   });
         }
+      };
+      for (int f = wv; f < ntask; f += MOE_WAVES) {
+        task(f, e, n, n_end, kind);
+        load_down<CPLI, DBLK>(DA, p, l, e, n, n_end, lane);
+        run(f, DA);
       }
+      __syncthreads();
     }
-    MOE_STAMP(6);
+    MOE_STAMP(7);
 
     // ---------------- P8: combine (+ residual) and hand off
-    // This workgroup owns output rows [n0, n0 + NR).  Its contributions are
-    // every workgroup's published partials for the rows of the token rows they
-    // cover, listed by token row, then workgroup, piece and row (a fixed order,
-    // so the sum is deterministic); they are staged in LDS in chunks and summed.
     const bool last = (l == p.L - 1);
     if (last && (p.flags & F_ALIAS)) {
       if (tid == 0) {
@@ -815,45 +829,34 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       __syncthreads();
       if (sm->abort_flag == 1) break;
     }
-    build_contributions(sm, G, NU, I2, M, tid, wv, lane);
-    MOE_STAMP(7);
+    if (NR > 0) {
+      // this workgroup's rows of every routed (expert, row) output -> LDS
+      const int nP = sm->nP;
+      if (!stage_tagged<4>(nP * NR, reinterpret_cast<uint32_t*>(ysr), tag, wt, tid,
+                           [&](int i) {
+                             const int pr = i / NR;
+                             return y_l + (size_t)pr * H + n0 + (i - pr * NR);
+                           }))
+        sm->abort_flag = 1;
+    }
+    __syncthreads();
+    if (sm->abort_flag == 1) break;
     {
-      const int NC = sm->ncontrib;
-      for (int i = tid; i < M * NR; i += MOE_WG) sm->osum[i] = 0.0f;
-      __syncthreads();
-      for (int c0 = 0; c0 < NC; c0 += p.zcap) {
-        const int nc = (NC - c0 < p.zcap) ? NC - c0 : p.zcap;
-        if (NR > 0 && !stage_tagged<8>(nc * NR, reinterpret_cast<uint32_t*>(zs), tag, wt, tid,
-                                       [&](int i) {
-                                         const int ci = i / NR;
-                                         const uint32_t cd = sm->clist[c0 + ci];
-                                         const int cg = (int)(cd >> 4), cq = (int)((cd >> 3) & 1u),
-                                                   ct = (int)(cd & 7u);
-                                         return part_l + (((size_t)cg * 2 + cq) * M + ct) * H + n0 +
-                                                (i - ci * NR);
-                                       }))
-          sm->abort_flag = 1;
-        __syncthreads();
-        if (sm->abort_flag == 1) break;
-        // output o = (m, nl): its contributions in this chunk are list entries
-        // [cstart[m], cstart[m+1]) clipped to [c0, c0 + nc); one wave per
-        // output, lanes strided over the entries, a fixed DPP tree at the end
-        for (int o = wv; o < M * NR; o += MOE_WAVES) {
-          const int m = o / NR, nl = o - m * NR;
-          const int ka = max(sm->cstart[m], c0), kb = min(sm->cstart[m + 1], c0 + nc);
-          float v = 0.0f;
-          for (int k = ka + lane; k < kb; k += 64) v += zs[(k - c0) * NR + nl];
-          v = group_sum(v, 64);
-          if (lane == 0) sm->osum[o] += v;
-        }
-        __syncthreads();
-      }
-      if (sm->abort_flag == 1) break;
       for (int i = tid; i < (NR >> 1) * M; i += MOE_WG) {
         const int np = i / M, m = i - np * M;
         const int nl = 2 * np, n = n0 + nl;
-        const float a0 = sm->osum[m * NR + nl];
-        const float a1 = sm->osum[m * NR + nl + 1];
+        float a0 = S ? ysh[m * p.nr_max + nl] : 0.0f;
+        float a1 = S ? ysh[m * p.nr_max + nl + 1] : 0.0f;
+        for (int k = 0; k < K; ++k) {
+          const int r = sm->upos[m * K + k];
+          if (r < 0) continue;
+          const int pr = sm->pbase[r] + __builtin_popcount(sm->umask[r] & ((1u << m) - 1u));
+          const float gk = sm->tk_gate[m * K + k];
+          const float t0 = gk * ysr[pr * NR + nl];
+          const float t1 = gk * ysr[pr * NR + nl + 1];
+          a0 = a0 + t0;
+          a1 = a1 + t1;
+        }
         if (p.flags & F_RESIDUAL) {
           const float h0 = bf_to_f(sm->hres[m * p.nr_max + nl]);
           const float h1 = bf_to_f(sm->hres[m * p.nr_max + nl + 1]);

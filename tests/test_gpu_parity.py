@@ -83,8 +83,7 @@ def test_device_generator_matches_host(gpu, dw):
         e = 7 if wl.E > 7 else 0
         assert np.array_equal(D.from_device_bf16(L.w_router), W.router(wl, 0))
         assert np.array_equal(D.from_device_bf16(L.w_gate_up[e]), W.expert_gate_up(wl, 0, e))
-        # down projections are stored transposed on the device ([I][H] per expert)
-        assert np.array_equal(D.from_device_bf16(L.w_down[wl.E]), W.expert_down(wl, 0, wl.E).T)
+        assert np.array_equal(D.from_device_bf16(L.w_down[wl.E]), W.expert_down(wl, 0, wl.E))
 
 
 # ------------------------------------------------------------------ router
