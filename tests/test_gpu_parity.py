@@ -442,6 +442,50 @@ def test_lmhead_ragged_and_planted_ties(gpu, M, V):
     assert np.array_equal(tok.cpu().numpy(), got)
 
 
+def test_repeated_calls_are_bit_identical(gpu, dw):
+    """The same call on a fresh workspace, four times: identical routing and
+    output bits (no summation order depends on timing)."""
+    wl = W.C3
+    x = x_tiefree(wl, 6)
+    ws = md.new_workspace(_dims(wl), 6, 1)
+    first = _layer_gpu(wl, dw, gpu, x, ws=ws)
+    for _ in range(3):
+        again = _layer_gpu(wl, dw, gpu, x, ws=ws)
+        assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1])
+
+
+@pytest.mark.parametrize("E", [256, 64])
+def test_layer_fewer_experts_than_groups_times_k(gpu, E):
+    """E = 256 and 64 with K = 8: fewer 64-expert groups than K, so every row
+    takes the plain selection rounds; full Ling-width layer otherwise."""
+    import torch
+    wl = replace(W.C2, E=E, M=2)
+    # tie-free rows: the oracle's K-th and (K+1)-th logits at least 1e-3 apart
+    wr = W.router(wl, 0)
+    attempts = []
+    for a in range(64):
+        lg = oracle.router_logits(W.x_rows(wl, [a]), wr)
+        if runner.router_margin(lg, wl.K)[0] >= 1e-3:
+            attempts.append(a)
+        if len(attempts) == 2:
+            break
+    x = W.x_rows(wl, attempts)
+    L = D.make_layer(wl, 0)
+    try:
+        d = _dims(wl)
+        ws = md.new_workspace(d, 2, 1)
+        out = _empty((2, wl.H), torch.int16, gpu)
+        idx = _empty((2, wl.K), torch.int32, gpu)
+        say("layer_chain LAYER_ONLY E=%d M=2" % E)
+        md.check(md.moe_layer_chain(d, 2, [_lw(L)], D.to_device(x), out, md.MOE_OUT_BF16,
+                                    md.MOE_CHAIN_LAYER_ONLY, idx, ws))
+        md.check(md.moe_last_device_status(ws))
+        _check_layer(wl, x, idx.cpu().numpy(), out.cpu().numpy().view(np.uint16))
+    finally:
+        del L
+        torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ workspace state
 
 def test_state_is_clean_across_calls_and_call_types(gpu, dw):
