@@ -20,6 +20,8 @@ TENSOR_ROUTER = 2
 TENSOR_GATE_UP = 3
 TENSOR_DOWN = 4
 TENSOR_LMHEAD = 5
+TENSOR_BIAS = 6     # per-expert router selection bias
+TENSOR_GAIN = 7     # RMSNorm gain in front of the router and experts
 
 SIGMA_W = 0.02   # weights ~ N(0, 0.02^2)
 SIGMA_X = 1.0    # inputs ~ N(0, 1)
@@ -81,6 +83,13 @@ def fill_host(k, rows, cols, sigma, row0=0, col0=0, ld_full=None):
     _host_lib().dg_fill_bf16(out.ctypes.data, k, row0, col0, rows, cols, ld_full,
                              scale_for(sigma))
     return out
+
+
+def round_bf16_bits(f):
+    """fp32 values -> bf16 bits, round to nearest even (finite inputs only)."""
+    u = np.ascontiguousarray(f, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
 
 
 def fill_device(out_ptr, keys_dev_ptr, n_blocks, block_stride, rows, cols, sigma,

@@ -9,8 +9,9 @@ dg_core.h).  Nothing here computes any part of the MoE layer.
 """
 from dataclasses import dataclass
 
-from . import (FAMILY_LING, FAMILY_TINY, SIGMA_W, SIGMA_X, TENSOR_DOWN, TENSOR_GATE_UP,
-               TENSOR_LMHEAD, TENSOR_ROUTER, TENSOR_X, fill_host, key)
+from . import (FAMILY_LING, FAMILY_TINY, SIGMA_W, SIGMA_X, TENSOR_BIAS, TENSOR_DOWN,
+               TENSOR_GAIN, TENSOR_GATE_UP, TENSOR_LMHEAD, TENSOR_ROUTER, TENSOR_X, fill_host,
+               key, round_bf16_bits)
 
 WEIGHT_SEED = 0x5EED0001
 
@@ -33,7 +34,10 @@ class Workload:
     shard: int = 0
     out_f32: bool = False
     residual: bool = False
-    prenorm: bool = False   # chain: each layer's MoE sees bf16(RMSNorm(h_l))
+    prenorm: bool = False   # each layer's MoE sees bf16(RMSNorm(h_l) * gain)
+    bias_sigma: float = 0.0     # router selection bias ~N(0, bias_sigma^2) per expert (0: none)
+    gain_sigma: float = 0.0     # norm gain ~1 + N(0, gain_sigma^2) per channel (0: unit gain)
+    routed_scale: float = 1.0   # routed scaling factor of the combine
 
     @property
     def I_full(self):
@@ -48,6 +52,10 @@ class Workload:
     def layer_bytes(self):
         return self.router_bytes() + (self.E + self.S) * self.expert_bytes()
 
+    def front_bytes(self):
+        """Bytes of the router front's small vectors: fp32 bias [E], bf16 gain [H]."""
+        return (4 * self.E if self.bias_sigma else 0) + (2 * self.H if self.gain_sigma else 0)
+
 
 C1 = Workload("tiny_moe_layer_m1", 1, FAMILY_TINY, H=256, E=16, K=2, I=64, S=1, M=1, x_seed=101)
 C2 = Workload("ling_moe_layer_m1", 2, FAMILY_LING, H=2560, E=512, K=8, I=768, S=1, M=1,
@@ -59,7 +67,17 @@ C4 = Workload("ling_tp4_shard_moe_layer_m6", 4, FAMILY_LING, H=2560, E=512, K=8,
 C5 = Workload("ling_chain16_lmhead_m6", 5, FAMILY_LING, H=2560, E=512, K=8, I=768, S=1, M=6,
               x_seed=505, n_layers=16, V=157184, residual=True, prenorm=True)
 
+# The router front on a single layer: RMSNorm with a gain vector, a per-expert
+# selection bias and a routed scaling factor (2.5: not a power of two, so the
+# scaling is a real rounding step).  Bias sigma 0.25 moves about a third of the
+# selections at E = 512 (the logits have std ~1 and the K-th gap ~0.05).
+C6 = Workload("tiny_moe_layer_front_m3", 6, FAMILY_TINY, H=256, E=16, K=2, I=64, S=1, M=3,
+              x_seed=606, prenorm=True, bias_sigma=0.25, gain_sigma=0.1, routed_scale=2.5)
+C7 = Workload("ling_moe_layer_front_m6", 7, FAMILY_LING, H=2560, E=512, K=8, I=768, S=1, M=6,
+              x_seed=707, prenorm=True, bias_sigma=0.25, gain_sigma=0.1, routed_scale=2.5)
+
 ALL = (C1, C2, C3, C4, C5)
+FRONT = (C6, C7)
 
 
 # ---- host slices ------------------------------------------------------------
@@ -92,6 +110,26 @@ def expert_down(wl, layer, e):
     """[H][I]: this shard's columns of the full [H][I_full] tensor."""
     k = key(WEIGHT_SEED, wl.family, layer, TENSOR_DOWN, e)
     return fill_host(k, wl.H, wl.I, SIGMA_W, col0=wl.shard * wl.I, ld_full=wl.I_full)
+
+
+def router_bias(wl, layer=0):
+    """fp32 [E] selection bias (bf16-representable values), or None."""
+    if not wl.bias_sigma:
+        return None
+    import numpy as np
+    k = key(WEIGHT_SEED, wl.family, layer, TENSOR_BIAS)
+    b = fill_host(k, 1, wl.E, wl.bias_sigma)[0]
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def norm_gain(wl, layer=0):
+    """bf16 bits [H] of 1 + N(0, gain_sigma^2), or None (unit gain)."""
+    if not wl.gain_sigma:
+        return None
+    import numpy as np
+    k = key(WEIGHT_SEED, wl.family, layer, TENSOR_GAIN)
+    v = (fill_host(k, 1, wl.H, wl.gain_sigma)[0].astype(np.uint32) << 16).view(np.float32)
+    return round_bf16_bits(v + np.float32(1.0))
 
 
 def lmhead(wl):

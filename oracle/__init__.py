@@ -30,16 +30,16 @@ def lib():
         L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
         L.oracle_set_threads.argtypes = [_I]
         L.oracle_router_logits.argtypes = [_I, _I, _I, _P, _P, _P]
-        L.oracle_select_gates.argtypes = [_I, _I, _I, _P, _P, _P]
+        L.oracle_select_gates.argtypes = [_I, _I, _I, _P, _P, _P, _P]
         L.oracle_swiglu.restype = ctypes.c_uint16
         L.oracle_swiglu.argtypes = [ctypes.c_float, ctypes.c_float]
         L.oracle_expert.argtypes = [_I, _I, _P, _P, _P, _P, _P]
         L.oracle_experts_combine.restype = _I
-        L.oracle_experts_combine.argtypes = [_I] * 6 + [_P] * 6
+        L.oracle_experts_combine.argtypes = [_I] * 6 + [_P] * 5 + [ctypes.c_float, _P]
         L.oracle_cast_bf16.argtypes = [_I64, _P, _P]
         L.oracle_residual.argtypes = [_I64, _P, _P, _P]
         L.oracle_lmhead_argmax.argtypes = [_I, _I, _I, _P, _P, _P, _P]
-        L.oracle_rmsnorm.argtypes = [_I, _I, _P, ctypes.c_float, _P]
+        L.oracle_rmsnorm.argtypes = [_I, _I, _P, ctypes.c_float, _P, _P]
         L.oracle_unique_weight_bytes.restype = _I64
         L.oracle_unique_weight_bytes.argtypes = [_I] * 6 + [_P, _I, _P]
         _lib = L
@@ -88,18 +88,24 @@ def router_logits(x, w_router):
     return out
 
 
-def select_gates(logits, K):
+def select_gates(logits, K, bias=None):
+    """bias: optional fp32 [E] selection bias (chooses experts; gates stay unbiased)."""
     logits = _c(logits, np.float32)
     M, E = logits.shape
+    if bias is not None:
+        bias = _c(bias, np.float32)
+        assert bias.shape == (E,)
     idx = np.empty((M, K), dtype=np.int32)
     gate = np.empty((M, K), dtype=np.float32)
-    lib().oracle_select_gates(E, K, M, logits.ctypes.data, idx.ctypes.data, gate.ctypes.data)
+    lib().oracle_select_gates(E, K, M, logits.ctypes.data,
+                              None if bias is None else bias.ctypes.data, idx.ctypes.data,
+                              gate.ctypes.data)
     return idx, gate
 
 
-def router_topk(x, w_router, K):
+def router_topk(x, w_router, K, bias=None):
     logits = router_logits(x, w_router)
-    idx, gate = select_gates(logits, K)
+    idx, gate = select_gates(logits, K, bias)
     return idx, gate, logits
 
 
@@ -118,8 +124,9 @@ def expert(x_row, w_gu, w_d):
     return y, h
 
 
-def experts_combine(x, idx, gate, w_gu_tab, w_d_tab, E, S):
-    """acc fp32 [M, H].  w_gu_tab / w_d_tab: dict expert id -> array (shared at E)."""
+def experts_combine(x, idx, gate, w_gu_tab, w_d_tab, E, S, scale=1.0):
+    """acc fp32 [M, H] = y_shared + scale * sum_k gate_k y_k.
+    w_gu_tab / w_d_tab: dict expert id -> array (shared at E)."""
     x = _c(x, np.uint16)
     idx = _c(idx, np.int32)
     gate = _c(gate, np.float32)
@@ -141,7 +148,7 @@ def experts_combine(x, idx, gate, w_gu_tab, w_d_tab, E, S):
     acc = np.empty((M, H), dtype=np.float32)
     rc = lib().oracle_experts_combine(H, E, K, I, int(S), M, x.ctypes.data, idx.ctypes.data,
                                       gate.ctypes.data, ctypes.cast(gu_ptrs, _P),
-                                      ctypes.cast(d_ptrs, _P), acc.ctypes.data)
+                                      ctypes.cast(d_ptrs, _P), float(scale), acc.ctypes.data)
     if rc != 0:
         raise ValueError("oracle_experts_combine: bad index or missing expert weights")
     return acc
@@ -159,11 +166,16 @@ def residual(h, acc):
 RMS_EPS = 1e-6
 
 
-def rmsnorm(h, eps=RMS_EPS):
+def rmsnorm(h, eps=RMS_EPS, gain=None):
+    """u = bf16((h * r) * gain) per row; gain: optional bf16 bits [H] (None: unit gain)."""
     h = _c(h, np.uint16)
     M, H = h.shape
+    if gain is not None:
+        gain = _c(gain, np.uint16)
+        assert gain.shape == (H,)
     u = np.empty_like(h)
-    lib().oracle_rmsnorm(M, H, h.ctypes.data, eps, u.ctypes.data)
+    lib().oracle_rmsnorm(M, H, h.ctypes.data, eps, None if gain is None else gain.ctypes.data,
+                         u.ctypes.data)
     return u
 
 

@@ -27,8 +27,11 @@
  *  gates are a full softmax over all experts' logits renormalised over the
  *  selected K; ties in selection and argmax go to the lower index; the shared
  *  expert is added with weight 1; a residual chain rounds h + acc once; the
- *  chain workload feeds each layer bf16(RMSNorm(h)) with unit gain (without
- *  it the residual stream of random layers diverges within a dozen layers).
+ *  chain workload feeds each layer bf16(RMSNorm(h)) (without it the residual
+ *  stream of random layers diverges within a dozen layers); a selection bias
+ *  is added to the logits in fp32 for choosing experts only; the routed
+ *  scaling factor multiplies the fp32 routed sum before the shared expert is
+ *  added; the norm's gain multiplies h * r in fp32 before the one rounding.
  *
  * Parity pins: every exported function is pinned by the CPU tests
  * (exact rational arithmetic on dyadic inputs, float64 bounds, brute-force
@@ -81,22 +84,29 @@ void oracle_router_logits(int H, int E, int M, const uint16_t* x, const uint16_t
 }
 
 /* ---- softmax top-k with renormalised gates ------------------------------
- * Selection: the K experts with the largest logits, in descending order,
- * equal logits ordered by lower expert index.
+ * Selection: the K experts with the largest selection scores
+ * s_e = fp32(l_e + b_e), in descending order, equal scores ordered by lower
+ * expert index; b is an optional per-expert selection bias (NULL: s_e = l_e).
+ * The bias only chooses experts: the gates use the unbiased logits.
+ * (Reading of "PDL: stacking ...", figure on the router path, where the top-k
+ * kernel loads a bias of its own before its producer's output is ready.)
  * Gates: p_e = exp(l_e - max_l) (exp in double, rounded once to fp32),
  * Z = sum_e p_e (index order), q_e = p_e / Z, G = sum_k q_{S[k]} (rank order),
  * g_k = q_{S[k]} / G. */
-void oracle_select_gates(int E, int K, int M, const float* logits, int32_t* idx, float* gate) {
+void oracle_select_gates(int E, int K, int M, const float* logits, const float* bias,
+                         int32_t* idx, float* gate) {
   float* p = (float*)malloc(sizeof(float) * (size_t)E);
+  float* sc = (float*)malloc(sizeof(float) * (size_t)E);
   unsigned char* taken = (unsigned char*)malloc((size_t)E);
   for (int m = 0; m < M; ++m) {
     const float* l = logits + (size_t)m * E;
+    for (int e = 0; e < E; ++e) sc[e] = bias ? l[e] + bias[e] : l[e];
     memset(taken, 0, (size_t)E);
     for (int k = 0; k < K; ++k) {
       int best = -1;
       for (int e = 0; e < E; ++e) {
         if (taken[e]) continue;
-        if (best < 0 || l[e] > l[best]) best = e; /* strict: first (lowest) index wins ties */
+        if (best < 0 || sc[e] > sc[best]) best = e; /* strict: first (lowest) index wins ties */
       }
       taken[best] = 1;
       idx[(size_t)m * K + k] = best;
@@ -114,6 +124,7 @@ void oracle_select_gates(int E, int K, int M, const float* logits, int32_t* idx,
     for (int k = 0; k < K; ++k) gate[(size_t)m * K + k] = (p[idx[(size_t)m * K + k]] / Z) / G;
   }
   free(p);
+  free(sc);
   free(taken);
 }
 
@@ -155,28 +166,27 @@ void oracle_expert(int H, int I, const uint16_t* x_row, const uint16_t* w_gu, co
 }
 
 /* ---- experts + gate-weighted combine + shared expert -----------------------
- * acc[m][n] = y_shared[m][n] (0 if no shared expert), then for k = 0..K-1 in
- * rank order: acc = acc + g[m][k] * y_{idx[m][k]}[m][n]   (fp32, one rounding
- * per operation, no contraction).  The caller casts acc once.
+ * Per row m and output n (fp32, one rounding per operation, no contraction):
+ *   R = 0, then for k = 0..K-1 in rank order: R = R + g[m][k] * y_{idx[m][k]}[m][n]
+ *   acc[m][n] = y_shared[m][n] + scale * R          (y_shared = 0 without one)
+ * The routed part is summed in fp32 and scaled once ("PDL: stacking ...": the
+ * small-M combine is an fp32 sum times a scale with a single final cast; the
+ * scale is the routed scaling factor, 1 unless the model sets one).  The
+ * caller casts acc once.
  * w_gu_tab / w_d_tab are tables of per-expert weight pointers indexed by expert
  * id (shared expert at index E); only the experts used need to be present.
  * Returns 0, or -1 if an index is out of range or a needed weight is missing. */
 int oracle_experts_combine(int H, int E, int K, int I, int S, int M, const uint16_t* x,
                            const int32_t* idx, const float* gate,
                            const uint16_t* const* w_gu_tab, const uint16_t* const* w_d_tab,
-                           float* acc) {
+                           float scale, float* acc) {
   float* y = (float*)malloc(sizeof(float) * (size_t)H);
+  float* R = (float*)malloc(sizeof(float) * (size_t)H);
   int rc = 0;
   for (int m = 0; m < M && rc == 0; ++m) {
     const uint16_t* xr = x + (size_t)m * H;
     float* a = acc + (size_t)m * H;
-    if (S) {
-      if (!w_gu_tab[E] || !w_d_tab[E]) { rc = -1; break; }
-      oracle_expert(H, I, xr, w_gu_tab[E], w_d_tab[E], NULL, y);
-      for (int n = 0; n < H; ++n) a[n] = y[n];
-    } else {
-      for (int n = 0; n < H; ++n) a[n] = 0.0f;
-    }
+    for (int n = 0; n < H; ++n) R[n] = 0.0f;
     for (int k = 0; k < K; ++k) {
       int e = idx[(size_t)m * K + k];
       if (e < 0 || e >= E || !w_gu_tab[e] || !w_d_tab[e]) { rc = -1; break; }
@@ -184,10 +194,22 @@ int oracle_experts_combine(int H, int E, int K, int I, int S, int M, const uint1
       float g = gate[(size_t)m * K + k];
       for (int n = 0; n < H; ++n) {
         float t = g * y[n];
-        a[n] = a[n] + t;
+        R[n] = R[n] + t;
       }
     }
+    if (rc) break;
+    if (S) {
+      if (!w_gu_tab[E] || !w_d_tab[E]) { rc = -1; break; }
+      oracle_expert(H, I, xr, w_gu_tab[E], w_d_tab[E], NULL, y);
+    } else {
+      for (int n = 0; n < H; ++n) y[n] = 0.0f;
+    }
+    for (int n = 0; n < H; ++n) {
+      float t = scale * R[n];
+      a[n] = y[n] + t;
+    }
   }
+  free(R);
   free(y);
   return rc;
 }
@@ -205,15 +227,17 @@ void oracle_residual(int64_t n, const uint16_t* h, const float* acc, uint16_t* o
   }
 }
 
-/* Pre-norm of the residual chain (reading: the router chain of "PDL: stacking
- * ..." starts with a norm, and the chain workload feeds every layer a unit-scale
- * input): RMSNorm with unit gain,
+/* RMSNorm in front of the router and the experts (the router chain of
+ * "PDL: stacking ..." opens with a norm; the chain workload also relies on it
+ * to keep every layer's input at unit scale):
  *   ss = sum_n h_n^2 accumulated in double (each square of a bf16 value is exact,
  *        and for the chain's value range so is every partial sum, so ss is the
  *        exact sum whatever the order),
  *   r = 1 / sqrt(ss / H + eps) in double, rounded once to fp32,
- *   u_n = bf16(h_n * r) with the product in fp32. */
-void oracle_rmsnorm(int M, int H, const uint16_t* h, float eps, uint16_t* u) {
+ *   u_n = bf16((h_n * r) * w_n), both products in fp32 and one rounding to bf16,
+ * with w the norm's bf16 gain vector [H] (NULL: unit gain, u_n = bf16(h_n * r)). */
+void oracle_rmsnorm(int M, int H, const uint16_t* h, float eps, const uint16_t* gain,
+                    uint16_t* u) {
   for (int m = 0; m < M; ++m) {
     const uint16_t* hr = h + (size_t)m * H;
     double ss = 0.0;
@@ -222,7 +246,11 @@ void oracle_rmsnorm(int M, int H, const uint16_t* h, float eps, uint16_t* u) {
       ss = ss + v * v;
     }
     float r = (float)(1.0 / sqrt(ss / (double)H + (double)eps));
-    for (int n = 0; n < H; ++n) u[(size_t)m * H + n] = oracle_f32_to_bf16(bf2f(hr[n]) * r);
+    for (int n = 0; n < H; ++n) {
+      float t = bf2f(hr[n]) * r;
+      if (gain) t = t * bf2f(gain[n]);
+      u[(size_t)m * H + n] = oracle_f32_to_bf16(t);
+    }
   }
 }
 

@@ -33,10 +33,11 @@ class ExpertCache:
 
 
 def layer(wl, x, layer_idx=0, cache=None, w_router=None):
-    """One MoE layer: returns dict(idx, gate, logits, acc fp32 [M, H])."""
+    """One MoE layer on its (already normed) input x: returns dict(idx, gate, logits,
+    acc fp32 [M, H]), with the workload's selection bias and routed scaling factor."""
     if w_router is None:
         w_router = W.router(wl, layer_idx)
-    idx, gate, logits = router_topk(x, w_router, wl.K)
+    idx, gate, logits = router_topk(x, w_router, wl.K, W.router_bias(wl, layer_idx))
     cache = cache or ExpertCache(wl)
     used = sorted(set(int(e) for e in idx.ravel()))
     if wl.S:
@@ -44,8 +45,17 @@ def layer(wl, x, layer_idx=0, cache=None, w_router=None):
     gu, d = {}, {}
     for e in used:
         gu[e], d[e] = cache.get(layer_idx, e)
-    acc = experts_combine(x, idx, gate, gu, d, wl.E, wl.S)
+    acc = experts_combine(x, idx, gate, gu, d, wl.E, wl.S, wl.routed_scale)
     return dict(idx=idx, gate=gate, logits=logits, acc=acc)
+
+
+def front_layer(wl, x, layer_idx=0, cache=None):
+    """One layer with the router front: u = bf16(RMSNorm(x) * gain) feeds the router and the
+    experts when wl.prenorm; returns layer()'s dict plus u_in."""
+    u = rmsnorm(x, gain=W.norm_gain(wl, layer_idx)) if wl.prenorm else x
+    r = layer(wl, u, layer_idx, cache)
+    r["u_in"] = u
+    return r
 
 
 def layer_output(wl, res):
@@ -54,15 +64,15 @@ def layer_output(wl, res):
 
 
 def chain(wl, x, n_layers=None, keep_cache=False, prenorm=None, routers=None):
-    """Residual chain h_{l+1} = bf16(h_l + MoE_l(u_l)) with u_l = bf16(RMSNorm(h_l)) when
-    prenorm (the chain workload), else u_l = h_l; returns (h_L, per-layer results)."""
+    """Residual chain h_{l+1} = bf16(h_l + MoE_l(u_l)) with u_l = bf16(RMSNorm(h_l) * gain_l)
+    when prenorm (the chain workload), else u_l = h_l; returns (h_L, per-layer results)."""
     n_layers = wl.n_layers if n_layers is None else n_layers
     prenorm = wl.prenorm if prenorm is None else prenorm
     h = np.ascontiguousarray(x, dtype=np.uint16)
     per = []
     cache = ExpertCache(wl)
     for l in range(n_layers):
-        u = rmsnorm(h) if prenorm else h
+        u = rmsnorm(h, gain=W.norm_gain(wl, l)) if prenorm else h
         r = layer(wl, u, l, cache, w_router=None if routers is None else routers[l])
         r["h_in"] = h
         r["u_in"] = u
@@ -73,9 +83,11 @@ def chain(wl, x, n_layers=None, keep_cache=False, prenorm=None, routers=None):
     return h, per
 
 
-def router_margin(logits, K):
-    """Per row: K-th largest logit minus (K+1)-th largest (how far from a tie the selection is)."""
-    s = -np.sort(-logits.astype(np.float64), axis=1)
+def router_margin(logits, K, bias=None):
+    """Per row: K-th largest selection score minus the (K+1)-th largest (how far from a tie
+    the selection is); the score is the logit plus the selection bias, if any."""
+    sc = logits.astype(np.float32) + (np.float32(0) if bias is None else bias.astype(np.float32))
+    s = -np.sort(-sc.astype(np.float64), axis=1)
     if s.shape[1] <= K:
         return np.full(s.shape[0], np.inf)
     return s[:, K - 1] - s[:, K]

@@ -140,6 +140,108 @@ def test_gates_sum_to_one_and_closed_forms(rng):
     assert np.all(np.abs(gs - g) <= 1e-6)
 
 
+
+# ---------------------------------------------------------------- router front: selection bias
+
+def test_selection_bias_matches_bruteforce(rng):
+    """Selection on fp32(logit + bias), lower index first on equal scores; gates are the
+    unbiased softmax renormalised over the chosen set (float64 closed form)."""
+    E, K = 9, 3
+    for trial in range(200):
+        lg = (rng.integers(-6, 7, size=(2, E)) / 4.0).astype(np.float32)
+        b = (rng.integers(-3, 4, size=E) / 4.0).astype(np.float32)   # exact sums, many ties
+        idx, g = oracle.select_gates(lg, K, b)
+        for m in range(2):
+            sc = lg[m] + b
+            order = sorted(range(E), key=lambda e: (-float(sc[e]), e))
+            assert list(idx[m]) == order[:K]
+            ex = np.exp(lg[m, idx[m]].astype(np.float64))
+            assert np.all(np.abs(g[m] - ex / ex.sum()) <= 1e-6 * ex / ex.sum())
+
+
+def test_selection_bias_special_cases(rng):
+    M, E, K = 4, 512, 8
+    lg = rng.standard_normal((M, E)).astype(np.float32)
+    idx0, g0 = oracle.select_gates(lg, K)
+    # zero bias is no bias, bit for bit
+    idxz, gz = oracle.select_gates(lg, K, np.zeros(E, np.float32))
+    assert np.array_equal(idxz, idx0) and np.array_equal(gz, g0)
+    # a bias that dwarfs the logits selects by bias alone, and the gates are still the
+    # unbiased softmax over that set (so they differ from a softmax of the biased scores)
+    b = np.zeros(E, np.float32)
+    forced = rng.choice(E, K, replace=False)
+    b[forced] = 1000.0 + 100.0 * np.arange(K, dtype=np.float32)
+    idx, g = oracle.select_gates(lg, K, b)
+    assert np.all(idx == forced[np.argsort(-b[forced], kind="stable")][None, :])
+    ex = np.exp(lg[:, forced[np.argsort(-b[forced], kind="stable")]].astype(np.float64))
+    ref = ex / ex.sum(1, keepdims=True)
+    assert np.all(np.abs(g - ref) <= 1e-6 * ref)
+    # the gates of a set depend only on the set: same set, same gate per expert
+    for m in range(M):
+        if set(idx0[m]) == set(idx[m]):
+            assert np.allclose(g0[m][np.argsort(idx0[m])], g[m][np.argsort(idx[m])], rtol=1e-6)
+
+
+# ---------------------------------------------------------------- router front: routed scale
+
+def test_routed_scale_combine_bound_and_power_of_two_exactness(rng):
+    """acc = y_shared + s * sum_k g_k y_k: the shared expert is not scaled."""
+    wl = W.C1
+    x = W.x_rows(wl, [0, 1, 2])
+    wr = W.router(wl)
+    gu = {e: W.expert_gate_up(wl, 0, e) for e in range(wl.E + 1)}
+    d = {e: W.expert_down(wl, 0, e) for e in range(wl.E + 1)}
+    idx, gate, _ = oracle.router_topk(x, wr, wl.K)
+    s = 2.5
+    acc = oracle.experts_combine(x, idx, gate, gu, d, wl.E, 1, s).astype(np.float64)
+    for m in range(3):
+        ysh = oracle.expert(x[m], gu[wl.E], d[wl.E])[0].astype(np.float64)
+        ys = [oracle.expert(x[m], gu[idx[m, k]], d[idx[m, k]])[0].astype(np.float64)
+              for k in range(wl.K)]
+        R = sum(float(gate[m, k]) * ys[k] for k in range(wl.K))
+        T = np.abs(ysh) + s * sum(float(gate[m, k]) * np.abs(ys[k]) for k in range(wl.K))
+        assert np.all(np.abs(acc[m] - (ysh + s * R)) <= gamma(wl.K + 3) * T)
+        # scaling the shared expert too would be far outside the bound
+        assert np.max(np.abs(acc[m] - s * (ysh + R)) - gamma(wl.K + 3) * T) > 0
+    # without a shared expert a power-of-two scale commutes with every rounding
+    a1 = oracle.experts_combine(x, idx, gate, gu, d, wl.E, 0, 1.0)
+    a2 = oracle.experts_combine(x, idx, gate, gu, d, wl.E, 0, 2.0)
+    a8 = oracle.experts_combine(x, idx, gate, gu, d, wl.E, 0, -0.125)
+    assert np.array_equal(a2, 2 * a1) and np.array_equal(a8, -0.125 * a1)
+    # scale zero leaves the shared expert alone
+    a0 = oracle.experts_combine(x, idx, gate, gu, d, wl.E, 1, 0.0)
+    for m in range(3):
+        assert np.array_equal(a0[m], oracle.expert(x[m], gu[wl.E], d[wl.E])[0])
+
+
+# ---------------------------------------------------------------- router front: norm gain
+
+def test_rmsnorm_gain_product_order_and_special_gains():
+    from decimal import Decimal, getcontext
+    getcontext().prec = 50
+    rng = np.random.default_rng(12)
+    H = 2560
+    h = bf16_bits_torch(rng.standard_normal((3, H)) * 1.3)
+    g = bf16_bits_torch(1.0 + 0.1 * rng.standard_normal(H))
+    u = oracle.rmsnorm(h, gain=g)
+    hf = f32(h).astype(np.float64)
+    for m in range(3):
+        ss = sum(Fraction(float(v)) ** 2 for v in hf[m])
+        ms = Decimal(ss.numerator) / Decimal(ss.denominator) / H + Decimal(oracle.RMS_EPS)
+        r = np.float32(float(1 / ms.sqrt()))
+        t = (f32(h[m]) * r).astype(np.float32) * f32(g)          # two fp32 products
+        assert np.array_equal(u[m], bf16_bits_torch(t.astype(np.float64)))
+    ones = to_bf16_bits_exact(np.ones(H))
+    assert np.array_equal(oracle.rmsnorm(h, gain=ones), oracle.rmsnorm(h))
+    twos = to_bf16_bits_exact(np.full(H, 2.0))
+    assert np.array_equal(f32(oracle.rmsnorm(h, gain=twos)), 2 * f32(oracle.rmsnorm(h)))
+    # the gain scales each channel, not each row
+    gv = f32(g).astype(np.float64)
+    ratio = f32(u).astype(np.float64) / f32(oracle.rmsnorm(h)).astype(np.float64)
+    ok = np.abs(f32(oracle.rmsnorm(h))) > 0.05
+    assert np.all(np.abs(ratio - gv[None, :])[ok] <= 2 ** -6 * gv[None, :].repeat(3, 0)[ok])
+
+
 # ---------------------------------------------------------------- SwiGLU
 
 def test_swiglu_exhaustive_over_bf16(rng):
