@@ -93,9 +93,10 @@ def main():
         rows = [W.x_rows(wl, [s * M + m for m in range(M)]) for s in range(n_steps)]
         return torch.stack([D.to_device(r) for r in rows])
 
-    def time_layer(wl, lws, M, steps, warmup, out_f32=False):
+    def time_layer(wl, lws, M, steps, warmup, out_f32=False, mode=None):
         """Cold rotating per-layer timing; returns dict of figures."""
-        d = md.dims(wl.H, wl.E, wl.K, wl.I, wl.S)
+        mode = md.MOE_CHAIN_LAYER_ONLY if mode is None else mode
+        d = md.dims(wl.H, wl.E, wl.K, wl.I, wl.S, wl.routed_scale)
         ws = md.new_workspace(d, M, 1)
         n = steps + warmup
         xs = x_pool(wl, n, M)
@@ -104,8 +105,8 @@ def main():
         dt = md.MOE_OUT_F32 if out_f32 else md.MOE_OUT_BF16
 
         def call(i):
-            return md.moe_layer_chain(d, M, [lws[i % len(lws)]], xs[i], out, dt,
-                                      md.MOE_CHAIN_LAYER_ONLY, idx[i], ws)
+            return md.moe_layer_chain(d, M, [lws[i % len(lws)]], xs[i], out, dt, mode, idx[i],
+                                      ws)
 
         for i in range(warmup):
             md.check(call(i))
@@ -134,7 +135,7 @@ def main():
         per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(ne)]) * 1e3
         ids = idx.cpu().numpy()[warmup:]
         U = np.array([len(np.unique(ids[i])) for i in range(steps)])
-        bytes_per = wl.router_bytes() + (U + wl.S) * wl.expert_bytes()
+        bytes_per = wl.router_bytes() + (U + wl.S) * wl.expert_bytes() + wl.front_bytes()
         gbs = bytes_per.mean() / (us_per * 1e-6) / 1e9
         return {
             "us_per_layer": float(us_per),
@@ -170,6 +171,18 @@ def main():
               % (s4["us_per_layer"], s4["effective_gbs"], s4["pct_of_hbm_peak"]),
               file=sys.stderr, flush=True)
         del shards, lws
+        # the router front (RMSNorm with gain, selection bias, routed scale) fused in
+        fronts = [(D.to_device(W.router_bias(W.C7, l)), D.to_device(W.norm_gain(W.C7, l)))
+                  for l in range(N_LAYERS)]
+        lwf = [md.layer_weights(L.w_router, L.w_gate_up, L.w_down, b, g)
+               for L, (b, g) in zip(layers, fronts)]
+        s7 = time_layer(W.C7, lwf, 6, args.steps, args.warmup,
+                        mode=md.MOE_CHAIN_PRENORM_LAYER_ONLY)
+        secondary[W.C7.name] = s7
+        print("front M=6: %.2f us/layer, %.0f GB/s (%.1f %%)"
+              % (s7["us_per_layer"], s7["effective_gbs"], s7["pct_of_hbm_peak"]),
+              file=sys.stderr, flush=True)
+        del fronts, lwf
         secondary[W.C5.name] = time_chain(md, D, W, np, torch, dev, lw, steps=10, warmup=2)
         c = secondary[W.C5.name]
         print("chain16+lm_head M=6: %.1f us (floor %.1f us, ratio %.2f)"

@@ -46,24 +46,40 @@ extern "C" {
 
 /* Layer shape: H hidden size, E routed experts, K experts per row, I expert
  * intermediate size (of this call: a tensor-parallel shard passes its share),
- * S shared experts (0 or 1).  [LING] "The model": H=2560, E=512, K=8, I=768, S=1. */
+ * S shared experts (0 or 1).  [LING] "The model": H=2560, E=512, K=8, I=768, S=1.
+ * routed_scale: the routed scaling factor s of the combine,
+ *   acc = y_shared + s * sum_k g_k y_k  (the routed part summed in fp32, scaled once:
+ *   [LING] "PDL: stacking ...", small-M combine as an fp32 sum times a scale);
+ *   must be finite; 0 (a zero-initialised struct) means 1. */
 typedef struct {
   int32_t hidden;
   int32_t n_experts;
   int32_t top_k;
   int32_t inter;
   int32_t n_shared;
+  float routed_scale;
 } moe_dims;
 
-/* One layer's weights (device pointers, bf16 bits):
- *   w_router  [E][H]
- *   w_gate_up [E+S][2I][H]  rows [0, I) are the gate projection, rows [I, 2I) the up projection
- *   w_down    [E+S][H][I]
+/* One layer's weights (device pointers, bf16 bits unless stated):
+ *   w_router    [E][H]
+ *   w_gate_up   [E+S][2I][H]  rows [0, I) are the gate projection, rows [I, 2I) the up projection
+ *   w_down      [E+S][H][I]
+ *   router_bias [E] fp32, optional (NULL: none): a per-expert selection bias.  Experts
+ *               are chosen by fp32(logit + bias); the gates still come from the
+ *               unbiased logits.  [LING] "PDL: stacking ...", figure on the router
+ *               path: the top-k kernel loads its bias before the logits are ready.
+ *               4-byte aligned.  Ignored by moe_experts_fused (routing is given).
+ *   norm_gain   [H] bf16, optional (NULL: unit gain): the gain of the RMSNorm in
+ *               front of the router and the experts (the norm that opens the router
+ *               chain in [LING] "PDL: stacking ...").  16-byte aligned.  Used by the
+ *               PRENORM modes of moe_layer_chain only, ignored elsewhere.
  * The shared expert, if any, is stored at expert index E. */
 typedef struct {
   const uint16_t* w_router;
   const uint16_t* w_gate_up;
   const uint16_t* w_down;
+  const float* router_bias;
+  const uint16_t* norm_gain;
 } moe_layer_weights;
 
 enum moe_status {
@@ -78,7 +94,12 @@ enum moe_status {
 };
 
 enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1 };
-enum { MOE_CHAIN_RESIDUAL = 0, MOE_CHAIN_LAYER_ONLY = 1, MOE_CHAIN_PRENORM_RESIDUAL = 2 };
+enum {
+  MOE_CHAIN_RESIDUAL = 0,
+  MOE_CHAIN_LAYER_ONLY = 1,
+  MOE_CHAIN_PRENORM_RESIDUAL = 2,
+  MOE_CHAIN_PRENORM_LAYER_ONLY = 3
+};
 
 #define MOE_MAX_ROWS 8      /* [LLM] item 3: at most eight rows per tile */
 #define MOE_MAX_LAYERS 64
@@ -95,21 +116,25 @@ int moe_workspace_size(const moe_dims* dims, int32_t max_rows, int32_t n_layers,
 int moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Router: logits[m][e] = sum_h x[m][h] * w_router[e][h] (fp32 accumulation of
- * bf16 products), then per row the K largest logits in descending order (equal
- * logits: lower expert index first) and gates g_k = p_k / sum_k' p_k' with
- * p = softmax(logits[m]) -- the renormalised top-k softmax.
+ * bf16 products), then per row the K largest selection scores
+ * s[m][e] = fp32(logits[m][e] + router_bias[e]) (s = logits without a bias) in
+ * descending order (equal scores: lower expert index first) and gates
+ * g_k = p_k / sum_k' p_k' with p = softmax(logits[m]) -- the renormalised top-k
+ * softmax of the unbiased logits.
  * [LING] "PDL: stacking the latency floors of small kernels" (router chain:
- * gate matvec then top-k) and "bf16 router gate and lm_head".
- *   x [M][H] bf16; topk_idx [M][K] int32 (out); topk_gate [M][K] fp32 (out);
- *   logits [M][E] fp32 (out, optional: NULL to skip). */
+ * gate matvec then top-k; the top-k's bias) and "bf16 router gate and lm_head".
+ *   x [M][H] bf16; router_bias [E] fp32 (optional, NULL: none; 4-byte aligned);
+ *   topk_idx [M][K] int32 (out); topk_gate [M][K] fp32 (out);
+ *   logits [M][E] fp32 (out, optional: NULL to skip; unbiased). */
 int moe_router_topk(const moe_dims* dims, int32_t M, const uint16_t* x, const uint16_t* w_router,
-                    int32_t* topk_idx, float* topk_gate, float* logits, void* ws, size_t ws_bytes,
-                    void* stream);
+                    const float* router_bias, int32_t* topk_idx, float* topk_gate, float* logits,
+                    void* ws, size_t ws_bytes, void* stream);
 
 /* Experts for given routing: for each row m and selected expert e = topk_idx[m][k]
  * (and the shared expert), a = W_gate[e] x_m, b = W_up[e] x_m (fp32),
  * h = bf16(silu(a) * b), y = W_down[e] h (fp32); then
  *   acc[m] = y_shared + sum_k topk_gate[m][k] * y_{topk_idx[m][k]}   (fp32)
+ * (times dims->routed_scale on the routed sum, see moe_dims)
  * and out[m] = bf16(acc[m]) (MOE_OUT_BF16) or acc[m] unrounded (MOE_OUT_F32, the
  * partial sum of a tensor-parallel shard).  Every selected expert is streamed
  * from HBM once per call, whatever the number of rows that chose it.
@@ -131,12 +156,17 @@ int moe_experts_fused(const moe_dims* dims, int32_t M, const uint16_t* x, const 
  *   MOE_CHAIN_LAYER_ONLY: n_layers must be 1; out = MoE(x_in) exactly as
  *                         moe_experts_fused would return it (bf16 or fp32).
  *   MOE_CHAIN_PRENORM_RESIDUAL: h_{l+1} = bf16(h_l + MoE_l(u_l)) with
- *                         u_l = bf16(h_l * r), r = fp32(1 / sqrt(mean(h_l^2) + 1e-6)),
- *                         the mean of squares summed in double (RMSNorm with unit gain, the norm that opens the
- *                         router chain in [LING] "PDL: stacking ..."); keeps
- *                         every layer's input at unit scale.  out = h_L.
+ *                         u_l = bf16((h_l * r) * norm_gain_l) (fp32 products; unit gain
+ *                         when layers[l].norm_gain is NULL),
+ *                         r = fp32(1 / sqrt(mean(h_l^2) + 1e-6)), the mean of squares
+ *                         summed in double (the RMSNorm that opens the router chain
+ *                         in [LING] "PDL: stacking ..."); keeps every layer's input
+ *                         at unit scale.  out = h_L.
+ *   MOE_CHAIN_PRENORM_LAYER_ONLY: n_layers must be 1; out = MoE(u) with u the
+ *                         normed input as above (router front, router and experts
+ *                         in one launch), bf16 or fp32.
  *   layers: host array [n_layers] of device weight pointers;
- *   x_in [M][H] bf16; out [M][H] (bf16, or fp32 in LAYER_ONLY); out may alias x_in;
+ *   x_in [M][H] bf16; out [M][H] (bf16, or fp32 in the LAYER_ONLY modes); out may alias x_in;
  *   topk_idx_all [n_layers][M][K] int32 (out, optional: NULL to skip);
  *   h_all [n_layers+1][M][H] bf16 (out, optional, residual modes only): h_all[0] = x_in,
  *         h_all[l+1] = the residual stream after layer l; must not overlap x_in. */

@@ -40,6 +40,7 @@ MOE_OUT_F32 = 1
 MOE_CHAIN_RESIDUAL = 0
 MOE_CHAIN_LAYER_ONLY = 1
 MOE_CHAIN_PRENORM_RESIDUAL = 2
+MOE_CHAIN_PRENORM_LAYER_ONLY = 3
 
 MOE_MAX_ROWS = 8
 MOE_MAX_LAYERS = 64
@@ -54,12 +55,13 @@ EXPORTED = ("moe_workspace_size", "moe_workspace_init", "moe_router_topk", "moe_
 class moe_dims(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32),
-                ("n_shared", ctypes.c_int32)]
+                ("n_shared", ctypes.c_int32), ("routed_scale", ctypes.c_float)]
 
 
 class moe_layer_weights(ctypes.Structure):
     _fields_ = [("w_router", ctypes.c_void_p), ("w_gate_up", ctypes.c_void_p),
-                ("w_down", ctypes.c_void_p)]
+                ("w_down", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
+                ("norm_gain", ctypes.c_void_p)]
 
 
 _P = ctypes.c_void_p
@@ -71,7 +73,8 @@ _lib.moe_workspace_size.argtypes = [ctypes.POINTER(moe_dims), _I32, _I32, ctypes
 _lib.moe_workspace_init.restype = ctypes.c_int
 _lib.moe_workspace_init.argtypes = [_P, _SZ, _P]
 _lib.moe_router_topk.restype = ctypes.c_int
-_lib.moe_router_topk.argtypes = [ctypes.POINTER(moe_dims), _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]
+_lib.moe_router_topk.argtypes = [ctypes.POINTER(moe_dims), _I32, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                 _P]
 _lib.moe_experts_fused.restype = ctypes.c_int
 _lib.moe_experts_fused.argtypes = [ctypes.POINTER(moe_dims), _I32, _P, _P, _P,
                                    ctypes.POINTER(moe_layer_weights), _P, _I32, _P, _SZ, _P]
@@ -126,12 +129,14 @@ def _nbytes(ws, ws_bytes):
     return ws.numel() * ws.element_size()
 
 
-def dims(hidden, n_experts, top_k, inter, n_shared):
-    return moe_dims(hidden, n_experts, top_k, inter, n_shared)
+def dims(hidden, n_experts, top_k, inter, n_shared, routed_scale=0.0):
+    """routed_scale 0 means 1 (the plain combine)."""
+    return moe_dims(hidden, n_experts, top_k, inter, n_shared, routed_scale)
 
 
-def layer_weights(w_router, w_gate_up, w_down):
-    return moe_layer_weights(_ptr(w_router), _ptr(w_gate_up), _ptr(w_down))
+def layer_weights(w_router, w_gate_up, w_down, router_bias=None, norm_gain=None):
+    return moe_layer_weights(_ptr(w_router), _ptr(w_gate_up), _ptr(w_down), _ptr(router_bias),
+                             _ptr(norm_gain))
 
 
 # ---- the C entry points, same names -------------------------------------------
@@ -152,11 +157,12 @@ def moe_workspace_init(ws, ws_bytes=None, stream=None):
     return _lib.moe_workspace_init(_ptr(ws), _nbytes(ws, ws_bytes), _stream(stream))
 
 
-def moe_router_topk(d, M, x, w_router, topk_idx, topk_gate, logits, ws, ws_bytes=None,
-                    stream=None):
+def moe_router_topk(d, M, x, w_router, router_bias, topk_idx, topk_gate, logits, ws,
+                    ws_bytes=None, stream=None):
     return _lib.moe_router_topk(ctypes.byref(d) if d is not None else None, M, _ptr(x),
-                                _ptr(w_router), _ptr(topk_idx), _ptr(topk_gate), _ptr(logits),
-                                _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream))
+                                _ptr(w_router), _ptr(router_bias), _ptr(topk_idx),
+                                _ptr(topk_gate), _ptr(logits), _ptr(ws), _nbytes(ws, ws_bytes),
+                                _stream(stream))
 
 
 def moe_experts_fused(d, M, x, topk_idx, topk_gate, w, out, out_dtype, ws, ws_bytes=None,

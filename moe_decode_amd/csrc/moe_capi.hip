@@ -7,6 +7,7 @@
 // Ling-3.0-flash on 4 Blackwell GPUs, Two fusions and a retune: the pair-axis
 // kernel's hard size gate with fallback).
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -20,6 +21,8 @@
 using namespace moe;
 
 static_assert(MOE_MAX_LAYERS == 64, "layer table size must match the header");
+// kernel arguments of the chain kernel (one weight slot per layer) stay within 4 KiB
+static_assert(sizeof(ParamsT<MOE_MAX_LAYERS>) <= 4096, "kernel argument block too large");
 
 namespace {
 
@@ -148,8 +151,11 @@ int check_dims(const moe_dims* d) {
   RowPlan a, b;
   if (!plan_h_rows(d->hidden, &a) || !plan_i_rows(d->inter, &b)) return MOE_E_UNSUPPORTED;
   if (d->hidden > 16384 || d->inter > 16384) return MOE_E_UNSUPPORTED;
+  if (!isfinite(d->routed_scale)) return MOE_E_ARG;
   return MOE_OK;
 }
+
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 // Workspace regions after the header (all tagged 64-bit words):
 //   lg  [L][M][E]        router logits
@@ -175,13 +181,13 @@ WsLayout ws_layout(const moe_dims& d, int M, int L) {
 }
 
 struct LdsPlan {
-  int xs, lg, hs, ysh, ysr, small, total, nr_max;
+  int xs, lg, hs, ysh, ysr, small, gn, total, nr_max;
 };
 
 // LDS of the layer kernel: x [M][H] bf16, logits [M][E] fp32, the SwiGLU rows
 // of the shared expert and of up to two routed slice pieces [3][M][I] bf16, the shared expert's outputs for the owned rows
 // [M][nr_max] fp32, the routed (expert, row) outputs of the owned rows
-// [M*K][nr_max] fp32, and the small tables.
+// [M*K][nr_max] fp32, the small tables and the norm's gain [H] bf16.
 int plan_lds(const moe_dims& d, int M, int G, int max_lds, LdsPlan* lp) {
   const int H = d.hidden, E = d.n_experts, I = d.inter;
   lp->nr_max = 2 * (((H / 2) + G - 1) / G);
@@ -199,6 +205,8 @@ int plan_lds(const moe_dims& d, int M, int G, int max_lds, LdsPlan* lp) {
   o = align_up(o + (size_t)M * d.top_k * lp->nr_max * 4, 16);
   lp->small = (int)o;
   o = align_up(o + sizeof(Small), 16);
+  lp->gn = (int)o;  // the norm's gain
+  o = align_up(o + (size_t)H * 2, 16);
   lp->total = (int)o;
   return o <= (size_t)max_lds ? MOE_OK : MOE_E_UNSUPPORTED;
 }
@@ -235,12 +243,14 @@ int launch_layer_nl(const moe_dims& d, int M, int L, uint32_t flags,
   p.L = L;
   p.flags = flags;
   p.nr_max = lp.nr_max;
+  p.scale = d.routed_scale == 0.0f ? 1.0f : d.routed_scale;
   p.lds_xs = lp.xs;
   p.lds_lg = lp.lg;
   p.lds_hs = lp.hs;
   p.lds_ysh = lp.ysh;
   p.lds_ysr = lp.ysr;
   p.lds_small = lp.small;
+  p.lds_gn = lp.gn;
   p.x_in = x;
   p.out = out;
   p.tk_idx_in = tk_in;
@@ -260,6 +270,8 @@ int launch_layer_nl(const moe_dims& d, int M, int L, uint32_t flags,
     p.lw[l].wr = layers[l].w_router;
     p.lw[l].wgu = layers[l].w_gate_up;
     p.lw[l].wd = layers[l].w_down;
+    p.lw[l].bias = layers[l].router_bias;
+    p.lw[l].gain = (flags & F_PRENORM) ? layers[l].norm_gain : nullptr;
   }
   hipLaunchKernelGGL(kern, dim3(G), dim3(MOE_WG), lp.total, st, p);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
@@ -326,17 +338,19 @@ int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
 }
 
 int moe_router_topk(const moe_dims* dims, int32_t M, const uint16_t* x, const uint16_t* w_router,
-                    int32_t* topk_idx, float* topk_gate, float* logits, void* ws, size_t ws_bytes,
-                    void* stream) {
+                    const float* router_bias, int32_t* topk_idx, float* topk_gate, float* logits,
+                    void* ws, size_t ws_bytes, void* stream) {
   int rc = check_dims(dims);
   if (rc) return rc;
   if (M < 1) return MOE_E_ARG;
   if (M > MOE_MAX_ROWS) return MOE_E_UNSUPPORTED;
   if (!x || !w_router || !topk_idx || !topk_gate) return MOE_E_ARG;
   if (!aligned16(x) || !aligned16(w_router)) return MOE_E_ALIGN;
+  if (!aligned4(router_bias) || !aligned4(topk_idx) || !aligned4(topk_gate) || !aligned4(logits))
+    return MOE_E_ALIGN;
   rc = check_ws(dims, M, 1, ws, ws_bytes);
   if (rc) return rc;
-  moe_layer_weights lw = {w_router, nullptr, nullptr};
+  moe_layer_weights lw = {w_router, nullptr, nullptr, router_bias, nullptr};
   return launch_layer(*dims, M, 1, F_ROUTER_ONLY, &lw, x, nullptr, nullptr, nullptr, topk_idx,
                       topk_gate, logits, nullptr, ws, (hipStream_t)stream);
 }
@@ -358,7 +372,7 @@ int moe_experts_fused(const moe_dims* dims, int32_t M, const uint16_t* x, const 
   const size_t osz = (size_t)M * dims->hidden * (out_dtype == MOE_OUT_F32 ? 4 : 2);
   uint32_t flags = F_TOPK_IN | (out_dtype == MOE_OUT_F32 ? F_OUT_F32 : 0u);
   if (overlaps(out, osz, x, (size_t)M * dims->hidden * 2)) flags |= F_ALIAS;
-  moe_layer_weights lw = {nullptr, w->w_gate_up, w->w_down};
+  moe_layer_weights lw = {nullptr, w->w_gate_up, w->w_down, nullptr, nullptr};
   return launch_layer(*dims, M, 1, flags, &lw, x, out, topk_idx, topk_gate, nullptr, nullptr,
                       nullptr, nullptr, ws, (hipStream_t)stream);
 }
@@ -373,20 +387,23 @@ int moe_layer_chain(const moe_dims* dims, int32_t M, int32_t n_layers,
   if (M > MOE_MAX_ROWS || n_layers > MOE_MAX_LAYERS) return MOE_E_UNSUPPORTED;
   if (!layers || !x_in || !out) return MOE_E_ARG;
   if (mode != MOE_CHAIN_RESIDUAL && mode != MOE_CHAIN_LAYER_ONLY &&
-      mode != MOE_CHAIN_PRENORM_RESIDUAL)
+      mode != MOE_CHAIN_PRENORM_RESIDUAL && mode != MOE_CHAIN_PRENORM_LAYER_ONLY)
     return MOE_E_ARG;
   if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return MOE_E_ARG;
-  if (mode == MOE_CHAIN_LAYER_ONLY && n_layers != 1) return MOE_E_UNSUPPORTED;
-  if (mode != MOE_CHAIN_LAYER_ONLY && out_dtype != MOE_OUT_BF16) return MOE_E_UNSUPPORTED;
+  const bool layer_only = mode == MOE_CHAIN_LAYER_ONLY || mode == MOE_CHAIN_PRENORM_LAYER_ONLY;
+  const bool prenorm = mode == MOE_CHAIN_PRENORM_RESIDUAL || mode == MOE_CHAIN_PRENORM_LAYER_ONLY;
+  if (layer_only && n_layers != 1) return MOE_E_UNSUPPORTED;
+  if (!layer_only && out_dtype != MOE_OUT_BF16) return MOE_E_UNSUPPORTED;
   for (int l = 0; l < n_layers; ++l) {
     const moe_layer_weights& w = layers[l];
     if (!w.w_router || !w.w_gate_up || !w.w_down) return MOE_E_ARG;
     if (!aligned16(w.w_router) || !aligned16(w.w_gate_up) || !aligned16(w.w_down))
       return MOE_E_ALIGN;
+    if (!aligned4(w.router_bias) || (prenorm && !aligned16(w.norm_gain))) return MOE_E_ALIGN;
   }
   if (!aligned16(x_in) || !aligned16(out)) return MOE_E_ALIGN;
   if (topk_idx_all && ((uintptr_t)topk_idx_all & 3u)) return MOE_E_ALIGN;
-  if (h_all && mode == MOE_CHAIN_LAYER_ONLY) return MOE_E_ARG;
+  if (h_all && layer_only) return MOE_E_ARG;
   if (h_all && !aligned16(h_all)) return MOE_E_ALIGN;
   if (h_all && (overlaps(h_all, (size_t)(n_layers + 1) * M * dims->hidden * 2, x_in,
                          (size_t)M * dims->hidden * 2)))
@@ -396,6 +413,7 @@ int moe_layer_chain(const moe_dims* dims, int32_t M, int32_t n_layers,
   uint32_t flags = 0;
   if (mode == MOE_CHAIN_RESIDUAL) flags |= F_RESIDUAL;
   if (mode == MOE_CHAIN_PRENORM_RESIDUAL) flags |= F_RESIDUAL | F_PRENORM;
+  if (mode == MOE_CHAIN_PRENORM_LAYER_ONLY) flags |= F_PRENORM;
   if (out_dtype == MOE_OUT_F32) flags |= F_OUT_F32;
   const size_t osz = (size_t)M * dims->hidden * (out_dtype == MOE_OUT_F32 ? 4 : 2);
   if (overlaps(out, osz, x_in, (size_t)M * dims->hidden * 2)) flags |= F_ALIAS;

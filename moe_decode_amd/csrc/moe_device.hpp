@@ -97,6 +97,30 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
   return ((uint64_t)hi << 32) | (uint64_t)lo;
 }
 
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = dpp_u<CTRL>((uint32_t)u), hi = dpp_u<CTRL>((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | (uint64_t)lo);
+}
+__device__ __forceinline__ double swz16_d(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = swz16_u((uint32_t)u), hi = swz16_u((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | (uint64_t)lo);
+}
+// Sum of a double over the 64 lanes (the same butterfly as group_sum); the
+// result is wave-uniform.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_d<0xB1>(v);
+  v += dpp_d<0x4E>(v);
+  v += dpp_d<0x141>(v);
+  v += dpp_d<0x140>(v);
+  v += swz16_d(v);
+  const uint64_t u = readlane_u64(__builtin_bit_cast(uint64_t, v), 0);
+  const uint64_t w = readlane_u64(__builtin_bit_cast(uint64_t, v), 32);
+  return __builtin_bit_cast(double, u) + __builtin_bit_cast(double, w);
+}
+
 // Sum over each group of `lpr` consecutive lanes (lpr = 8, 16, 32 or 64);
 // every lane of a group receives the group's sum.  lpr is wave-uniform.
 __device__ __forceinline__ float group_sum(float v, int lpr) {

@@ -47,9 +47,11 @@ namespace moe {
 constexpr int kMaxPK = MOE_MAXM * 16;  // max (routed expert, row) pairs = M * K
 
 struct LayerW {
-  const uint16_t* wr;   // [E][H]
-  const uint16_t* wgu;  // [E+S][2I][H]
-  const uint16_t* wd;   // [E+S][H][I]
+  const uint16_t* wr;    // [E][H]
+  const uint16_t* wgu;   // [E+S][2I][H]
+  const uint16_t* wd;    // [E+S][H][I]
+  const float* bias;     // [E] selection bias, or null
+  const uint16_t* gain;  // [H] RMSNorm gain (bf16), or null for unit gain
 };
 
 enum : uint32_t {
@@ -58,7 +60,7 @@ enum : uint32_t {
   F_TOPK_IN = 4u,      // routing comes from the caller (experts only)
   F_ROUTER_ONLY = 8u,  // router + top-k only
   F_ALIAS = 16u,       // out overlaps x_in: wait until every workgroup has read x_in
-  F_PRENORM = 32u,     // chain: each layer's MoE input is bf16(RMSNorm(h_l)), unit gain
+  F_PRENORM = 32u,     // each layer's MoE input is bf16(RMSNorm(h_l) * gain_l)
 };
 
 constexpr float kRmsEps = 1e-6f;
@@ -70,8 +72,10 @@ struct ParamsT {
   int H, E, K, I, S, M, L;
   uint32_t flags;
   int nr_max;         // output rows owned by one workgroup, at most
+  float scale;        // routed scaling factor of the combine
   // LDS byte offsets
   int lds_xs, lds_lg, lds_hs, lds_ysh, lds_ysr, lds_small;  // lds_hs: [3*M][I] bf16
+  int lds_gn;         // [H] bf16 norm gain
   const uint16_t* x_in;
   void* out;
   const int32_t* tk_idx_in;
@@ -328,12 +332,13 @@ __device__ __forceinline__ void compute_down(const DownRegs<CPLI, DBLK>& r, int 
 // K rounds over one row held by one wave, PER keys per lane in lane-major
 // blocks (lane L holds experts L*PER .. L*PER+PER-1); key 0 marks "no expert".
 template <int PER>
-__device__ __forceinline__ void select_rounds(const float* lr, int E, int K, int* out, int lane) {
+__device__ __forceinline__ void select_rounds(const float* lr, const float* bias, int E, int K,
+                                              int* out, int lane) {
   uint32_t keys[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane * PER + i;
-    keys[i] = e < E ? f_key(lr[e]) : 0u;
+    keys[i] = e < E ? f_key(lr[e] + (bias ? bias[e] : 0.0f)) : 0u;
   }
 #pragma unroll 1
   for (int k = 0; k < K; ++k) {
@@ -355,14 +360,14 @@ __device__ __forceinline__ void select_rounds(const float* lr, int E, int K, int
   }
 }
 
-__device__ __forceinline__ void select_row_plain(const float* lr, int E, int K, int* out,
-                                                 int lane) {
+__device__ __forceinline__ void select_row_plain(const float* lr, const float* bias, int E, int K,
+                                                 int* out, int lane) {
   const int per = (E + 63) >> 6;
-  if (per <= 1) select_rounds<1>(lr, E, K, out, lane);
-  else if (per <= 2) select_rounds<2>(lr, E, K, out, lane);
-  else if (per <= 4) select_rounds<4>(lr, E, K, out, lane);
-  else if (per <= 8) select_rounds<8>(lr, E, K, out, lane);
-  else select_rounds<16>(lr, E, K, out, lane);
+  if (per <= 1) select_rounds<1>(lr, bias, E, K, out, lane);
+  else if (per <= 2) select_rounds<2>(lr, bias, E, K, out, lane);
+  else if (per <= 4) select_rounds<4>(lr, bias, E, K, out, lane);
+  else if (per <= 8) select_rounds<8>(lr, bias, E, K, out, lane);
+  else select_rounds<16>(lr, bias, E, K, out, lane);
 }
 
 // Gates of row m from its K selected experts (tk_idx written by this wave):
@@ -379,12 +384,13 @@ __device__ __forceinline__ void gates_from_idx(const float* lr, int K, Small* sm
 
 // Fast path for exactly MM token rows (see above).
 template <int MM>
-__device__ __forceinline__ void topk_fast(const float* lgs, Small* sm, int E, int K, int nW,
-                                          int tid, int wv, int lane) {
-  // (a) every wave: its group maximum, for every row
+__device__ __forceinline__ void topk_fast(const float* lgs, float bv, Small* sm, int E, int K,
+                                          int nW, int tid, int wv, int lane) {
+  // (a) every wave: its group maximum, for every row (scores = logit + this
+  //     thread's expert bias, 0 without one)
   uint32_t key[MM];
 #pragma unroll
-  for (int m = 0; m < MM; ++m) key[m] = tid < E ? f_key(lgs[m * E + tid]) : 0u;
+  for (int m = 0; m < MM; ++m) key[m] = tid < E ? f_key(lgs[m * E + tid] + bv) : 0u;
   uint32_t mine = 0u;
 #pragma unroll
   for (int m = 0; m < MM; ++m) {
@@ -426,22 +432,25 @@ __device__ __forceinline__ void topk_fast(const float* lgs, Small* sm, int E, in
   __syncthreads();
 }
 
+// bv: the selection bias of expert tid (0 without a bias), loaded before the
+// logits arrive; bias: the bias vector for the plain path (or null).
 template <class P>
-__device__ __forceinline__ void topk_rows(const P& p, const float* lgs, Small* sm, int tid,
-                                          int wv, int lane) {
+__device__ __forceinline__ void topk_rows(const P& p, const float* lgs, float bv,
+                                          const float* bias, Small* sm, int tid, int wv,
+                                          int lane) {
   const int M = p.M, E = p.E, K = p.K;
   const int nW = (E + 63) >> 6;
   const bool fast = E <= MOE_WG && K <= nW;
   if (fast) {
     switch (M) {
-      case 1: topk_fast<1>(lgs, sm, E, K, nW, tid, wv, lane); break;
-      case 2: topk_fast<2>(lgs, sm, E, K, nW, tid, wv, lane); break;
-      case 3: topk_fast<3>(lgs, sm, E, K, nW, tid, wv, lane); break;
-      case 4: topk_fast<4>(lgs, sm, E, K, nW, tid, wv, lane); break;
-      case 5: topk_fast<5>(lgs, sm, E, K, nW, tid, wv, lane); break;
-      case 6: topk_fast<6>(lgs, sm, E, K, nW, tid, wv, lane); break;
-      case 7: topk_fast<7>(lgs, sm, E, K, nW, tid, wv, lane); break;
-      default: topk_fast<8>(lgs, sm, E, K, nW, tid, wv, lane); break;
+      case 1: topk_fast<1>(lgs, bv, sm, E, K, nW, tid, wv, lane); break;
+      case 2: topk_fast<2>(lgs, bv, sm, E, K, nW, tid, wv, lane); break;
+      case 3: topk_fast<3>(lgs, bv, sm, E, K, nW, tid, wv, lane); break;
+      case 4: topk_fast<4>(lgs, bv, sm, E, K, nW, tid, wv, lane); break;
+      case 5: topk_fast<5>(lgs, bv, sm, E, K, nW, tid, wv, lane); break;
+      case 6: topk_fast<6>(lgs, bv, sm, E, K, nW, tid, wv, lane); break;
+      case 7: topk_fast<7>(lgs, bv, sm, E, K, nW, tid, wv, lane); break;
+      default: topk_fast<8>(lgs, bv, sm, E, K, nW, tid, wv, lane); break;
     }
   }
   // (c) one wave per row: rank the candidates, or K plain rounds
@@ -465,7 +474,7 @@ __device__ __forceinline__ void topk_rows(const P& p, const float* lgs, Small* s
       // gates in rank order (the candidates' lane order depends on timing)
       gates_from_idx(lgs + m * E, K, sm, m, lane);
     } else {
-      select_row_plain(lgs + m * E, E, K, sm->tk_idx + m * K, lane);
+      select_row_plain(lgs + m * E, bias, E, K, sm->tk_idx + m * K, lane);
       gates_from_idx(lgs + m * E, K, sm, m, lane);
     }
   }
@@ -557,6 +566,8 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
   const uint4* hs4 = reinterpret_cast<const uint4*>(lds + p.lds_hs);
   float* ysh = reinterpret_cast<float*>(lds + p.lds_ysh);
   float* ysr = reinterpret_cast<float*>(lds + p.lds_ysr);
+  uint4* gn4 = reinterpret_cast<uint4*>(lds + p.lds_gn);
+  static_assert(CPLH * 32 <= MOE_WG, "one 16-byte gain chunk per thread");
   Small* sm = reinterpret_cast<Small*>(lds + p.lds_small);
 
   const int G = gridDim.x, g = blockIdx.x;
@@ -598,6 +609,10 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     if (gw < NRI + NSI) p1_load<CPLH>(p, l, gw, NRI, A, B, lane, false);
 
     // ---------------- P0: layer input -> LDS
+    // the norm's gain does not depend on the input: its load flies during the stage
+    const uint16_t* gain = (p.flags & F_PRENORM) ? p.lw[l].gain : nullptr;
+    uint4 gpre = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);  // bf16 ones
+    if (gain && tid < (H >> 3)) gpre = reinterpret_cast<const uint4*>(gain)[tid];
     if (l == 0) {
       const uint4* src = reinterpret_cast<const uint4*>(p.x_in);
       uint4* dst = reinterpret_cast<uint4*>(xs);
@@ -622,28 +637,41 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       for (int i = tid; i < (M * H) >> 3; i += MOE_WG) dst[i] = xs4[i];
     }
     if (p.flags & F_PRENORM) {
+      if (tid < (H >> 3)) gn4[tid] = gpre;
       // Sum of squares per row in double: every bf16 square is exact in fp32 and,
       // over the value range of a residual stream, every partial sum is exact in
       // double, so the sum (and the scale) does not depend on the order.
-      const uint32_t* xr32 = reinterpret_cast<const uint32_t*>(xs);
       for (int m = wv; m < M; m += MOE_WAVES) {
         double ss = 0.0;
-        for (int c = lane; c < H2; c += 64) {
-          const uint32_t w = xr32[m * H2 + c];
-          const float a = bf_lo(w), b = bf_hi(w);
-          ss += (double)(a * a);
-          ss += (double)(b * b);
-        }
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+        for (int j = 0; j < (CPLH + 1) / 2; ++j) {
+          const int c = lane + 64 * j;
+          if (c < (H >> 3)) {
+            const uint4 v = xs4[m * (H >> 3) + c];
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float a = bf_lo(w4[q]), b = bf_hi(w4[q]);
+              ss += (double)(a * a);
+              ss += (double)(b * b);
+            }
+          }
+        }
+        ss = wave_sum_f64(ss);
         if (lane == 0) sm->rn[m] = (float)(1.0 / sqrt(ss / (double)H + (double)kRmsEps));
       }
       __syncthreads();
+      // u = bf16((h * r) * gain): two fp32 products, one rounding
       uint32_t* x32 = reinterpret_cast<uint32_t*>(xs);
-      for (int i = tid; i < M * H2; i += MOE_WG) {
-        const float r = sm->rn[i / H2];
-        const uint32_t w = x32[i];
-        x32[i] = f_to_bf(bf_lo(w) * r) | (f_to_bf(bf_hi(w) * r) << 16);
+      const uint32_t* g32 = reinterpret_cast<const uint32_t*>(gn4);
+      for (int c = tid; c < H2; c += MOE_WG) {
+        const uint32_t gw = g32[c];
+        const float glo = bf_lo(gw), ghi = bf_hi(gw);
+        for (int m = 0; m < M; ++m) {
+          const float r = sm->rn[m];
+          const uint32_t w = x32[m * H2 + c];
+          x32[m * H2 + c] = f_to_bf((bf_lo(w) * r) * glo) | (f_to_bf((bf_hi(w) * r) * ghi) << 16);
+        }
       }
     }
     __syncthreads();
@@ -683,6 +711,9 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       }
       __syncthreads();
     } else {
+      // the selection bias does not depend on the logits: load it before waiting
+      const float* bias = p.lw[l].bias;
+      const float bv = (bias && tid < E) ? bias[tid] : 0.0f;
       const uint64_t* src = p.lg_buf + (size_t)l * M * E;
       if (!stage_tagged<8>(M * E, reinterpret_cast<uint32_t*>(lgs), tag, wt, tid,
                            [&](int i) { return src + i; }))
@@ -690,7 +721,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       __syncthreads();
       MOE_STAMP(3);
       if (sm->abort_flag == 1) break;
-      topk_rows(p, lgs, sm, tid, wv, lane);
+      topk_rows(p, lgs, bv, bias, sm, tid, wv, lane);
       __syncthreads();
       MOE_STAMP(9);
       if (g == 0 || router_only) {
@@ -845,18 +876,18 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       for (int i = tid; i < (NR >> 1) * M; i += MOE_WG) {
         const int np = i / M, m = i - np * M;
         const int nl = 2 * np, n = n0 + nl;
-        float a0 = S ? ysh[m * p.nr_max + nl] : 0.0f;
-        float a1 = S ? ysh[m * p.nr_max + nl + 1] : 0.0f;
+        // routed sum in fp32, scaled once, then the shared expert
+        float q0 = 0.0f, q1 = 0.0f;
         for (int k = 0; k < K; ++k) {
           const int r = sm->upos[m * K + k];
           if (r < 0) continue;
           const int pr = sm->pbase[r] + __builtin_popcount(sm->umask[r] & ((1u << m) - 1u));
           const float gk = sm->tk_gate[m * K + k];
-          const float t0 = gk * ysr[pr * NR + nl];
-          const float t1 = gk * ysr[pr * NR + nl + 1];
-          a0 = a0 + t0;
-          a1 = a1 + t1;
+          q0 = q0 + gk * ysr[pr * NR + nl];
+          q1 = q1 + gk * ysr[pr * NR + nl + 1];
         }
+        const float a0 = (S ? ysh[m * p.nr_max + nl] : 0.0f) + p.scale * q0;
+        const float a1 = (S ? ysh[m * p.nr_max + nl + 1] : 0.0f) + p.scale * q1;
         if (p.flags & F_RESIDUAL) {
           const float h0 = bf_to_f(sm->hres[m * p.nr_max + nl]);
           const float h1 = bf_to_f(sm->hres[m * p.nr_max + nl + 1]);

@@ -1,7 +1,9 @@
 """Write tiefree_rows.json: per workload, the generator attempt index of each
 input row such that the oracle's routing has no near-tie (K-th minus (K+1)-th
-logit >= DELTA at every layer) and, for the lm_head workload, no near-tie in
-the argmax (top two float64 logits DELTA apart).
+selection score >= DELTA at every layer; the score is the logit plus the
+selection bias, on the normed input where the workload has the router front)
+and, for the lm_head workload, no near-tie in the argmax (top two float64
+logits DELTA apart).
 
 Calls only the oracle and the seeded generator.  Usage:
     python tests/golden/make_tiefree.py
@@ -16,15 +18,20 @@ sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
 import numpy as np  # noqa: E402
 
 from datagen import workloads as W  # noqa: E402
-from oracle import router_topk, runner  # noqa: E402
+from oracle import rmsnorm, router_topk, runner  # noqa: E402
 
 DELTA = 1e-3
-ROWS = {W.C1.name: 8, W.C2.name: 8, W.C3.name: 6, W.C4.name: 6, W.C5.name: 6}
+ROWS = {W.C1.name: 8, W.C2.name: 8, W.C3.name: 6, W.C4.name: 6, W.C5.name: 6,
+        W.C6.name: 8, W.C7.name: 8}
 
 
 def row_ok_single(wl, xrow, wr):
-    _, _, lg = router_topk(xrow[None, :], wr, wl.K)
-    return runner.router_margin(lg, wl.K)[0] >= DELTA
+    u = xrow[None, :]
+    if wl.prenorm:
+        u = rmsnorm(u, gain=W.norm_gain(wl, 0))
+    bias = W.router_bias(wl, 0)
+    _, _, lg = router_topk(u, wr, wl.K, bias)
+    return runner.router_margin(lg, wl.K, bias)[0] >= DELTA
 
 
 def row_ok_chain(wl, xrow, routers, lm):
@@ -36,7 +43,7 @@ def row_ok_chain(wl, xrow, routers, lm):
 
 def main():
     out = {"delta": DELTA, "workloads": {}}
-    for wl in W.ALL:
+    for wl in W.ALL + W.FRONT:
         n = ROWS[wl.name]
         attempts = []
         if wl.n_layers == 1:

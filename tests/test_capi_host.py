@@ -90,22 +90,22 @@ def test_workspace_size_layout_and_errors():
 def test_dims_validation(kw, rc):
     d = md.dims(**dict(LING, **kw))
     assert md.moe_workspace_size(d, 1, 1)[0] == rc
-    assert md.moe_router_topk(d, 1, A, A, A, A, None, A, 1 << 30, stream=0) == rc
+    assert md.moe_router_topk(d, 1, A, A, None, A, A, None, A, 1 << 30, stream=0) == rc
 
 
 def test_router_topk_validation():
     d = md.dims(**LING)
     big = 1 << 30
-    assert md.moe_router_topk(d, 0, A, A, A, A, None, A, big, stream=0) == md.MOE_E_ARG
-    assert md.moe_router_topk(d, 9, A, A, A, A, None, A, big, stream=0) == md.MOE_E_UNSUPPORTED
-    assert md.moe_router_topk(d, 1, None, A, A, A, None, A, big, stream=0) == md.MOE_E_ARG
-    assert md.moe_router_topk(d, 1, A, None, A, A, None, A, big, stream=0) == md.MOE_E_ARG
-    assert md.moe_router_topk(d, 1, A, A, None, A, None, A, big, stream=0) == md.MOE_E_ARG
-    assert md.moe_router_topk(d, 1, BAD, A, A, A, None, A, big, stream=0) == md.MOE_E_ALIGN
-    assert md.moe_router_topk(d, 1, A, BAD, A, A, None, A, big, stream=0) == md.MOE_E_ALIGN
-    assert md.moe_router_topk(d, 1, A, A, A, A, None, None, big, stream=0) == md.MOE_E_WORKSPACE
-    assert md.moe_router_topk(d, 1, A, A, A, A, None, BAD, big, stream=0) == md.MOE_E_ALIGN
-    assert md.moe_router_topk(d, 1, A, A, A, A, None, A, 4096, stream=0) == md.MOE_E_WORKSPACE
+    assert md.moe_router_topk(d, 0, A, A, None, A, A, None, A, big, stream=0) == md.MOE_E_ARG
+    assert md.moe_router_topk(d, 9, A, A, None, A, A, None, A, big, stream=0) == md.MOE_E_UNSUPPORTED
+    assert md.moe_router_topk(d, 1, None, A, None, A, A, None, A, big, stream=0) == md.MOE_E_ARG
+    assert md.moe_router_topk(d, 1, A, None, None, A, A, None, A, big, stream=0) == md.MOE_E_ARG
+    assert md.moe_router_topk(d, 1, A, A, None, None, A, None, A, big, stream=0) == md.MOE_E_ARG
+    assert md.moe_router_topk(d, 1, BAD, A, None, A, A, None, A, big, stream=0) == md.MOE_E_ALIGN
+    assert md.moe_router_topk(d, 1, A, BAD, None, A, A, None, A, big, stream=0) == md.MOE_E_ALIGN
+    assert md.moe_router_topk(d, 1, A, A, None, A, A, None, None, big, stream=0) == md.MOE_E_WORKSPACE
+    assert md.moe_router_topk(d, 1, A, A, None, A, A, None, BAD, big, stream=0) == md.MOE_E_ALIGN
+    assert md.moe_router_topk(d, 1, A, A, None, A, A, None, A, 4096, stream=0) == md.MOE_E_WORKSPACE
 
 
 def test_experts_fused_validation():
@@ -141,6 +141,32 @@ def test_layer_chain_validation():
     assert c(d, 1, [lw], A, A, 0, R, A + 2, A, big, stream=0) == md.MOE_E_ALIGN
     rc, need = md.moe_workspace_size(d, 6, 16)
     assert c(d, 6, [lw] * 16, A, A, 0, R, None, A, need - 256, stream=0) == md.MOE_E_WORKSPACE
+
+
+def test_router_front_validation():
+    """Selection bias, norm gain and routed scale are checked on the host too."""
+    assert ctypes.sizeof(md.moe_dims) == 24 and ctypes.sizeof(md.moe_layer_weights) == 40
+    big = 1 << 30
+    for bad in (float("nan"), float("inf"), -float("inf")):
+        d = md.dims(**LING, routed_scale=bad)
+        assert md.moe_workspace_size(d, 1, 1)[0] == md.MOE_E_ARG
+        assert md.moe_router_topk(d, 1, A, A, None, A, A, None, A, big, stream=0) == md.MOE_E_ARG
+    d = md.dims(**LING, routed_scale=2.5)
+    assert md.moe_workspace_size(d, 1, 1)[0] == md.MOE_OK
+    assert md.moe_router_topk(d, 1, A, A, A + 2, A, A, None, A, big, stream=0) == md.MOE_E_ALIGN
+    c = md.moe_layer_chain
+    R, PN, PL = (md.MOE_CHAIN_RESIDUAL, md.MOE_CHAIN_PRENORM_RESIDUAL,
+                 md.MOE_CHAIN_PRENORM_LAYER_ONLY)
+    lw = md.layer_weights(A, A, A, A, A)
+    assert c(d, 1, [lw, lw], A, A, 0, PL, None, A, big, stream=0) == md.MOE_E_UNSUPPORTED
+    assert c(d, 1, [lw], A, A, 0, PL, None, A, big, stream=0, h_all=A * 4) == md.MOE_E_ARG
+    assert c(d, 1, [lw], A, A, 0, 4, None, A, big, stream=0) == md.MOE_E_ARG
+    assert c(d, 1, [md.layer_weights(A, A, A, A + 1, A)], A, A, 0, R, None, A, big,
+             stream=0) == md.MOE_E_ALIGN
+    assert c(d, 1, [md.layer_weights(A, A, A, None, A + 2)], A, A, 0, PN, None, A, big,
+             stream=0) == md.MOE_E_ALIGN
+    assert c(d, 1, [md.layer_weights(A, A, A, None, A + 2)], A, A, 1, PL, None, A, big,
+             stream=0) == md.MOE_E_ALIGN
 
 
 def test_lmhead_validation():

@@ -100,7 +100,7 @@ def test_router_topk(gpu, dw, wl, M):
     gate = _empty((M, wl.K), torch.float32, gpu)
     lg = _empty((M, wl.E), torch.float32, gpu)
     say("router_topk %s M=%d" % (wl.name, M))
-    md.check(md.moe_router_topk(d, M, D.to_device(x), L.w_router, idx, gate, lg, ws))
+    md.check(md.moe_router_topk(d, M, D.to_device(x), L.w_router, None, idx, gate, lg, ws))
     md.check(md.moe_last_device_status(ws))
     ri, rg, rl = oracle.router_topk(x, W.router(wl, 0), wl.K)
     gi, gg, gl = idx.cpu().numpy(), gate.cpu().numpy(), lg.cpu().numpy()
@@ -130,7 +130,7 @@ def test_router_exact_on_dyadic_inputs(gpu):
     gate = _empty((M, K), torch.float32, gpu)
     lg = _empty((M, E), torch.float32, gpu)
     say("router_topk dyadic exact")
-    md.check(md.moe_router_topk(d, M, D.to_device(xb), D.to_device(wb), idx, gate, lg, ws))
+    md.check(md.moe_router_topk(d, M, D.to_device(xb), D.to_device(wb), None, idx, gate, lg, ws))
     ri, _, rl = oracle.router_topk(xb, wb, K)
     assert np.array_equal(lg.cpu().numpy(), rl)
     assert np.array_equal(idx.cpu().numpy(), ri)   # exact logits: ties resolved identically
@@ -179,7 +179,7 @@ def test_router_topk_planted_ties(gpu, M):
     gate = _empty((M, K), torch.float32, gpu)
     lg = _empty((M, E), torch.float32, gpu)
     say("router_topk planted ties M=%d" % M)
-    md.check(md.moe_router_topk(d, M, D.to_device(xb), D.to_device(wb), idx, gate, lg, ws))
+    md.check(md.moe_router_topk(d, M, D.to_device(xb), D.to_device(wb), None, idx, gate, lg, ws))
     md.check(md.moe_last_device_status(ws))
     ri, rg, rl = oracle.router_topk(xb, wb, K)
     assert np.array_equal(lg.cpu().numpy(), rl)
