@@ -53,7 +53,8 @@ def parse():
 # Workloads of --profile-run: (workload name, rows, fp32 partial output)
 PROFILE_WORKLOADS = {"m1": ("ling_moe_layer_m1", 1, False),
                      "m6": ("ling_moe_layer_m6", 6, False),
-                     "tp4": ("ling_tp4_shard_moe_layer_m6", 6, True)}
+                     "tp4": ("ling_tp4_shard_moe_layer_m6", 6, True),
+                     "front": ("ling_moe_layer_front_m6", 6, False)}
 COPY_BYTES = 256 << 20   # reference copy for the counter scale
 PROFILE_CALLS = 64
 
@@ -300,12 +301,20 @@ def profile_run(key):
     from datagen import workloads as W
 
     name, M, f32 = PROFILE_WORKLOADS[key]
-    wl = {w.name: w for w in (W.C2, W.C3, W.C4)}[name]
+    wl = {w.name: w for w in (W.C2, W.C3, W.C4, W.C7)}[name]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     layers = [D.make_layer(wl, l) for l in range(N_LAYERS)]
-    lws = [md.layer_weights(L.w_router, L.w_gate_up, L.w_down) for L in layers]
-    d = md.dims(wl.H, wl.E, wl.K, wl.I, wl.S)
+    keep = []
+    lws = []
+    for l, L in enumerate(layers):
+        b, g = W.router_bias(wl, l), W.norm_gain(wl, l)
+        b = None if b is None else D.to_device(b)
+        g = None if g is None else D.to_device(g)
+        keep.append((b, g))
+        lws.append(md.layer_weights(L.w_router, L.w_gate_up, L.w_down, b, g))
+    mode = md.MOE_CHAIN_PRENORM_LAYER_ONLY if wl.prenorm else md.MOE_CHAIN_LAYER_ONLY
+    d = md.dims(wl.H, wl.E, wl.K, wl.I, wl.S, wl.routed_scale)
     ws = md.new_workspace(d, M, 1)
     xs = torch.stack([D.to_device(W.x_rows(wl, [s * M + m for m in range(M)]))
                       for s in range(PROFILE_CALLS)])
@@ -319,13 +328,12 @@ def profile_run(key):
     torch.cuda.synchronize()
     for i in range(PROFILE_CALLS):
         md.check(md.moe_layer_chain(d, M, [lws[i % N_LAYERS]], xs[i], out,
-                                    md.MOE_OUT_F32 if f32 else md.MOE_OUT_BF16,
-                                    md.MOE_CHAIN_LAYER_ONLY, idx[i], ws))
+                                    md.MOE_OUT_F32 if f32 else md.MOE_OUT_BF16, mode, idx[i], ws))
     torch.cuda.synchronize()
     md.check(md.moe_last_device_status(ws))
     ids = idx.cpu().numpy()
     U = [len(set(ids[i].ravel().tolist())) for i in range(PROFILE_CALLS)]
-    alg = wl.router_bytes() + (sum(U) / len(U) + wl.S) * wl.expert_bytes()
+    alg = wl.router_bytes() + (sum(U) / len(U) + wl.S) * wl.expert_bytes() + wl.front_bytes()
     print("profile run %s: 1 copy of %d bytes, %d layer launches" % (key, COPY_BYTES,
                                                                       PROFILE_CALLS))
     print("algorithmic bytes per launch: %.0f (mean union %.2f experts)" % (alg, sum(U) / len(U)),
