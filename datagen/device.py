@@ -5,15 +5,18 @@ workloads.py, so every device tensor equals its host counterpart bit for bit.
 """
 import numpy as np
 
-from . import SIGMA_W, TENSOR_DOWN, TENSOR_GATE_UP, TENSOR_LMHEAD, TENSOR_ROUTER, fill_device, key
+from . import (SIGMA_W, TENSOR_DOWN, TENSOR_DOWN_FP8, TENSOR_GATE_UP, TENSOR_GATE_UP_FP8,
+               TENSOR_LMHEAD, TENSOR_ROUTER, fill_device, fill_device_fp8, key)
 from .workloads import WEIGHT_SEED
 
 
 class DeviceLayer:
-    def __init__(self, w_router, w_gate_up, w_down):
+    def __init__(self, w_router, w_gate_up, w_down, s_gate_up=None, s_down=None):
         self.w_router = w_router      # int16 [E][H]
-        self.w_gate_up = w_gate_up    # int16 [E+S][2I][H]
-        self.w_down = w_down          # int16 [E+S][H][I]
+        self.w_gate_up = w_gate_up    # int16 [E+S][2I][H] (uint8 codes for fp8)
+        self.w_down = w_down          # int16 [E+S][H][I] (uint8 codes for fp8)
+        self.s_gate_up = s_gate_up    # fp8 only: float32 [E+S][2I/128][H/128]
+        self.s_down = s_down          # fp8 only: float32 [E+S][H/128][I/128]
 
 
 def _keys(keys, dev):
@@ -50,6 +53,29 @@ def make_layer(wl, layer, dev="cuda"):
     torch.cuda.synchronize()
     del kr, kg, kd
     return DeviceLayer(wr, gu, dn)
+
+
+def make_layer_fp8(wl, layer, dev="cuda"):
+    """fp8 expert codes generated on the device; block scales generated on the host."""
+    import torch
+    from . import workloads as W
+    H, E, I, S = wl.H, wl.E, wl.I, wl.S
+    st = _stream()
+    wr = torch.empty((E, H), dtype=torch.int16, device=dev)
+    kr = _keys([key(WEIGHT_SEED, wl.family, layer, TENSOR_ROUTER)], dev)
+    fill_device(wr.data_ptr(), kr.data_ptr(), 1, 0, E, H, SIGMA_W, stream=st)
+    gu = torch.empty((E + S, 2 * I, H), dtype=torch.uint8, device=dev)
+    kg = _keys([key(WEIGHT_SEED, wl.family, layer, TENSOR_GATE_UP_FP8, e) for e in range(E + S)],
+               dev)
+    fill_device_fp8(gu.data_ptr(), kg.data_ptr(), E + S, 2 * I * H, 2 * I, H, stream=st)
+    dn = torch.empty((E + S, H, I), dtype=torch.uint8, device=dev)
+    kd = _keys([key(WEIGHT_SEED, wl.family, layer, TENSOR_DOWN_FP8, e) for e in range(E + S)], dev)
+    fill_device_fp8(dn.data_ptr(), kd.data_ptr(), E + S, H * I, H, I, stream=st)
+    sg = np.stack([W.expert_gate_up_scales(wl, layer, e) for e in range(E + S)])
+    sd = np.stack([W.expert_down_scales(wl, layer, e) for e in range(E + S)])
+    torch.cuda.synchronize()
+    del kr, kg, kd
+    return DeviceLayer(wr, gu, dn, to_device(sg), to_device(sd))
 
 
 def make_lmhead(wl, dev="cuda"):

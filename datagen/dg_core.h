@@ -1,7 +1,7 @@
 /* Seeded synthetic-input generator: counter-based, integer-exact.
  *
  * Test and benchmark infrastructure only.  It holds none of the MoE method's
- * arithmetic; it only produces the seeded bf16 tensors that both the CPU
+ * arithmetic; it only produces the seeded bf16 (and fp8 code) tensors that both the CPU
  * oracle and the GPU path consume.  The same element is produced bit-for-bit
  * on the host (dg_host.c, gcc) and on the device (dg_device.hip, hipcc)
  * because every step is integer arithmetic followed by exactly one IEEE fp32
@@ -69,6 +69,44 @@ DG_FN uint16_t dg_f32_to_bf16(float f) {
 DG_FN uint16_t dg_value(uint64_t key, uint64_t n, float scale) {
   float x = (float)dg_ih12(key, n);  /* exact: |s| < 2^24 */
   return dg_f32_to_bf16(x * scale);
+}
+
+/* fp8 e4m3 (OCP "e4m3fn") code of v = s * mul / 65536, rounded to nearest
+ * (ties to even) and saturated at +-448; integer arithmetic only, so host and
+ * device agree.  Used to draw synthetic block-quantised expert weights
+ * directly in the code domain (s: an Irwin-Hall(12) sample, mul: the code-unit
+ * standard deviation).  Values are q * 2^p with q < 16; exponent field p + 10
+ * for q >= 8, field 0 (subnormal, p = -9) for q < 8. */
+DG_FN uint8_t dg_e4m3_code(int32_t s, int32_t mul) {
+  const uint8_t sign = s < 0 ? 0x80u : 0u;
+  const uint64_t a = (uint64_t)(s < 0 ? -(int64_t)s : (int64_t)s) * (uint64_t)mul;
+  if (a == 0) return sign;
+  int lg = 0;
+  for (uint64_t t = a; t > 1; t >>= 1) ++lg;
+  int e = lg - 16;
+  if (e < -6) e = -6;
+  int p = e - 3;
+  const int sh = 16 + p;
+  uint64_t q;
+  if (sh <= 0) {
+    q = a << (-sh);
+  } else {
+    q = a >> sh;
+    const uint64_t rem = a & ((1ULL << sh) - 1ULL), half = 1ULL << (sh - 1);
+    if (rem > half || (rem == half && (q & 1ULL))) ++q;
+  }
+  if (q >= 16) {
+    q >>= 1;
+    ++p;
+  }
+  const int ef = p + 10;
+  if (ef > 15 || (ef == 15 && q > 14)) return (uint8_t)(sign | 0x7Eu);
+  if (q < 8) return (uint8_t)(sign | (uint8_t)q);
+  return (uint8_t)(sign | (uint8_t)((ef << 3) | (int)(q - 8)));
+}
+
+DG_FN uint8_t dg_value_fp8(uint64_t key, uint64_t n, int32_t mul) {
+  return dg_e4m3_code(dg_ih12(key, n), mul);
 }
 
 #endif

@@ -49,6 +49,39 @@ extern "C" int dg_fill_bf16_dev(uint16_t* out, const uint64_t* keys_dev, int n_b
   return e == hipSuccess ? 0 : -(1000 + (int)e);
 }
 
+/* fp8 codes, laid out as dg_fill_kernel lays out bf16 values (row-major only). */
+__global__ void dg_fill_fp8_kernel(uint8_t* __restrict__ out, const uint64_t* __restrict__ keys,
+                                   int64_t block_stride, int64_t row0, int64_t col0, int64_t rows,
+                                   int64_t cols, int64_t ld_full, int32_t mul) {
+  const int64_t b = blockIdx.y;
+  const uint64_t key = keys[b];
+  const int64_t total = rows * cols;
+  uint8_t* o = out + b * block_stride;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / cols, c = i - r * cols;
+    const uint64_t n = (uint64_t)(row0 + r) * (uint64_t)ld_full + (uint64_t)(col0 + c);
+    o[i] = dg_value_fp8(key, n, mul);
+  }
+}
+
+extern "C" int dg_fill_fp8_dev(uint8_t* out, const uint64_t* keys_dev, int n_blocks,
+                               int64_t block_stride, int64_t row0, int64_t col0, int64_t rows,
+                               int64_t cols, int64_t ld_full, int32_t mul, void* stream) {
+  if (n_blocks <= 0 || rows <= 0 || cols <= 0) return 0;
+  if (n_blocks > 65535) return -1;
+  const hipError_t before = hipGetLastError();
+  if (before != hipSuccess) return -(2000 + (int)before);
+  const int threads = 256;
+  int64_t per = (rows * cols + threads - 1) / threads;
+  int gx = (int)(per < 4096 ? per : 4096);
+  hipLaunchKernelGGL(dg_fill_fp8_kernel, dim3(gx, n_blocks), dim3(threads), 0,
+                     (hipStream_t)stream, out, keys_dev, block_stride, row0, col0, rows, cols,
+                     ld_full, mul);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? 0 : -(1000 + (int)e);
+}
+
 extern "C" const char* dg_error_string(int code) {
   int e = -code;
   if (e >= 2000) e -= 2000; else if (e >= 1000) e -= 1000;

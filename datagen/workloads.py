@@ -9,9 +9,10 @@ dg_core.h).  Nothing here computes any part of the MoE layer.
 """
 from dataclasses import dataclass
 
-from . import (FAMILY_LING, FAMILY_TINY, SIGMA_W, SIGMA_X, TENSOR_BIAS, TENSOR_DOWN,
-               TENSOR_GAIN, TENSOR_GATE_UP, TENSOR_LMHEAD, TENSOR_ROUTER, TENSOR_X, fill_host,
-               key, round_bf16_bits)
+from . import (FAMILY_LING, FAMILY_TINY, FP8_BLOCK, FP8_MUL, SIGMA_W, SIGMA_X, TENSOR_BIAS,
+               TENSOR_DOWN, TENSOR_DOWN_FP8, TENSOR_GAIN, TENSOR_GATE_UP, TENSOR_GATE_UP_FP8,
+               TENSOR_LMHEAD, TENSOR_ROUTER, TENSOR_SCALE_D, TENSOR_SCALE_GU, TENSOR_X, fill_host,
+               fill_host_fp8, fill_scales, key, round_bf16_bits)
 
 WEIGHT_SEED = 0x5EED0001
 
@@ -38,12 +39,18 @@ class Workload:
     bias_sigma: float = 0.0     # router selection bias ~N(0, bias_sigma^2) per expert (0: none)
     gain_sigma: float = 0.0     # norm gain ~1 + N(0, gain_sigma^2) per channel (0: unit gain)
     routed_scale: float = 1.0   # routed scaling factor of the combine
+    fp8: bool = False           # expert weights as fp8 e4m3 codes with 128x128 block scales
 
     @property
     def I_full(self):
         return self.I * self.n_shards
 
     def expert_bytes(self):
+        """HBM bytes of one expert (weights, plus block scales for fp8)."""
+        if self.fp8:
+            nb = (2 * self.I // FP8_BLOCK) * (self.H // FP8_BLOCK) + \
+                (self.H // FP8_BLOCK) * (self.I // FP8_BLOCK)
+            return 3 * self.H * self.I + 4 * nb
         return 3 * self.H * self.I * 2
 
     def router_bytes(self):
@@ -76,8 +83,18 @@ C6 = Workload("tiny_moe_layer_front_m3", 6, FAMILY_TINY, H=256, E=16, K=2, I=64,
 C7 = Workload("ling_moe_layer_front_m6", 7, FAMILY_LING, H=2560, E=512, K=8, I=768, S=1, M=6,
               x_seed=707, prenorm=True, bias_sigma=0.25, gain_sigma=0.1, routed_scale=2.5)
 
+# fp8 e4m3 expert weights with 128x128 block scales (the router stays bf16).  The
+# block-128 format needs I % 128 == 0, so there is no TP4 shard of I = 768.
+C8 = Workload("tiny_fp8_moe_layer_m3", 8, FAMILY_TINY, H=256, E=16, K=2, I=128, S=1, M=3,
+              x_seed=808, fp8=True)
+C9 = Workload("ling_fp8_moe_layer_m1", 9, FAMILY_LING, H=2560, E=512, K=8, I=768, S=1, M=1,
+              x_seed=909, fp8=True)
+C10 = Workload("ling_fp8_moe_layer_m6", 10, FAMILY_LING, H=2560, E=512, K=8, I=768, S=1, M=6,
+               x_seed=1010, fp8=True)
+
 ALL = (C1, C2, C3, C4, C5)
 FRONT = (C6, C7)
+FP8 = (C8, C9, C10)
 
 
 # ---- host slices ------------------------------------------------------------
@@ -110,6 +127,28 @@ def expert_down(wl, layer, e):
     """[H][I]: this shard's columns of the full [H][I_full] tensor."""
     k = key(WEIGHT_SEED, wl.family, layer, TENSOR_DOWN, e)
     return fill_host(k, wl.H, wl.I, SIGMA_W, col0=wl.shard * wl.I, ld_full=wl.I_full)
+
+
+def expert_gate_up_scales(wl, layer, e):
+    ks = key(WEIGHT_SEED, wl.family, layer, TENSOR_SCALE_GU, e)
+    return fill_scales(ks, (2 * wl.I // FP8_BLOCK, wl.H // FP8_BLOCK), SIGMA_W / FP8_MUL)
+
+
+def expert_down_scales(wl, layer, e):
+    ks = key(WEIGHT_SEED, wl.family, layer, TENSOR_SCALE_D, e)
+    return fill_scales(ks, (wl.H // FP8_BLOCK, wl.I // FP8_BLOCK), SIGMA_W / FP8_MUL)
+
+
+def expert_gate_up_fp8(wl, layer, e):
+    """(codes uint8 [2I][H], block scales fp32 [2I/128][H/128]) of one expert."""
+    k = key(WEIGHT_SEED, wl.family, layer, TENSOR_GATE_UP_FP8, e)
+    return fill_host_fp8(k, 2 * wl.I, wl.H), expert_gate_up_scales(wl, layer, e)
+
+
+def expert_down_fp8(wl, layer, e):
+    """(codes uint8 [H][I], block scales fp32 [H/128][I/128]) of one expert."""
+    k = key(WEIGHT_SEED, wl.family, layer, TENSOR_DOWN_FP8, e)
+    return fill_host_fp8(k, wl.H, wl.I), expert_down_scales(wl, layer, e)
 
 
 def router_bias(wl, layer=0):

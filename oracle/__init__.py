@@ -40,6 +40,12 @@ def lib():
         L.oracle_residual.argtypes = [_I64, _P, _P, _P]
         L.oracle_lmhead_argmax.argtypes = [_I, _I, _I, _P, _P, _P, _P]
         L.oracle_rmsnorm.argtypes = [_I, _I, _P, ctypes.c_float, _P, _P]
+        L.oracle_fp8_e4m3_to_f32.restype = ctypes.c_float
+        L.oracle_fp8_e4m3_to_f32.argtypes = [ctypes.c_uint8]
+        L.oracle_dequant_fp8.argtypes = [_I, _I, _P, _P, _P]
+        L.oracle_expert_fp8.argtypes = [_I, _I] + [_P] * 7
+        L.oracle_experts_combine_fp8.restype = _I
+        L.oracle_experts_combine_fp8.argtypes = [_I] * 6 + [_P] * 7 + [ctypes.c_float, _P]
         L.oracle_unique_weight_bytes.restype = _I64
         L.oracle_unique_weight_bytes.argtypes = [_I] * 6 + [_P, _I, _P]
         _lib = L
@@ -151,6 +157,67 @@ def experts_combine(x, idx, gate, w_gu_tab, w_d_tab, E, S, scale=1.0):
                                       ctypes.cast(d_ptrs, _P), float(scale), acc.ctypes.data)
     if rc != 0:
         raise ValueError("oracle_experts_combine: bad index or missing expert weights")
+    return acc
+
+
+def fp8_decode(codes):
+    """float32 values of fp8 e4m3 codes (uint8 array)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib().oracle_fp8_e4m3_to_f32(int(v)) for v in c.ravel()],
+                    dtype=np.float32).reshape(c.shape)
+
+
+def dequant_fp8(q, s):
+    """fp32 weights [rows, cols] of codes q with 128x128 block scales s."""
+    q = _c(q, np.uint8)
+    s = _c(s, np.float32)
+    rows, cols = q.shape
+    assert s.shape == ((rows + 127) // 128, (cols + 127) // 128)
+    w = np.empty((rows, cols), dtype=np.float32)
+    lib().oracle_dequant_fp8(rows, cols, q.ctypes.data, s.ctypes.data, w.ctypes.data)
+    return w
+
+
+def expert_fp8(x_row, q_gu, s_gu, q_d, s_d):
+    """One fp8 expert on one row: returns (y fp32 [H], h bf16 bits [I])."""
+    x_row = _c(x_row, np.uint16)
+    q_gu, s_gu = _c(q_gu, np.uint8), _c(s_gu, np.float32)
+    q_d, s_d = _c(q_d, np.uint8), _c(s_d, np.float32)
+    H = x_row.shape[0]
+    I = q_gu.shape[0] // 2
+    assert q_gu.shape == (2 * I, H) and q_d.shape == (H, I)
+    y = np.empty(H, dtype=np.float32)
+    h = np.empty(I, dtype=np.uint16)
+    lib().oracle_expert_fp8(H, I, x_row.ctypes.data, q_gu.ctypes.data, s_gu.ctypes.data,
+                            q_d.ctypes.data, s_d.ctypes.data, h.ctypes.data, y.ctypes.data)
+    return y, h
+
+
+def experts_combine_fp8(x, idx, gate, gu_tab, d_tab, E, S, scale=1.0):
+    """acc fp32 [M, H] with fp8 experts.  gu_tab / d_tab: dict expert id -> (codes, scales)."""
+    x = _c(x, np.uint16)
+    idx = _c(idx, np.int32)
+    gate = _c(gate, np.float32)
+    M, H = x.shape
+    K = idx.shape[1]
+    keep = []
+    tabs = [(ctypes.c_void_p * (E + 1))() for _ in range(4)]
+    I = None
+    for e, (q, s) in gu_tab.items():
+        q, s = _c(q, np.uint8), _c(s, np.float32)
+        keep += [q, s]
+        I = q.shape[0] // 2
+        tabs[0][e], tabs[1][e] = q.ctypes.data, s.ctypes.data
+    for e, (q, s) in d_tab.items():
+        q, s = _c(q, np.uint8), _c(s, np.float32)
+        keep += [q, s]
+        tabs[2][e], tabs[3][e] = q.ctypes.data, s.ctypes.data
+    acc = np.empty((M, H), dtype=np.float32)
+    rc = lib().oracle_experts_combine_fp8(H, E, K, I, int(S), M, x.ctypes.data, idx.ctypes.data,
+                                          gate.ctypes.data, *[ctypes.cast(t, _P) for t in tabs],
+                                          float(scale), acc.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_experts_combine_fp8: bad index or missing expert weights")
     return acc
 
 

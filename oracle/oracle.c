@@ -165,6 +165,74 @@ void oracle_expert(int H, int I, const uint16_t* x_row, const uint16_t* w_gu, co
   free(hb);
 }
 
+/* ---- fp8 block-128 expert weights ---------------------------------------
+ * ("Ling-3.0-flash on 4 Blackwell GPUs", "Where the time goes now": fp8 weights with
+ * 128-wide quantisation blocks halve the bytes of the bandwidth-bound work.)
+ * Codes are OCP FP8 E4M3 ("e4m3fn"): sign bit, 4 exponent bits with bias 7,
+ * 3 mantissa bits; exponent field 0 holds subnormals m * 2^-9; the code with
+ * every exponent and mantissa bit set is NaN; there are no infinities.
+ * A weight is code value times the fp32 scale of its 128 x 128 block:
+ *   W[r][c] = dec(q[r][c]) * s[r / 128][c / 128],
+ * formed exactly in double and rounded once to fp32; activations stay bf16. */
+float oracle_fp8_e4m3_to_f32(uint8_t c) {
+  int sign = (c >> 7) & 1, e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m, -9);
+  else v = ldexp((double)(8 + m), e - 10);
+  return (float)(sign ? -v : v);
+}
+
+void oracle_dequant_fp8(int rows, int cols, const uint8_t* q, const float* s, float* w) {
+  const int cb = cols / 128;
+  for (int r = 0; r < rows; ++r)
+    for (int c = 0; c < cols; ++c) {
+      double v = (double)oracle_fp8_e4m3_to_f32(q[(size_t)r * cols + c]) *
+                 (double)s[(size_t)(r / 128) * cb + c / 128];
+      w[(size_t)r * cols + c] = (float)v;
+    }
+}
+
+/* One expert on one token row with fp32 weights (the dequantised fp8 ones):
+ * a_j = sum_h x_h Wg[j][h], b_j = sum_h x_h Wu[j][h] (fp32, h ascending),
+ * hb_j = bf16(silu(a_j) * b_j), y_n = sum_j hb_j Wd[n][j] (fp32, j ascending). */
+static void expert_f32w(int H, int I, const uint16_t* x_row, const float* w_gu, const float* w_d,
+                        uint16_t* h_out, float* y) {
+  uint16_t* hb = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)I);
+#pragma omp parallel for schedule(static)
+  for (int j = 0; j < I; ++j) {
+    const float* wg = w_gu + (size_t)j * H;
+    const float* wu = w_gu + (size_t)(I + j) * H;
+    float a = 0.0f, b = 0.0f;
+    for (int h = 0; h < H; ++h) a = a + bf2f(x_row[h]) * wg[h];
+    for (int h = 0; h < H; ++h) b = b + bf2f(x_row[h]) * wu[h];
+    hb[j] = oracle_swiglu(a, b);
+  }
+#pragma omp parallel for schedule(static)
+  for (int n = 0; n < H; ++n) {
+    const float* wd = w_d + (size_t)n * I;
+    float t = 0.0f;
+    for (int j = 0; j < I; ++j) t = t + bf2f(hb[j]) * wd[j];
+    y[n] = t;
+  }
+  if (h_out) memcpy(h_out, hb, sizeof(uint16_t) * (size_t)I);
+  free(hb);
+}
+
+/* One fp8 expert: q_gu [2I][H] codes with s_gu [2I/128][H/128], q_d [H][I] codes
+ * with s_d [H/128][I/128]; dequantise, then the fp32-weight expert above. */
+void oracle_expert_fp8(int H, int I, const uint16_t* x_row, const uint8_t* q_gu,
+                       const float* s_gu, const uint8_t* q_d, const float* s_d, uint16_t* h_out,
+                       float* y) {
+  float* wgu = (float*)malloc(sizeof(float) * (size_t)2 * I * H);
+  float* wd = (float*)malloc(sizeof(float) * (size_t)H * I);
+  oracle_dequant_fp8(2 * I, H, q_gu, s_gu, wgu);
+  oracle_dequant_fp8(H, I, q_d, s_d, wd);
+  expert_f32w(H, I, x_row, wgu, wd, h_out, y);
+  free(wgu);
+  free(wd);
+}
+
 /* ---- experts + gate-weighted combine + shared expert -----------------------
  * Per row m and output n (fp32, one rounding per operation, no contraction):
  *   R = 0, then for k = 0..K-1 in rank order: R = R + g[m][k] * y_{idx[m][k]}[m][n]
@@ -172,14 +240,12 @@ void oracle_expert(int H, int I, const uint16_t* x_row, const uint16_t* w_gu, co
  * The routed part is summed in fp32 and scaled once ("PDL: stacking ...": the
  * small-M combine is an fp32 sum times a scale with a single final cast; the
  * scale is the routed scaling factor, 1 unless the model sets one).  The
- * caller casts acc once.
- * w_gu_tab / w_d_tab are tables of per-expert weight pointers indexed by expert
- * id (shared expert at index E); only the experts used need to be present.
- * Returns 0, or -1 if an index is out of range or a needed weight is missing. */
-int oracle_experts_combine(int H, int E, int K, int I, int S, int M, const uint16_t* x,
-                           const int32_t* idx, const float* gate,
-                           const uint16_t* const* w_gu_tab, const uint16_t* const* w_d_tab,
-                           float scale, float* acc) {
+ * caller casts acc once.  `expert(ctx, e, row, y)` computes expert e on one
+ * token row, returning -1 if its weights are missing. */
+typedef int (*expert_fn)(void* ctx, int e, const uint16_t* x_row, float* y);
+
+static int combine_core(int H, int E, int K, int S, int M, const uint16_t* x, const int32_t* idx,
+                        const float* gate, float scale, expert_fn expert, void* ctx, float* acc) {
   float* y = (float*)malloc(sizeof(float) * (size_t)H);
   float* R = (float*)malloc(sizeof(float) * (size_t)H);
   int rc = 0;
@@ -189,8 +255,7 @@ int oracle_experts_combine(int H, int E, int K, int I, int S, int M, const uint1
     for (int n = 0; n < H; ++n) R[n] = 0.0f;
     for (int k = 0; k < K; ++k) {
       int e = idx[(size_t)m * K + k];
-      if (e < 0 || e >= E || !w_gu_tab[e] || !w_d_tab[e]) { rc = -1; break; }
-      oracle_expert(H, I, xr, w_gu_tab[e], w_d_tab[e], NULL, y);
+      if (e < 0 || e >= E || expert(ctx, e, xr, y) != 0) { rc = -1; break; }
       float g = gate[(size_t)m * K + k];
       for (int n = 0; n < H; ++n) {
         float t = g * y[n];
@@ -199,8 +264,7 @@ int oracle_experts_combine(int H, int E, int K, int I, int S, int M, const uint1
     }
     if (rc) break;
     if (S) {
-      if (!w_gu_tab[E] || !w_d_tab[E]) { rc = -1; break; }
-      oracle_expert(H, I, xr, w_gu_tab[E], w_d_tab[E], NULL, y);
+      if (expert(ctx, E, xr, y) != 0) { rc = -1; break; }
     } else {
       for (int n = 0; n < H; ++n) y[n] = 0.0f;
     }
@@ -212,6 +276,56 @@ int oracle_experts_combine(int H, int E, int K, int I, int S, int M, const uint1
   free(R);
   free(y);
   return rc;
+}
+
+/* bf16 experts: w_gu_tab / w_d_tab are tables of per-expert weight pointers
+ * indexed by expert id (shared expert at index E); only the experts used need
+ * to be present.  Returns 0, or -1 if an index is out of range or a needed
+ * weight is missing. */
+struct bf16_tabs {
+  int H, I;
+  const uint16_t* const* gu;
+  const uint16_t* const* d;
+};
+
+static int bf16_expert(void* ctx, int e, const uint16_t* x_row, float* y) {
+  const struct bf16_tabs* t = (const struct bf16_tabs*)ctx;
+  if (!t->gu[e] || !t->d[e]) return -1;
+  oracle_expert(t->H, t->I, x_row, t->gu[e], t->d[e], NULL, y);
+  return 0;
+}
+
+int oracle_experts_combine(int H, int E, int K, int I, int S, int M, const uint16_t* x,
+                           const int32_t* idx, const float* gate,
+                           const uint16_t* const* w_gu_tab, const uint16_t* const* w_d_tab,
+                           float scale, float* acc) {
+  struct bf16_tabs t = {H, I, w_gu_tab, w_d_tab};
+  return combine_core(H, E, K, S, M, x, idx, gate, scale, bf16_expert, &t, acc);
+}
+
+/* fp8 experts: code and scale tables per expert id, as above. */
+struct fp8_tabs {
+  int H, I;
+  const uint8_t* const* qgu;
+  const float* const* sgu;
+  const uint8_t* const* qd;
+  const float* const* sd;
+};
+
+static int fp8_expert(void* ctx, int e, const uint16_t* x_row, float* y) {
+  const struct fp8_tabs* t = (const struct fp8_tabs*)ctx;
+  if (!t->qgu[e] || !t->sgu[e] || !t->qd[e] || !t->sd[e]) return -1;
+  oracle_expert_fp8(t->H, t->I, x_row, t->qgu[e], t->sgu[e], t->qd[e], t->sd[e], NULL, y);
+  return 0;
+}
+
+int oracle_experts_combine_fp8(int H, int E, int K, int I, int S, int M, const uint16_t* x,
+                               const int32_t* idx, const float* gate,
+                               const uint8_t* const* q_gu_tab, const float* const* s_gu_tab,
+                               const uint8_t* const* q_d_tab, const float* const* s_d_tab,
+                               float scale, float* acc) {
+  struct fp8_tabs t = {H, I, q_gu_tab, s_gu_tab, q_d_tab, s_d_tab};
+  return combine_core(H, E, K, S, M, x, idx, gate, scale, fp8_expert, &t, acc);
 }
 
 /* out = bf16(acc): the single final cast of the combine. */

@@ -8,7 +8,8 @@ import numpy as np
 
 from datagen import workloads as W
 
-from . import experts_combine, lmhead_argmax, residual, rmsnorm, router_topk, cast_bf16
+from . import (cast_bf16, experts_combine, experts_combine_fp8, lmhead_argmax, residual, rmsnorm,
+               router_topk)
 
 
 class ExpertCache:
@@ -20,10 +21,15 @@ class ExpertCache:
         self.d = {}
 
     def get(self, layer, e):
+        """bf16 weights, or (codes, scales) pairs for an fp8 workload."""
         k = (layer, e)
         if k not in self.gu:
-            self.gu[k] = W.expert_gate_up(self.wl, layer, e)
-            self.d[k] = W.expert_down(self.wl, layer, e)
+            if self.wl.fp8:
+                self.gu[k] = W.expert_gate_up_fp8(self.wl, layer, e)
+                self.d[k] = W.expert_down_fp8(self.wl, layer, e)
+            else:
+                self.gu[k] = W.expert_gate_up(self.wl, layer, e)
+                self.d[k] = W.expert_down(self.wl, layer, e)
         return self.gu[k], self.d[k]
 
     def drop_layer(self, layer):
@@ -45,7 +51,8 @@ def layer(wl, x, layer_idx=0, cache=None, w_router=None):
     gu, d = {}, {}
     for e in used:
         gu[e], d[e] = cache.get(layer_idx, e)
-    acc = experts_combine(x, idx, gate, gu, d, wl.E, wl.S, wl.routed_scale)
+    combine = experts_combine_fp8 if wl.fp8 else experts_combine
+    acc = combine(x, idx, gate, gu, d, wl.E, wl.S, wl.routed_scale)
     return dict(idx=idx, gate=gate, logits=logits, acc=acc)
 
 

@@ -22,7 +22,7 @@ from oracle import rmsnorm, router_topk, runner  # noqa: E402
 
 DELTA = 1e-3
 ROWS = {W.C1.name: 8, W.C2.name: 8, W.C3.name: 6, W.C4.name: 6, W.C5.name: 6,
-        W.C6.name: 8, W.C7.name: 8}
+        W.C6.name: 8, W.C7.name: 8, W.C8.name: 8, W.C9.name: 8, W.C10.name: 8}
 
 
 def row_ok_single(wl, xrow, wr):
@@ -43,7 +43,7 @@ def row_ok_chain(wl, xrow, routers, lm):
 
 def main():
     out = {"delta": DELTA, "workloads": {}}
-    for wl in W.ALL + W.FRONT:
+    for wl in W.ALL + W.FRONT + W.FP8:
         n = ROWS[wl.name]
         attempts = []
         if wl.n_layers == 1:

@@ -56,3 +56,47 @@ def test_shard_slices_are_quarters_of_the_full_expert():
     assert np.array_equal(sh[:192], full[:192])
     assert np.array_equal(sh[192:], full[768:768 + 192])
     assert np.array_equal(W.expert_down(W.C4, 0, 5), W.expert_down(W.C3, 0, 5)[:, :192])
+
+
+def _torch_e4m3(v32):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(v32, np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_fp8_codes_round_like_the_library():
+    """dg_e4m3_code(s, mul) is the round-to-nearest-even e4m3 code of s * mul / 65536,
+    saturated at 448: checked against torch's float32 -> float8_e4m3fn cast (exact
+    float32 inputs only, below torch's NaN threshold of 480)."""
+    k = datagen.key(5, 2, 0, datagen.TENSOR_GATE_UP_FP8, 1)
+    s = np.array([datagen.ih12(k, n) for n in range(4000)], dtype=np.int64)
+    for mul in (1, 100, 255):
+        v = s * mul
+        ok = np.abs(v) < (1 << 24)                 # exact in float32
+        v32 = (v[ok].astype(np.float64) / 65536.0).astype(np.float32)
+        keep = np.abs(v32) < 480
+        mine = np.array([datagen.e4m3_code(int(a), mul) for a in s[ok][keep]], np.uint8)
+        assert np.array_equal(mine, _torch_e4m3(v32[keep]))
+    # midpoints round to the even code; zero keeps its sign; large values saturate
+    mids = [(69632, 1), (-69632, 1), (65536 * 9 // 16 * 16 + 65536 // 32, 1), (1, 1)]
+    for si, mul in mids:
+        v32 = np.float32(si * mul / 65536.0)
+        assert datagen.e4m3_code(si, mul) == int(_torch_e4m3(np.array([v32]))[0])
+    assert datagen.e4m3_code(0, 100) == 0
+    assert datagen.e4m3_code(480 * 65536, 1) == 0x7E
+    assert datagen.e4m3_code(-10 ** 9, 1) == 0xFE
+    assert datagen.e4m3_code(464 * 65536, 1) == 0x7E     # midpoint 448 / 480 goes to even 448
+
+
+def test_fp8_slices_distribution_and_scales():
+    k = datagen.key(7, 2, 0, datagen.TENSOR_DOWN_FP8, 3)
+    full = datagen.fill_host_fp8(k, 64, 512)
+    assert np.array_equal(datagen.fill_host_fp8(k, 8, 128, row0=5, col0=256, ld_full=512),
+                          full[5:13, 256:384])
+    import torch
+    v = torch.from_numpy(full).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    assert not np.isnan(v).any()
+    assert abs(v.std() / datagen.FP8_MUL - 1.0) < 0.03
+    q, sc = W.expert_gate_up_fp8(W.C8, 0, 2)
+    assert q.shape == (256, 256) and sc.shape == (2, 2)
+    assert np.all(np.abs(sc / (0.02 / datagen.FP8_MUL) - 1.0) < 0.2)

@@ -569,3 +569,95 @@ def test_byte_counts_match_the_numbers_the_pages_print():
     # full M=1 layer call: router + 8 experts + shared expert
     b1, _ = oracle.unique_weight_bytes(wl.H, wl.E, wl.K, wl.I, 1, idx, include_router=True)
     assert b1 == 108_789_760
+
+
+# ---------------------------------------------------------------- fp8 block-128 experts
+
+def _f8(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn)
+
+
+def test_fp8_decode_matches_library():
+    c = np.arange(256, dtype=np.uint8)
+    mine = oracle.fp8_decode(c)
+    ref = _f8(c).float().numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+    assert np.array_equal(np.signbit(mine[ok]), np.signbit(ref[ok]))   # -0 stays -0
+
+
+def _finite_codes(rng, shape):
+    q = rng.integers(0, 256, size=shape).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x3C                      # no NaN codes
+    return q
+
+
+def test_fp8_dequant_block_indexing_and_rounding(rng):
+    rows, cols = 384, 256                             # 3 x 2 blocks: a transposed index fails
+    q = _finite_codes(rng, (rows, cols))
+    dec = _f8(q).double()
+    # unit scales: the codes' values; power-of-two scales: exact scaling per block
+    assert np.array_equal(oracle.dequant_fp8(q, np.ones((3, 2), np.float32)), dec.float().numpy())
+    p2 = np.array([[0.5, 4.0], [2.0 ** -12, 1.0], [8.0, 0.25]], np.float32)
+    big = np.kron(p2, np.ones((128, 128))).astype(np.float64)
+    assert np.array_equal(oracle.dequant_fp8(q, p2), (dec.numpy() * big).astype(np.float32))
+    # arbitrary scales: the exact product rounded once to fp32 (library float64 -> float32)
+    s = (rng.random((3, 2)) * 1e-3 + 1e-4).astype(np.float32)
+    full = torch.from_numpy(np.kron(s.astype(np.float64), np.ones((128, 128))))
+    assert np.array_equal(oracle.dequant_fp8(q, s), (dec * full).float().numpy())
+
+
+def test_fp8_expert_with_unit_scales_is_the_bf16_expert(rng):
+    """Codes are exact in bf16 and every product of a bf16 input and a code value is exact
+    in fp32, so with unit scales the fp8 expert must equal the pinned bf16 expert bit for bit."""
+    H, I = 256, 128
+    x = W.x_rows(W.C8, [0])[0]
+    qgu = _finite_codes(rng, (2 * I, H)) & 0xBF        # exponent field <= 7: |v| < 2
+    qd = _finite_codes(rng, (H, I)) & 0xBF
+    one_gu, one_d = np.ones((2, 2), np.float32), np.ones((2, 1), np.float32)
+    y8, h8 = oracle.expert_fp8(x, qgu, one_gu, qd, one_d)
+    wgu = to_bf16_bits_exact(_f8(qgu).double().numpy())
+    wd = to_bf16_bits_exact(_f8(qd).double().numpy())
+    y, h = oracle.expert(x, wgu, wd)
+    assert np.array_equal(h8, h) and np.array_equal(y8, y)
+
+
+def test_fp8_expert_within_float64_bound_with_block_scales(rng):
+    wl = W.C8
+    x = W.x_rows(wl, [1])[0]
+    (qgu, sgu), (qd, sd) = W.expert_gate_up_fp8(wl, 0, 4), W.expert_down_fp8(wl, 0, 4)
+    y, h = oracle.expert_fp8(x, qgu, sgu, qd, sd)
+    wgu = _f8(qgu).double().numpy() * np.kron(sgu.astype(np.float64), np.ones((128, 128)))
+    wd = _f8(qd).double().numpy() * np.kron(sd.astype(np.float64), np.ones((128, 128)))
+    xf = f32(x).astype(np.float64)
+    a, b = wgu[:wl.I] @ xf, wgu[wl.I:] @ xf
+    h_ref = bf16_bits_torch(a / (1 + np.exp(-a)) * b)
+    assert np.mean(h == h_ref) > 0.97
+    mism = h != h_ref
+    assert np.all(np.abs(f32(h[mism]) - f32(h_ref[mism])) <= np.abs(f32(h_ref[mism])) * 2.0 ** -7)
+    hf = f32(h).astype(np.float64)
+    # the oracle's down weights are the dequantised values rounded once to fp32
+    ref = wd @ hf
+    bound = (gamma(wl.I) + 2 * U32) * (np.abs(wd) @ np.abs(hf))
+    assert np.all(np.abs(y - ref) <= bound)
+    # a block scale applied to the wrong block would be far outside the bound
+    wd_t = _f8(qd).double().numpy() * np.kron(sd.astype(np.float64)[::-1], np.ones((128, 128)))
+    assert np.max(np.abs(y - wd_t @ hf) - bound) > 0
+
+
+def test_fp8_combine_with_unit_scales_is_the_bf16_combine(rng):
+    wl = W.C8
+    x = W.x_rows(wl, [0, 1, 2])
+    idx, gate, _ = oracle.router_topk(x, W.router(wl), wl.K)
+    gu8, d8, gu, d = {}, {}, {}, {}
+    for e in sorted(set(idx.ravel().tolist())) + [wl.E]:
+        qgu = _finite_codes(rng, (2 * wl.I, wl.H)) & 0xBF
+        qd = _finite_codes(rng, (wl.H, wl.I)) & 0xBF
+        gu8[e], d8[e] = (qgu, np.ones((2, 2), np.float32)), (qd, np.ones((2, 1), np.float32))
+        gu[e] = to_bf16_bits_exact(_f8(qgu).double().numpy())
+        d[e] = to_bf16_bits_exact(_f8(qd).double().numpy())
+    for scale in (1.0, 2.5):
+        a8 = oracle.experts_combine_fp8(x, idx, gate, gu8, d8, wl.E, 1, scale)
+        a = oracle.experts_combine(x, idx, gate, gu, d, wl.E, 1, scale)
+        assert np.array_equal(a8, a)
