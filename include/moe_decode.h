@@ -50,7 +50,12 @@ extern "C" {
  * routed_scale: the routed scaling factor s of the combine,
  *   acc = y_shared + s * sum_k g_k y_k  (the routed part summed in fp32, scaled once:
  *   [LING] "PDL: stacking ...", small-M combine as an fp32 sum times a scale);
- *   must be finite; 0 (a zero-initialised struct) means 1. */
+ *   must be finite; 0 (a zero-initialised struct) means 1.
+ * expert_format: how every expert weight of the call is stored (MOE_EXPERT_BF16,
+ *   or MOE_EXPERT_FP8_B128: fp8 e4m3 codes with one fp32 scale per 128 x 128
+ *   block, the block quantisation of [LING] "Where the time goes now"; it needs
+ *   H and I to be multiples of 128, so a TP4 shard of I = 768 is not
+ *   representable, as that section notes).  The router is bf16 either way. */
 typedef struct {
   int32_t hidden;
   int32_t n_experts;
@@ -58,12 +63,20 @@ typedef struct {
   int32_t inter;
   int32_t n_shared;
   float routed_scale;
+  int32_t expert_format;
 } moe_dims;
+
+enum { MOE_EXPERT_BF16 = 0, MOE_EXPERT_FP8_B128 = 1 };
 
 /* One layer's weights (device pointers, bf16 bits unless stated):
  *   w_router    [E][H]
  *   w_gate_up   [E+S][2I][H]  rows [0, I) are the gate projection, rows [I, 2I) the up projection
  *   w_down      [E+S][H][I]
+ *               (MOE_EXPERT_FP8_B128: one byte per weight, an OCP fp8 e4m3 code;
+ *               the weight is its value times the scale of its 128 x 128 block)
+ *   s_gate_up   MOE_EXPERT_FP8_B128 only: [E+S][2I/128][H/128] fp32 block scales of
+ *               w_gate_up, 4-byte aligned (NULL for bf16)
+ *   s_down      MOE_EXPERT_FP8_B128 only: [E+S][H/128][I/128] fp32 block scales of w_down
  *   router_bias [E] fp32, optional (NULL: none): a per-expert selection bias.  Experts
  *               are chosen by fp32(logit + bias); the gates still come from the
  *               unbiased logits.  [LING] "PDL: stacking ...", figure on the router
@@ -76,10 +89,12 @@ typedef struct {
  * The shared expert, if any, is stored at expert index E. */
 typedef struct {
   const uint16_t* w_router;
-  const uint16_t* w_gate_up;
-  const uint16_t* w_down;
+  const void* w_gate_up;
+  const void* w_down;
   const float* router_bias;
   const uint16_t* norm_gain;
+  const float* s_gate_up;
+  const float* s_down;
 } moe_layer_weights;
 
 enum moe_status {
@@ -131,7 +146,8 @@ int moe_router_topk(const moe_dims* dims, int32_t M, const uint16_t* x, const ui
                     void* ws, size_t ws_bytes, void* stream);
 
 /* Experts for given routing: for each row m and selected expert e = topk_idx[m][k]
- * (and the shared expert), a = W_gate[e] x_m, b = W_up[e] x_m (fp32),
+ * (and the shared expert), a = W_gate[e] x_m, b = W_up[e] x_m (fp32; fp8 weights are
+ * decoded and scaled per block, activations stay bf16),
  * h = bf16(silu(a) * b), y = W_down[e] h (fp32); then
  *   acc[m] = y_shared + sum_k topk_gate[m][k] * y_{topk_idx[m][k]}   (fp32)
  * (times dims->routed_scale on the routed sum, see moe_dims)

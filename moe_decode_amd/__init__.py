@@ -41,6 +41,8 @@ MOE_CHAIN_RESIDUAL = 0
 MOE_CHAIN_LAYER_ONLY = 1
 MOE_CHAIN_PRENORM_RESIDUAL = 2
 MOE_CHAIN_PRENORM_LAYER_ONLY = 3
+MOE_EXPERT_BF16 = 0
+MOE_EXPERT_FP8_B128 = 1
 
 MOE_MAX_ROWS = 8
 MOE_MAX_LAYERS = 64
@@ -55,13 +57,15 @@ EXPORTED = ("moe_workspace_size", "moe_workspace_init", "moe_router_topk", "moe_
 class moe_dims(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32),
-                ("n_shared", ctypes.c_int32), ("routed_scale", ctypes.c_float)]
+                ("n_shared", ctypes.c_int32), ("routed_scale", ctypes.c_float),
+                ("expert_format", ctypes.c_int32)]
 
 
 class moe_layer_weights(ctypes.Structure):
     _fields_ = [("w_router", ctypes.c_void_p), ("w_gate_up", ctypes.c_void_p),
                 ("w_down", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
-                ("norm_gain", ctypes.c_void_p)]
+                ("norm_gain", ctypes.c_void_p), ("s_gate_up", ctypes.c_void_p),
+                ("s_down", ctypes.c_void_p)]
 
 
 _P = ctypes.c_void_p
@@ -129,14 +133,16 @@ def _nbytes(ws, ws_bytes):
     return ws.numel() * ws.element_size()
 
 
-def dims(hidden, n_experts, top_k, inter, n_shared, routed_scale=0.0):
+def dims(hidden, n_experts, top_k, inter, n_shared, routed_scale=0.0,
+         expert_format=MOE_EXPERT_BF16):
     """routed_scale 0 means 1 (the plain combine)."""
-    return moe_dims(hidden, n_experts, top_k, inter, n_shared, routed_scale)
+    return moe_dims(hidden, n_experts, top_k, inter, n_shared, routed_scale, expert_format)
 
 
-def layer_weights(w_router, w_gate_up, w_down, router_bias=None, norm_gain=None):
+def layer_weights(w_router, w_gate_up, w_down, router_bias=None, norm_gain=None,
+                  s_gate_up=None, s_down=None):
     return moe_layer_weights(_ptr(w_router), _ptr(w_gate_up), _ptr(w_down), _ptr(router_bias),
-                             _ptr(norm_gain))
+                             _ptr(norm_gain), _ptr(s_gate_up), _ptr(s_down))
 
 
 # ---- the C entry points, same names -------------------------------------------

@@ -91,12 +91,15 @@ template <int NL>
 using LayerKern = void (*)(ParamsT<NL>);
 
 template <int NL>
-LayerKern<NL> pick_layer_kernel(int cplh, int cpli) {
-#define MOE_K(a, b)              \
-  if (cplh == a && cpli == b)   \
-    return moe_layer_kernel<a, b, (10 / b < 1 ? 1 : (10 / b > 4 ? 4 : 10 / b)), NL>;
-  MOE_K(1, 1) MOE_K(10, 12) MOE_K(10, 3) MOE_K(10, 1) MOE_K(10, 4) MOE_K(8, 12) MOE_K(8, 3)
-  MOE_K(4, 4) MOE_K(2, 2)
+LayerKern<NL> pick_layer_kernel(int cplh, int cpli, bool w8) {
+#define MOE_K(a, b, f)                      \
+  if (cplh == a && cpli == b && w8 == f)   \
+    return moe_layer_kernel<a, b, (10 / b < 1 ? 1 : (10 / b > 4 ? 4 : 10 / b)), NL, f>;
+  MOE_K(1, 1, false) MOE_K(10, 12, false) MOE_K(10, 3, false) MOE_K(10, 1, false)
+  MOE_K(10, 4, false) MOE_K(8, 12, false) MOE_K(8, 3, false) MOE_K(4, 4, false)
+  MOE_K(2, 2, false)
+  // fp8 experts (I a multiple of 128)
+  MOE_K(1, 2, true) MOE_K(10, 12, true) MOE_K(2, 2, true)
 #undef MOE_K
   return nullptr;
 }
@@ -152,10 +155,22 @@ int check_dims(const moe_dims* d) {
   if (!plan_h_rows(d->hidden, &a) || !plan_i_rows(d->inter, &b)) return MOE_E_UNSUPPORTED;
   if (d->hidden > 16384 || d->inter > 16384) return MOE_E_UNSUPPORTED;
   if (!isfinite(d->routed_scale)) return MOE_E_ARG;
+  if (d->expert_format != MOE_EXPERT_BF16 && d->expert_format != MOE_EXPERT_FP8_B128)
+    return MOE_E_ARG;
+  if (d->expert_format == MOE_EXPERT_FP8_B128 && (d->hidden % 128 || d->inter % 128))
+    return MOE_E_UNSUPPORTED;  // block-128 quantisation
   return MOE_OK;
 }
 
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+// fp8 experts need both block-scale tensors; bf16 experts take none.
+int check_expert_scales(const moe_dims& d, const moe_layer_weights& w) {
+  if (d.expert_format != MOE_EXPERT_FP8_B128) return (!w.s_gate_up && !w.s_down) ? MOE_OK : MOE_E_ARG;
+  if (!w.s_gate_up || !w.s_down) return MOE_E_ARG;
+  if (!aligned4(w.s_gate_up) || !aligned4(w.s_down)) return MOE_E_ALIGN;
+  return MOE_OK;
+}
 
 // Workspace regions after the header (all tagged 64-bit words):
 //   lg  [L][M][E]        router logits
@@ -222,7 +237,8 @@ int launch_layer_nl(const moe_dims& d, int M, int L, uint32_t flags,
   RowPlan ph, pi;
   plan_h_rows(d.hidden, &ph);
   plan_i_rows(d.inter, &pi);
-  LayerKern<NL> kern = pick_layer_kernel<NL>(ph.cpl, pi.cpl);
+  LayerKern<NL> kern =
+      pick_layer_kernel<NL>(ph.cpl, pi.cpl, d.expert_format == MOE_EXPERT_FP8_B128);
   if (!kern) return MOE_E_UNSUPPORTED;
   const int G = di.num_cu;
   LdsPlan lp;
@@ -272,6 +288,8 @@ int launch_layer_nl(const moe_dims& d, int M, int L, uint32_t flags,
     p.lw[l].wd = layers[l].w_down;
     p.lw[l].bias = layers[l].router_bias;
     p.lw[l].gain = (flags & F_PRENORM) ? layers[l].norm_gain : nullptr;
+    p.lw[l].sgu = layers[l].s_gate_up;
+    p.lw[l].sd = layers[l].s_down;
   }
   hipLaunchKernelGGL(kern, dim3(G), dim3(MOE_WG), lp.total, st, p);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
@@ -350,7 +368,7 @@ int moe_router_topk(const moe_dims* dims, int32_t M, const uint16_t* x, const ui
     return MOE_E_ALIGN;
   rc = check_ws(dims, M, 1, ws, ws_bytes);
   if (rc) return rc;
-  moe_layer_weights lw = {w_router, nullptr, nullptr, router_bias, nullptr};
+  moe_layer_weights lw = {w_router, nullptr, nullptr, router_bias, nullptr, nullptr, nullptr};
   return launch_layer(*dims, M, 1, F_ROUTER_ONLY, &lw, x, nullptr, nullptr, nullptr, topk_idx,
                       topk_gate, logits, nullptr, ws, (hipStream_t)stream);
 }
@@ -367,12 +385,15 @@ int moe_experts_fused(const moe_dims* dims, int32_t M, const uint16_t* x, const 
   if (!aligned16(x) || !aligned16(w->w_gate_up) || !aligned16(w->w_down) || !aligned16(out))
     return MOE_E_ALIGN;
   if (((uintptr_t)topk_idx & 3u) || ((uintptr_t)topk_gate & 3u)) return MOE_E_ALIGN;
+  rc = check_expert_scales(*dims, *w);
+  if (rc) return rc;
   rc = check_ws(dims, M, 1, ws, ws_bytes);
   if (rc) return rc;
   const size_t osz = (size_t)M * dims->hidden * (out_dtype == MOE_OUT_F32 ? 4 : 2);
   uint32_t flags = F_TOPK_IN | (out_dtype == MOE_OUT_F32 ? F_OUT_F32 : 0u);
   if (overlaps(out, osz, x, (size_t)M * dims->hidden * 2)) flags |= F_ALIAS;
-  moe_layer_weights lw = {nullptr, w->w_gate_up, w->w_down, nullptr, nullptr};
+  moe_layer_weights lw = {nullptr, w->w_gate_up, w->w_down, nullptr, nullptr, w->s_gate_up,
+                          w->s_down};
   return launch_layer(*dims, M, 1, flags, &lw, x, out, topk_idx, topk_gate, nullptr, nullptr,
                       nullptr, nullptr, ws, (hipStream_t)stream);
 }
@@ -400,6 +421,8 @@ int moe_layer_chain(const moe_dims* dims, int32_t M, int32_t n_layers,
     if (!aligned16(w.w_router) || !aligned16(w.w_gate_up) || !aligned16(w.w_down))
       return MOE_E_ALIGN;
     if (!aligned4(w.router_bias) || (prenorm && !aligned16(w.norm_gain))) return MOE_E_ALIGN;
+    rc = check_expert_scales(*dims, w);
+    if (rc) return rc;
   }
   if (!aligned16(x_in) || !aligned16(out)) return MOE_E_ALIGN;
   if (topk_idx_all && ((uintptr_t)topk_idx_all & 3u)) return MOE_E_ALIGN;

@@ -36,6 +36,8 @@
 // all the token rows that chose it; no workgroup reads another's weights.
 #pragma once
 
+#include <type_traits>
+
 #include "moe_device.hpp"
 
 namespace moe {
@@ -48,10 +50,12 @@ constexpr int kMaxPK = MOE_MAXM * 16;  // max (routed expert, row) pairs = M * K
 
 struct LayerW {
   const uint16_t* wr;    // [E][H]
-  const uint16_t* wgu;   // [E+S][2I][H]
-  const uint16_t* wd;    // [E+S][H][I]
+  const void* wgu;       // [E+S][2I][H] bf16, or fp8 e4m3 codes
+  const void* wd;        // [E+S][H][I]  bf16, or fp8 e4m3 codes
   const float* bias;     // [E] selection bias, or null
   const uint16_t* gain;  // [H] RMSNorm gain (bf16), or null for unit gain
+  const float* sgu;      // fp8: [E+S][2I/128][H/128] block scales of wgu
+  const float* sd;       // fp8: [E+S][H/128][I/128] block scales of wd
 };
 
 enum : uint32_t {
@@ -202,13 +206,104 @@ __device__ __forceinline__ float dot_rows(const RowRegs<CPLH>& r, const uint4* x
   return group_sum(acc, 32);
 }
 
+// ---- fp8 e4m3 weights with 128 x 128 block scales
+//
+// A row of H codes takes H/16 16-byte chunks; lane li of a half-wave takes
+// chunks li + 32q (q < C8 = ceil(CPLH / 2)), all of them when H is a multiple
+// of 512.  Chunk c lies in column block c / 8, so its partial dot product is
+// multiplied by that block's scale before it joins the lane's sum.  Codes
+// become bf16 pairs in one conversion each (every e4m3 value is a bf16 value)
+// and meet the bf16 activations in v_dot2.
+
+// sum_{k<16} dec(w_k) * x_k for 16 codes and 16 bf16 activations (xa: 0-7, xb: 8-15)
+__device__ __forceinline__ float dot16_fp8(const uint4 w, const uint4 xa, const uint4 xb) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+  const uint32_t xx[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ww[i], 1.0f, false);
+    const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ww[i], 1.0f, true);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(lo, __builtin_bit_cast(bf16x2_t, xx[2 * i]), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(hi, __builtin_bit_cast(bf16x2_t, xx[2 * i + 1]), acc,
+                                          false);
+  }
+  return acc;
+}
+
+template <int CPLH>
+struct Fp8Row {
+  static constexpr int C = (CPLH + 1) / 2;            // chunks per lane
+  static constexpr bool ragged = (CPLH & 1) != 0;     // H/16 < 32 C: some lanes idle
+  __device__ static bool valid(int c, int H) { return !ragged || c < (H >> 4); }
+};
+
+template <int CPLH>
+__device__ __forceinline__ void load_rows8(RowRegs<CPLH>& r, const uint8_t* row0,
+                                           const uint8_t* row1, int H, int lane) {
+  const uint4* src = reinterpret_cast<const uint4*>((lane >> 5) ? row1 : row0);
+  const int li = lane & 31;
+#pragma unroll
+  for (int q = 0; q < Fp8Row<CPLH>::C; ++q) {
+    const int c = li + 32 * q;
+    r.w[q] = Fp8Row<CPLH>::valid(c, H) ? src[c] : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// Block scales of this lane's chunks; srow0 / srow1: the scale rows of the
+// half-waves' weight rows.
+template <int CPLH>
+__device__ __forceinline__ void load_scales8(float (&sc)[Fp8Row<CPLH>::C], const float* srow0,
+                                             const float* srow1, int H, int lane) {
+  const float* srow = (lane >> 5) ? srow1 : srow0;
+  const int li = lane & 31;
+#pragma unroll
+  for (int q = 0; q < Fp8Row<CPLH>::C; ++q) {
+    const int c = li + 32 * q;
+    sc[q] = Fp8Row<CPLH>::valid(c, H) ? srow[c >> 3] : 0.0f;
+  }
+}
+
+template <int CPLH>
+__device__ __forceinline__ float dot_rows8(const RowRegs<CPLH>& r,
+                                           const float (&sc)[Fp8Row<CPLH>::C], const uint4* xs4,
+                                           int H, int m, int lane) {
+  const int li = lane & 31, H8 = H >> 3;
+  float acc = 0.0f;
+#pragma unroll
+  for (int q = 0; q < Fp8Row<CPLH>::C; ++q) {
+    const int c = Fp8Row<CPLH>::valid(li + 32 * q, H) ? li + 32 * q : 0;
+    // convert at the point of use: hoisting the conversions out of the caller's
+    // token-row loop would double the registers the codes occupy
+    uint4 w = r.w[q];
+    asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+    const float part = dot16_fp8(w, xs4[m * H8 + 2 * c], xs4[m * H8 + 2 * c + 1]);
+    acc = fmaf(sc[q], part, acc);
+  }
+  return group_sum(acc, 32);
+}
+
 // P1 item `it`: router rows (it < NRI) or a shared-expert gate/up row pair.
 // The first unit goes to A; a gate/up item's second unit goes to B when
 // `second` is set.
-template <int CPLH, class P>
+template <int CPLH, bool W8, class P>
 __device__ __forceinline__ void p1_load(const P& p, int l, int it, int NRI,
-                                        RowRegs<CPLH>& A, RowRegs<CPLH>& B, int lane,
-                                        bool second) {
+                                        RowRegs<CPLH>& A, RowRegs<CPLH>& B,
+                                        float (&SC)[Fp8Row<CPLH>::C], int lane, bool second) {
+  if constexpr (W8) {
+    if (it >= NRI) {  // shared expert: fp8 rows and their block scales
+      const size_t H = (size_t)p.H, I = (size_t)p.I, HB = H >> 7;
+      const size_t j0 = 2 * (size_t)(it - NRI);
+      const uint8_t* base =
+          static_cast<const uint8_t*>(p.lw[l].wgu) + (size_t)p.E * (2 * I) * H;
+      const float* sb = p.lw[l].sgu + (size_t)p.E * ((2 * I) >> 7) * HB;
+      load_rows8<CPLH>(A, base + j0 * H, base + (I + j0) * H, p.H, lane);
+      if (second) load_rows8<CPLH>(B, base + (j0 + 1) * H, base + (I + j0 + 1) * H, p.H, lane);
+      load_scales8<CPLH>(SC, sb + (j0 >> 7) * HB, sb + ((I + j0) >> 7) * HB, p.H, lane);
+      return;
+    }
+  }
   // Row pointers are chosen first and the loads issued unconditionally after,
   // so the two register buffers never meet in one pointer (which would force
   // them out of registers).
@@ -223,7 +318,7 @@ __device__ __forceinline__ void p1_load(const P& p, int l, int it, int NRI,
     b1 = a1;
   } else {
     const size_t j0 = 2 * (size_t)(it - NRI);
-    const uint16_t* base = p.lw[l].wgu + (size_t)p.E * (2 * I) * H;
+    const uint16_t* base = static_cast<const uint16_t*>(p.lw[l].wgu) + (size_t)p.E * (2 * I) * H;
     a0 = base + j0 * H;
     a1 = base + (I + j0) * H;
     b0 = base + (j0 + 1) * H;
@@ -233,20 +328,25 @@ __device__ __forceinline__ void p1_load(const P& p, int l, int it, int NRI,
   if (!router && second) load_rows<CPLH>(B, b0, b1, lane);
 }
 
-template <int CPLH, class P>
+template <int CPLH, bool W8, class P>
 __device__ __forceinline__ void p1_load_second(const P& p, int l, int it, int NRI,
                                                RowRegs<CPLH>& B, int lane) {
   const size_t H = (size_t)p.H, I = (size_t)p.I;
   const size_t j1 = 2 * (size_t)(it - NRI) + 1;
-  const uint16_t* base = p.lw[l].wgu + (size_t)p.E * (2 * I) * H;
-  load_rows<CPLH>(B, base + j1 * H, base + (I + j1) * H, lane);
+  if constexpr (W8) {
+    const uint8_t* base = static_cast<const uint8_t*>(p.lw[l].wgu) + (size_t)p.E * (2 * I) * H;
+    load_rows8<CPLH>(B, base + j1 * H, base + (I + j1) * H, p.H, lane);
+  } else {
+    const uint16_t* base = static_cast<const uint16_t*>(p.lw[l].wgu) + (size_t)p.E * (2 * I) * H;
+    load_rows<CPLH>(B, base + j1 * H, base + (I + j1) * H, lane);
+  }
 }
 
-template <int CPLH, class P>
+template <int CPLH, bool W8, class P>
 __device__ __forceinline__ void p1_compute(const P& p, int l, int it, int NRI,
                                            const RowRegs<CPLH>& A, const RowRegs<CPLH>& B,
-                                           const uint4* xs4, uint32_t tag, int lane,
-                                           uint32_t dbg) {
+                                           const float (&SC)[Fp8Row<CPLH>::C], const uint4* xs4,
+                                           uint32_t tag, int lane, uint32_t dbg) {
   const int H8 = p.H >> 3;
   if (it < NRI) {
     const int e = 2 * it + (lane >> 5);
@@ -262,8 +362,14 @@ __device__ __forceinline__ void p1_compute(const P& p, int l, int it, int NRI,
     uint64_t* dst = p.hs_buf + (size_t)l * p.M * I2 + jp;
 #pragma unroll 1
     for (int m = 0; m < p.M; ++m) {
-      const float a0 = dot_rows<CPLH>(A, xs4, H8, m, lane);
-      const float a1 = dot_rows<CPLH>(B, xs4, H8, m, lane);
+      float a0, a1;
+      if constexpr (W8) {
+        a0 = dot_rows8<CPLH>(A, SC, xs4, p.H, m, lane);
+        a1 = dot_rows8<CPLH>(B, SC, xs4, p.H, m, lane);
+      } else {
+        a0 = dot_rows<CPLH>(A, xs4, H8, m, lane);
+        a1 = dot_rows<CPLH>(B, xs4, H8, m, lane);
+      }
       const uint32_t word = f_to_bf(swiglu(readlane_f(a0, 0), readlane_f(a0, 32))) |
                             (f_to_bf(swiglu(readlane_f(a1, 0), readlane_f(a1, 32))) << 16);
       if (lane == 0) st_tag(dst + (size_t)m * I2, word, tag);
@@ -286,7 +392,7 @@ __device__ __forceinline__ void load_down(DownRegs<CPLI, DBLK>& r, const P& p, i
   for (int b = 0; b < DBLK; ++b) {
     const int row = n + 8 * b + gl;
     const uint4* src = reinterpret_cast<const uint4*>(
-        p.lw[l].wd + ((size_t)e * p.H + (row < n_end ? row : n)) * p.I);
+        static_cast<const uint16_t*>(p.lw[l].wd) + ((size_t)e * p.H + (row < n_end ? row : n)) * p.I);
 #pragma unroll
     for (int q = 0; q < CPLI; ++q) r.w[b][q] = src[li + 8 * q];
   }
@@ -306,6 +412,55 @@ __device__ __forceinline__ void compute_down(const DownRegs<CPLI, DBLK>& r, int 
       float acc = 0.0f;
 #pragma unroll
       for (int q = 0; q < CPLI; ++q) acc = dot8(r.w[b][q], hv4[t * I8 + li + 8 * q], acc);
+      acc = group_sum(acc, 8);
+      const int row = n + 8 * b + gl;
+      if (li == 0 && row < n_end) emit(t, row, acc);
+    }
+  }
+}
+
+// fp8 down rows: 8 lanes per row, lane li takes chunks li + 8q (q < C = I/128),
+// so chunk q lies in column block q; the row's scale row is (row / 128).
+template <int C, int DB>
+struct DownRegs8 {
+  uint4 w[DB][C];
+  float s[DB][C];
+};
+
+template <int C, int DB, class P>
+__device__ __forceinline__ void load_down8(DownRegs8<C, DB>& r, const P& p, int l, int e, int n,
+                                           int n_end, int lane) {
+  const int gl = lane >> 3, li = lane & 7;
+  const size_t IB = (size_t)(p.I >> 7), HB = (size_t)(p.H >> 7);
+#pragma unroll
+  for (int b = 0; b < DB; ++b) {
+    const int row = n + 8 * b + gl < n_end ? n + 8 * b + gl : n;
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(p.lw[l].wd) +
+                                                      ((size_t)e * p.H + row) * p.I);
+    const float* srow = p.lw[l].sd + ((size_t)e * HB + (size_t)(row >> 7)) * IB;
+#pragma unroll
+    for (int q = 0; q < C; ++q) {
+      r.w[b][q] = src[li + 8 * q];
+      r.s[b][q] = srow[q];
+    }
+  }
+}
+
+template <int C, int DB, typename Emit>
+__device__ __forceinline__ void compute_down8(const DownRegs8<C, DB>& r, int I8, int n, int n_end,
+                                              int nrows, const uint4* hv4, int lane, Emit emit) {
+  const int gl = lane >> 3, li = lane & 7;
+#pragma unroll 1
+  for (int t = 0; t < nrows; ++t) {
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int q = 0; q < C; ++q) {
+        const int c = li + 8 * q;
+        const float part = dot16_fp8(r.w[b][q], hv4[t * I8 + 2 * c], hv4[t * I8 + 2 * c + 1]);
+        acc = fmaf(r.s[b][q], part, acc);
+      }
       acc = group_sum(acc, 8);
       const int row = n + 8 * b + gl;
       if (li == 0 && row < n_end) emit(t, row, acc);
@@ -556,8 +711,13 @@ __device__ __forceinline__ bool slice_piece(int g, int G, int U, int I, int H, i
 
 // ---------------------------------------------------------------- the kernel
 
-template <int CPLH, int CPLI, int DBLK, int NL>
+// W8: expert weights are fp8 e4m3 codes with 128 x 128 block scales (the
+// router stays bf16); C8I fp8 chunks per down-row lane, DB8 down blocks per task.
+template <int CPLH, int CPLI, int DBLK, int NL, bool W8 = false>
 __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
+  constexpr int C8I = CPLI / 2 > 0 ? CPLI / 2 : 1;
+  constexpr int DB8 = 6 / C8I < 1 ? 1 : (6 / C8I > 4 ? 4 : 6 / C8I);
+  constexpr int DB = W8 ? DB8 : DBLK;
   extern __shared__ __align__(16) unsigned char lds[];
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds + p.lds_xs);
   const uint4* xs4 = reinterpret_cast<const uint4*>(xs);
@@ -606,7 +766,8 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     const int NRI = topk_in ? 0 : (E + 1) >> 1;
     const int NSI = (router_only || !S) ? 0 : I2;
     RowRegs<CPLH> A, B;
-    if (gw < NRI + NSI) p1_load<CPLH>(p, l, gw, NRI, A, B, lane, false);
+    float SC[Fp8Row<CPLH>::C];
+    if (gw < NRI + NSI) p1_load<CPLH, W8>(p, l, gw, NRI, A, B, SC, lane, false);
 
     // ---------------- P0: layer input -> LDS
     // the norm's gain does not depend on the input: its load flies during the stage
@@ -680,10 +841,10 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     // ---------------- P1: router rows + shared expert gate/up rows
     for (int it = gw; it < NRI + NSI; it += NW) {
       if (it != gw)
-        p1_load<CPLH>(p, l, it, NRI, A, B, lane, true);
+        p1_load<CPLH, W8>(p, l, it, NRI, A, B, SC, lane, true);
       else if (it >= NRI)  // the prefetched gate/up item still needs its second row
-        p1_load_second<CPLH>(p, l, it, NRI, B, lane);
-      p1_compute<CPLH>(p, l, it, NRI, A, B, xs4, tag, lane, dbg);
+        p1_load_second<CPLH, W8>(p, l, it, NRI, B, lane);
+      p1_compute<CPLH, W8>(p, l, it, NRI, A, B, SC, xs4, tag, lane, dbg);
     }
     MOE_STAMP(2);
 
@@ -758,10 +919,21 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       for (int f = wv; f < F0 + F1; f += MOE_WAVES) {
         const int jp = f + (f < F0 ? jb0 : jb1);
         const int rr = f < F0 ? r0s : r1s;
-        const uint16_t* base = p.lw[l].wgu + (size_t)sm->uexp[rr] * (2 * (size_t)I) * H;
         const size_t j0 = 2 * (size_t)jp;
-        load_rows<CPLH>(A, base + j0 * H, base + ((size_t)I + j0) * H, lane);
-        load_rows<CPLH>(B, base + (j0 + 1) * H, base + ((size_t)I + j0 + 1) * H, lane);
+        if constexpr (W8) {
+          const uint8_t* base = static_cast<const uint8_t*>(p.lw[l].wgu) +
+                                (size_t)sm->uexp[rr] * (2 * (size_t)I) * H;
+          load_rows8<CPLH>(A, base + j0 * H, base + ((size_t)I + j0) * H, H, lane);
+          load_rows8<CPLH>(B, base + (j0 + 1) * H, base + ((size_t)I + j0 + 1) * H, H, lane);
+          const size_t HB = (size_t)(H >> 7);
+          const float* sb = p.lw[l].sgu + (size_t)sm->uexp[rr] * ((2 * (size_t)I) >> 7) * HB;
+          load_scales8<CPLH>(SC, sb + (j0 >> 7) * HB, sb + (((size_t)I + j0) >> 7) * HB, H, lane);
+        } else {
+          const uint16_t* base = static_cast<const uint16_t*>(p.lw[l].wgu) +
+                                 (size_t)sm->uexp[rr] * (2 * (size_t)I) * H;
+          load_rows<CPLH>(A, base + j0 * H, base + ((size_t)I + j0) * H, lane);
+          load_rows<CPLH>(B, base + (j0 + 1) * H, base + ((size_t)I + j0 + 1) * H, lane);
+        }
         const uint32_t mask = sm->umask[rr];
         uint64_t* dst = hr_l + (size_t)sm->pbase[rr] * I2 + jp;
         uint32_t bits = mask;
@@ -770,8 +942,14 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
         while (bits) {
           const int m = __builtin_ctz(bits);
           bits &= bits - 1u;
-          const float a0 = dot_rows<CPLH>(A, xs4, H8, m, lane);
-          const float a1 = dot_rows<CPLH>(B, xs4, H8, m, lane);
+          float a0, a1;
+          if constexpr (W8) {
+            a0 = dot_rows8<CPLH>(A, SC, xs4, H, m, lane);
+            a1 = dot_rows8<CPLH>(B, SC, xs4, H, m, lane);
+          } else {
+            a0 = dot_rows<CPLH>(A, xs4, H8, m, lane);
+            a1 = dot_rows<CPLH>(B, xs4, H8, m, lane);
+          }
           const uint32_t word = f_to_bf(swiglu(readlane_f(a0, 0), readlane_f(a0, 32))) |
                                 (f_to_bf(swiglu(readlane_f(a1, 0), readlane_f(a1, 32))) << 16);
           if (lane == 0) st_tag(dst + (size_t)t * I2, word, tag);
@@ -787,7 +965,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     // inputs of all of them are staged in LDS with one batched wait.
     uint64_t* y_l = p.y_buf + (size_t)l * MK * H;
     {
-      const int BR = 8 * DBLK;
+      const int BR = 8 * DB;
       const int nbs = (S && NR > 0) ? (NR + BR - 1) / BR : 0;
       const int nb0 = has0 ? (pc0.n1 - pc0.n0 + BR - 1) / BR : 0;
       const int nb1 = has1 ? (pc1.n1 - pc1.n0 + BR - 1) / BR : 0;
@@ -804,7 +982,8 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
           e = sm->uexp[pc1.r]; n = pc1.n0 + (f - nbs - nb0) * BR; n_end = pc1.n1; kind = 2;
         }
       };
-      DownRegs<CPLI, DBLK> DA;
+      using DR = std::conditional_t<W8, DownRegs8<C8I, DB8>, DownRegs<CPLI, DBLK>>;
+      DR DA;
       int e, n, n_end, kind;
       // SwiGLU inputs of all this workgroup's down tasks -> LDS: shared | piece 0 | piece 1
       const int ws0 = nbs ? M * I2 : 0;
@@ -821,26 +1000,34 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       MOE_STAMP(6);
       if (sm->abort_flag == 1) break;
       const int pb0 = has0 ? sm->pbase[pc0.r] : 0, pb1 = has1 ? sm->pbase[pc1.r] : 0;
-      auto run = [&](int f, const DownRegs<CPLI, DBLK>& R) __attribute__((always_inline)) {
+      auto down = [&](const DR& R, int nn, int ne, int nrows, const uint4* hv, auto emit)
+                      __attribute__((always_inline)) {
+        if constexpr (W8)
+          compute_down8<C8I, DB8>(R, I8, nn, ne, nrows, hv, lane, emit);
+        else
+          compute_down<CPLI, DBLK>(R, I8, nn, ne, nrows, hv, lane, emit);
+      };
+      auto run = [&](int f, const DR& R) __attribute__((always_inline)) {
         int e2, nn, ne, kd;
         task(f, e2, nn, ne, kd);
         if (kd == 0) {
-          compute_down<CPLI, DBLK>(R, I8, nn, ne, M, hs4, lane, [&](int m, int row, float y) {
+          down(R, nn, ne, M, hs4, [&](int m, int row, float y) {
             ysh[m * p.nr_max + (row - n0)] = y;
           });
         } else {
           const uint4* hv = hs4 + (size_t)(ws0 + (kd == 2 ? ws1 : 0)) / 4;
           const int pb = kd == 1 ? pb0 : pb1;
-          compute_down<CPLI, DBLK>(R, I8, nn, ne, kd == 1 ? nrow0 : nrow1, hv, lane,
-                                   [&](int t, int row, float y) {
-                                     st_tag(y_l + (size_t)(pb + t) * H + row, __float_as_uint(y),
-                                            tag);
-                                   });
+          down(R, nn, ne, kd == 1 ? nrow0 : nrow1, hv, [&](int t, int row, float y) {
+            st_tag(y_l + (size_t)(pb + t) * H + row, __float_as_uint(y), tag);
+          });
         }
       };
       for (int f = wv; f < ntask; f += MOE_WAVES) {
         task(f, e, n, n_end, kind);
-        load_down<CPLI, DBLK>(DA, p, l, e, n, n_end, lane);
+        if constexpr (W8)
+          load_down8<C8I, DB8>(DA, p, l, e, n, n_end, lane);
+        else
+          load_down<CPLI, DBLK>(DA, p, l, e, n, n_end, lane);
         run(f, DA);
       }
       __syncthreads();

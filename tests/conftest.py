@@ -47,6 +47,13 @@ class _DeviceWeights:
             self.layers[key] = D.make_layer(wl, l)
         return self.layers[key]
 
+    def layer_fp8(self, wl, l):
+        from datagen import device as D
+        key = ("fp8", wl.family, wl.I, l)
+        if key not in self.layers:
+            self.layers[key] = D.make_layer_fp8(wl, l)
+        return self.layers[key]
+
     def lmhead(self, wl):
         from datagen import device as D
         if self.lm is None:

@@ -145,7 +145,7 @@ def test_layer_chain_validation():
 
 def test_router_front_validation():
     """Selection bias, norm gain and routed scale are checked on the host too."""
-    assert ctypes.sizeof(md.moe_dims) == 24 and ctypes.sizeof(md.moe_layer_weights) == 40
+    assert ctypes.sizeof(md.moe_dims) == 28 and ctypes.sizeof(md.moe_layer_weights) == 56
     big = 1 << 30
     for bad in (float("nan"), float("inf"), -float("inf")):
         d = md.dims(**LING, routed_scale=bad)
@@ -167,6 +167,33 @@ def test_router_front_validation():
              stream=0) == md.MOE_E_ALIGN
     assert c(d, 1, [md.layer_weights(A, A, A, None, A + 2)], A, A, 1, PL, None, A, big,
              stream=0) == md.MOE_E_ALIGN
+
+
+def test_fp8_expert_validation():
+    """fp8 block-128 experts: format code, the block-128 shape rule, and the scale tensors."""
+    big = 1 << 30
+    F8 = md.MOE_EXPERT_FP8_B128
+    assert md.moe_workspace_size(md.dims(**LING, expert_format=7), 1, 1)[0] == md.MOE_E_ARG
+    assert md.moe_workspace_size(md.dims(**LING, expert_format=F8), 1, 1)[0] == md.MOE_OK
+    # I = 192 (a TP4 shard of 768) is not a whole number of 128-blocks
+    tp4 = dict(LING, inter=192)
+    assert md.moe_workspace_size(md.dims(**tp4, expert_format=F8), 1, 1)[0] == md.MOE_E_UNSUPPORTED
+    assert md.moe_workspace_size(md.dims(**tp4), 1, 1)[0] == md.MOE_OK
+    d8, d16 = md.dims(**LING, expert_format=F8), md.dims(**LING)
+    f, c = md.moe_experts_fused, md.moe_layer_chain
+    LO = md.MOE_CHAIN_LAYER_ONLY
+    no_scales = md.layer_weights(A, A, A)
+    one_scale = md.layer_weights(A, A, A, s_gate_up=A)
+    bad_scale = md.layer_weights(A, A, A, s_gate_up=A, s_down=A + 2)
+    with_scales = md.layer_weights(A, A, A, s_gate_up=A, s_down=A)
+    assert f(d8, 1, A, A, A, no_scales, A, 0, A, big, stream=0) == md.MOE_E_ARG
+    assert f(d8, 1, A, A, A, one_scale, A, 0, A, big, stream=0) == md.MOE_E_ARG
+    assert f(d8, 1, A, A, A, bad_scale, A, 0, A, big, stream=0) == md.MOE_E_ALIGN
+    assert f(d16, 1, A, A, A, with_scales, A, 0, A, big, stream=0) == md.MOE_E_ARG
+    assert c(d8, 1, [no_scales], A, A, 0, LO, None, A, big, stream=0) == md.MOE_E_ARG
+    assert c(d8, 1, [with_scales, bad_scale], A, A, 0, md.MOE_CHAIN_RESIDUAL, None, A, big,
+             stream=0) == md.MOE_E_ALIGN
+    assert c(d16, 1, [with_scales], A, A, 0, LO, None, A, big, stream=0) == md.MOE_E_ARG
 
 
 def test_lmhead_validation():
