@@ -54,7 +54,9 @@ def parse():
 PROFILE_WORKLOADS = {"m1": ("ling_moe_layer_m1", 1, False),
                      "m6": ("ling_moe_layer_m6", 6, False),
                      "tp4": ("ling_tp4_shard_moe_layer_m6", 6, True),
-                     "front": ("ling_moe_layer_front_m6", 6, False)}
+                     "front": ("ling_moe_layer_front_m6", 6, False),
+                     "fp8m1": ("ling_fp8_moe_layer_m1", 1, False),
+                     "fp8m6": ("ling_fp8_moe_layer_m6", 6, False)}
 COPY_BYTES = 256 << 20   # reference copy for the counter scale
 PROFILE_CALLS = 64
 
@@ -97,7 +99,8 @@ def main():
     def time_layer(wl, lws, M, steps, warmup, out_f32=False, mode=None):
         """Cold rotating per-layer timing; returns dict of figures."""
         mode = md.MOE_CHAIN_LAYER_ONLY if mode is None else mode
-        d = md.dims(wl.H, wl.E, wl.K, wl.I, wl.S, wl.routed_scale)
+        d = md.dims(wl.H, wl.E, wl.K, wl.I, wl.S, wl.routed_scale,
+                    md.MOE_EXPERT_FP8_B128 if wl.fp8 else md.MOE_EXPERT_BF16)
         ws = md.new_workspace(d, M, 1)
         n = steps + warmup
         xs = x_pool(wl, n, M)
@@ -184,6 +187,18 @@ def main():
               % (s7["us_per_layer"], s7["effective_gbs"], s7["pct_of_hbm_peak"]),
               file=sys.stderr, flush=True)
         del fronts, lwf
+        # fp8 e4m3 experts with 128 x 128 block scales (bf16 router), 16 distinct layers
+        f8 = [D.make_layer_fp8(W.C9, l) for l in range(N_LAYERS)]
+        lw8 = [md.layer_weights(L.w_router, L.w_gate_up, L.w_down, None, None, L.s_gate_up,
+                                L.s_down) for L in f8]
+        for wl8, M8 in ((W.C9, 1), (W.C10, 6)):
+            r8 = time_layer(wl8, lw8, M8, args.steps, args.warmup)
+            secondary[wl8.name] = r8
+            print("fp8 M=%d: %.2f us/layer, %.0f GB/s (%.1f %%)"
+                  % (M8, r8["us_per_layer"], r8["effective_gbs"], r8["pct_of_hbm_peak"]),
+                  file=sys.stderr, flush=True)
+        del f8, lw8
+        torch.cuda.empty_cache()
         secondary[W.C5.name] = time_chain(md, D, W, np, torch, dev, lw, steps=10, warmup=2)
         c = secondary[W.C5.name]
         print("chain16+lm_head M=6: %.1f us (floor %.1f us, ratio %.2f)"
@@ -301,10 +316,11 @@ def profile_run(key):
     from datagen import workloads as W
 
     name, M, f32 = PROFILE_WORKLOADS[key]
-    wl = {w.name: w for w in (W.C2, W.C3, W.C4, W.C7)}[name]
+    wl = {w.name: w for w in (W.C2, W.C3, W.C4, W.C7, W.C9, W.C10)}[name]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    layers = [D.make_layer(wl, l) for l in range(N_LAYERS)]
+    make = D.make_layer_fp8 if wl.fp8 else D.make_layer
+    layers = [make(wl, l) for l in range(N_LAYERS)]
     keep = []
     lws = []
     for l, L in enumerate(layers):
@@ -312,9 +328,11 @@ def profile_run(key):
         b = None if b is None else D.to_device(b)
         g = None if g is None else D.to_device(g)
         keep.append((b, g))
-        lws.append(md.layer_weights(L.w_router, L.w_gate_up, L.w_down, b, g))
+        lws.append(md.layer_weights(L.w_router, L.w_gate_up, L.w_down, b, g, L.s_gate_up,
+                                    L.s_down))
     mode = md.MOE_CHAIN_PRENORM_LAYER_ONLY if wl.prenorm else md.MOE_CHAIN_LAYER_ONLY
-    d = md.dims(wl.H, wl.E, wl.K, wl.I, wl.S, wl.routed_scale)
+    d = md.dims(wl.H, wl.E, wl.K, wl.I, wl.S, wl.routed_scale,
+                md.MOE_EXPERT_FP8_B128 if wl.fp8 else md.MOE_EXPERT_BF16)
     ws = md.new_workspace(d, M, 1)
     xs = torch.stack([D.to_device(W.x_rows(wl, [s * M + m for m in range(M)]))
                       for s in range(PROFILE_CALLS)])
