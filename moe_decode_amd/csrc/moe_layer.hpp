@@ -42,6 +42,11 @@
 
 namespace moe {
 
+// Pause between polling rounds of a tagged stage (units of 64 clocks).
+#ifndef MOE_POLL_SLEEP
+#define MOE_POLL_SLEEP 1
+#endif
+
 #ifndef MOE_MAX_LAYERS
 #define MOE_MAX_LAYERS 64
 #endif
@@ -158,7 +163,7 @@ __device__ __forceinline__ bool stage_tagged(int n, uint32_t* dst32, uint32_t ta
         record_status(wt.hdr, -6 /* MOE_E_TIMEOUT */);
         return false;
       }
-      __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_s_sleep(MOE_POLL_SLEEP);
 #pragma unroll
       for (int b = 0; b < B; ++b)
         if ((uint32_t)(v[b] >> 32) != tag) v[b] = ld_tag(addr(base + b * MOE_WG));
@@ -458,7 +463,9 @@ __device__ __forceinline__ void compute_down8(const DownRegs8<C, DB>& r, int I8,
 #pragma unroll
       for (int q = 0; q < C; ++q) {
         const int c = li + 8 * q;
-        const float part = dot16_fp8(r.w[b][q], hv4[t * I8 + 2 * c], hv4[t * I8 + 2 * c + 1]);
+        uint4 w = r.w[b][q];  // converted at the point of use (see dot_rows8)
+        asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+        const float part = dot16_fp8(w, hv4[t * I8 + 2 * c], hv4[t * I8 + 2 * c + 1]);
         acc = fmaf(r.s[b][q], part, acc);
       }
       acc = group_sum(acc, 8);
@@ -916,27 +923,12 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       const int r0s = has0 ? pc0.r : 0, r1s = has1 ? pc1.r : 0;
       const int jb0 = has0 ? pc0.j0 >> 1 : 0, jb1 = has1 ? (pc1.j0 >> 1) - F0 : 0;
       const int H8 = H >> 3;
-      for (int f = wv; f < F0 + F1; f += MOE_WAVES) {
-        const int jp = f + (f < F0 ? jb0 : jb1);
-        const int rr = f < F0 ? r0s : r1s;
-        const size_t j0 = 2 * (size_t)jp;
-        if constexpr (W8) {
-          const uint8_t* base = static_cast<const uint8_t*>(p.lw[l].wgu) +
-                                (size_t)sm->uexp[rr] * (2 * (size_t)I) * H;
-          load_rows8<CPLH>(A, base + j0 * H, base + ((size_t)I + j0) * H, H, lane);
-          load_rows8<CPLH>(B, base + (j0 + 1) * H, base + ((size_t)I + j0 + 1) * H, H, lane);
-          const size_t HB = (size_t)(H >> 7);
-          const float* sb = p.lw[l].sgu + (size_t)sm->uexp[rr] * ((2 * (size_t)I) >> 7) * HB;
-          load_scales8<CPLH>(SC, sb + (j0 >> 7) * HB, sb + (((size_t)I + j0) >> 7) * HB, H, lane);
-        } else {
-          const uint16_t* base = static_cast<const uint16_t*>(p.lw[l].wgu) +
-                                 (size_t)sm->uexp[rr] * (2 * (size_t)I) * H;
-          load_rows<CPLH>(A, base + j0 * H, base + ((size_t)I + j0) * H, lane);
-          load_rows<CPLH>(B, base + (j0 + 1) * H, base + ((size_t)I + j0 + 1) * H, lane);
-        }
-        const uint32_t mask = sm->umask[rr];
+      // one task: SwiGLU of gate/up row pairs (2jp, 2jp + 1) for every row that chose slot rr
+      auto emit_task = [&](const RowRegs<CPLH>& X, const RowRegs<CPLH>& Y,
+                           const float (&S)[Fp8Row<CPLH>::C], int jp, int rr)
+                           __attribute__((always_inline)) {
         uint64_t* dst = hr_l + (size_t)sm->pbase[rr] * I2 + jp;
-        uint32_t bits = mask;
+        uint32_t bits = sm->umask[rr];
         int t = 0;
 #pragma unroll 1
         while (bits) {
@@ -944,16 +936,42 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
           bits &= bits - 1u;
           float a0, a1;
           if constexpr (W8) {
-            a0 = dot_rows8<CPLH>(A, SC, xs4, H, m, lane);
-            a1 = dot_rows8<CPLH>(B, SC, xs4, H, m, lane);
+            a0 = dot_rows8<CPLH>(X, S, xs4, H, m, lane);
+            a1 = dot_rows8<CPLH>(Y, S, xs4, H, m, lane);
           } else {
-            a0 = dot_rows<CPLH>(A, xs4, H8, m, lane);
-            a1 = dot_rows<CPLH>(B, xs4, H8, m, lane);
+            a0 = dot_rows<CPLH>(X, xs4, H8, m, lane);
+            a1 = dot_rows<CPLH>(Y, xs4, H8, m, lane);
           }
           const uint32_t word = f_to_bf(swiglu(readlane_f(a0, 0), readlane_f(a0, 32))) |
                                 (f_to_bf(swiglu(readlane_f(a1, 0), readlane_f(a1, 32))) << 16);
           if (lane == 0) st_tag(dst + (size_t)t * I2, word, tag);
           ++t;
+        }
+      };
+      if constexpr (W8) {
+        const size_t HB = (size_t)(H >> 7);
+        for (int f = wv; f < F0 + F1; f += MOE_WAVES) {
+          const int jp = f + (f < F0 ? jb0 : jb1);
+          const int rr = f < F0 ? r0s : r1s;
+          const size_t j0 = 2 * (size_t)jp;
+          const uint8_t* base = static_cast<const uint8_t*>(p.lw[l].wgu) +
+                                (size_t)sm->uexp[rr] * (2 * (size_t)I) * H;
+          load_rows8<CPLH>(A, base + j0 * H, base + ((size_t)I + j0) * H, H, lane);
+          load_rows8<CPLH>(B, base + (j0 + 1) * H, base + ((size_t)I + j0 + 1) * H, H, lane);
+          const float* sb = p.lw[l].sgu + (size_t)sm->uexp[rr] * ((2 * (size_t)I) >> 7) * HB;
+          load_scales8<CPLH>(SC, sb + (j0 >> 7) * HB, sb + (((size_t)I + j0) >> 7) * HB, H, lane);
+          emit_task(A, B, SC, jp, rr);
+        }
+      } else {
+        for (int f = wv; f < F0 + F1; f += MOE_WAVES) {
+          const int jp = f + (f < F0 ? jb0 : jb1);
+          const int rr = f < F0 ? r0s : r1s;
+          const size_t j0 = 2 * (size_t)jp;
+          const uint16_t* base = static_cast<const uint16_t*>(p.lw[l].wgu) +
+                                 (size_t)sm->uexp[rr] * (2 * (size_t)I) * H;
+          load_rows<CPLH>(A, base + j0 * H, base + ((size_t)I + j0) * H, lane);
+          load_rows<CPLH>(B, base + (j0 + 1) * H, base + ((size_t)I + j0 + 1) * H, lane);
+          emit_task(A, B, SC, jp, rr);
         }
       }
     }
