@@ -197,6 +197,11 @@ def main():
             print("fp8 M=%d: %.2f us/layer, %.0f GB/s (%.1f %%)"
                   % (M8, r8["us_per_layer"], r8["effective_gbs"], r8["pct_of_hbm_peak"]),
                   file=sys.stderr, flush=True)
+        c8 = time_chain(md, D, W, np, torch, dev, lw8, steps=10, warmup=2, wl=W.C11)
+        secondary[W.C11.name] = c8
+        print("fp8 chain16+lm_head M=6: %.1f us (floor %.1f us, ratio %.2f)"
+              % (c8["us_per_step"], c8["floor_us_at_peak"], c8["ratio_to_floor"]),
+              file=sys.stderr, flush=True)
         del f8, lw8
         torch.cuda.empty_cache()
         secondary[W.C5.name] = time_chain(md, D, W, np, torch, dev, lw, steps=10, warmup=2)
@@ -245,11 +250,12 @@ def main():
     print(json.dumps(rec))
 
 
-def time_chain(md, D, W, np, torch, dev, lw, steps, warmup):
+def time_chain(md, D, W, np, torch, dev, lw, steps, warmup, wl=None):
     """16-layer pre-norm residual chain (one launch) + lm_head argmax (one launch)."""
-    wl = W.C5
+    wl = W.C5 if wl is None else wl
     M = wl.M
-    d = md.dims(wl.H, wl.E, wl.K, wl.I, wl.S)
+    d = md.dims(wl.H, wl.E, wl.K, wl.I, wl.S, wl.routed_scale,
+                md.MOE_EXPERT_FP8_B128 if wl.fp8 else md.MOE_EXPERT_BF16)
     ws = md.new_workspace(d, M, wl.n_layers)
     lm = D.make_lmhead(wl)
     n = steps + warmup

@@ -185,6 +185,7 @@ float oracle_fp8_e4m3_to_f32(uint8_t c) {
 
 void oracle_dequant_fp8(int rows, int cols, const uint8_t* q, const float* s, float* w) {
   const int cb = cols / 128;
+#pragma omp parallel for schedule(static)
   for (int r = 0; r < rows; ++r)
     for (int c = 0; c < cols; ++c) {
       double v = (double)oracle_fp8_e4m3_to_f32(q[(size_t)r * cols + c]) *

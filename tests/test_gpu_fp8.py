@@ -195,3 +195,53 @@ def test_fp8_chain_tiny_teacher_forced(gpu, dw):
         ref_next = oracle.residual(hs[l], r["acc"])
         assert rel_err_normwise(f32(hs[l + 1][rows]), f32(ref_next[rows])) <= 1e-2
     assert exact >= 0.75 * NL * M
+
+
+def test_fp8_chain16_lmhead_full_size(gpu, dw):
+    """The 16-layer Ling chain with fp8 experts at M=6 (pre-norm residual, one launch),
+    then the lm_head argmax: every layer checked against the oracle on the GPU's own
+    input to it, and the tokens equal to the oracle's argmax of the final hidden state."""
+    import torch
+    wl = W.C11
+    M, NL = 6, wl.n_layers
+    x = x_tiefree(wl, M)
+    layers = [_lw(dw.layer_fp8(wl, l)) for l in range(NL)]
+    d = _dims(wl)
+    ws = md.new_workspace(d, M, NL)
+    out = _empty((M, wl.H), torch.int16, gpu)
+    idx = _empty((NL, M, wl.K), torch.int32, gpu)
+    h_all = _empty((NL + 1, M, wl.H), torch.int16, gpu)
+    say("layer_chain fp8 PRENORM_RESIDUAL L=%d M=%d" % (NL, M))
+    md.check(md.moe_layer_chain(d, M, layers, D.to_device(x), out, md.MOE_OUT_BF16,
+                                md.MOE_CHAIN_PRENORM_RESIDUAL, idx, ws, h_all=h_all))
+    md.check(md.moe_last_device_status(ws))
+    hs = h_all.cpu().numpy().view(np.uint16)
+    h = out.cpu().numpy().view(np.uint16)
+    ids = idx.cpu().numpy()
+    assert np.array_equal(hs[0], x) and np.array_equal(hs[NL], h)
+    cache = runner.ExpertCache(wl)
+    exact = 0
+    for l in range(NL):
+        u = oracle.rmsnorm(hs[l])
+        r = runner.layer(wl, u, l, cache)
+        clear = runner.router_margin(r["logits"], wl.K) >= 1e-3
+        for m in range(M):
+            if clear[m]:
+                assert set(ids[l, m]) == set(r["idx"][m]), (l, m)
+                exact += 1
+        rows = np.nonzero(clear)[0]
+        ref_next = oracle.residual(hs[l], r["acc"])
+        assert rel_err_normwise(f32(hs[l + 1][rows]), f32(ref_next[rows])) <= 1e-2, l
+        cache.drop_layer(l)
+    assert exact >= 0.9 * NL * M
+    lm = dw.lmhead(wl)
+    tok = _empty((M,), torch.int32, gpu)
+    say("lmhead_argmax V=%d M=%d on the fp8 chain output" % (wl.V, M))
+    md.check(md.lmhead_argmax(M, wl.H, wl.V, D.to_device(h), lm, tok, None, ws))
+    w_host = D.from_device_bf16(lm)
+    t_ref, _ = oracle.lmhead_argmax(h, w_host)
+    marg = runner.lmhead_margin(h, w_host)
+    got = tok.cpu().numpy()
+    for m in range(M):
+        if marg[m] >= 1e-4:
+            assert got[m] == t_ref[m], (m, got[m], t_ref[m])
