@@ -32,6 +32,8 @@ enum : int {
   HDR_DEADLINE = 129,   // wait budget in 100 MHz ticks (0 = default)
   HDR_LM_DONE = 160,    // lm_head: workgroups finished
   HDR_LM_KEYS = 192,    // lm_head: MOE_MAXM packed (logit, index) keys, u64 each
+  HDR_DONE_GRP = 224,   // end of call: workgroups finished per group of g % 8 (8 words, 32 apart)
+  HDR_DONE_ALL = 480,   // end of call: groups finished
   HDR_WORDS = 1024,     // control words: 4 KiB
   HDR_STAMPS = 1024,    // phase stamps: [256 workgroups][32] u64 after the control words
   STAMP_WG = 256,

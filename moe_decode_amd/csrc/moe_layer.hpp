@@ -1121,11 +1121,22 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
   sbase = 0;
   MOE_STAMP(31);
 #undef MOE_STAMP
+  // Workgroups count themselves in two levels (8 group counters, then one
+  // counter of finished groups) so the atomics of 256 workgroups finishing
+  // together queue on 8 addresses instead of one.
   if (tid == 0) {
-    const bool counted = router_only;  // router-only already counted itself
-    uint32_t old = 0;
-    if (!counted) old = add_u32(p.hdr + HDR_DONE, 1u);
-    if (counted || old == (uint32_t)(G - 1)) {
+    bool last = router_only;  // router-only: the workgroup that ran the top-k
+    if (!router_only) {
+      const int grp = g & 7, in_grp = (G - grp + 7) >> 3;
+      const uint32_t old = add_u32(p.hdr + HDR_DONE_GRP + 32 * grp, 1u);
+      if (old == (uint32_t)(in_grp - 1)) {
+        const int groups = G < 8 ? G : 8;
+        last = add_u32(p.hdr + HDR_DONE_ALL, 1u) == (uint32_t)(groups - 1);
+      }
+    }
+    if (last) {
+      for (int c = 0; c < 8; ++c) st_u32(p.hdr + HDR_DONE_GRP + 32 * c, 0u);
+      st_u32(p.hdr + HDR_DONE_ALL, 0u);
       st_u32(p.hdr + HDR_DONE, 0u);
       st_u32(p.hdr + HDR_XREAD, 0u);
       st_u32(p.hdr + HDR_EPOCH, tag);
