@@ -460,7 +460,7 @@ int lmhead_argmax(int32_t M, int32_t H, int32_t V, const uint16_t* h, const uint
   DevInfo di;
   int rc = device_info(&di);
   if (rc) return rc;
-  const int lds = (int)align_up((size_t)M * H * 2, 16) + (MOE_LM_WG / 64) * MOE_MAXM * 8;
+  const int lds = (int)align_up((size_t)M * H * 2, 16) + MOE_LM_WAVES * MOE_MAXM * 8 + 16;
   if (lds > di.max_lds) return MOE_E_UNSUPPORTED;
   rc = prepare_kernel((const void*)kern, lds, MOE_LM_WG);
   if (rc) return rc;
@@ -473,10 +473,13 @@ int lmhead_argmax(int32_t M, int32_t H, int32_t V, const uint16_t* h, const uint
   p.token = token;
   p.max_logit = max_logit;
   p.hdr = (uint32_t*)ws;
-  long long rows = ((long long)V + 1) / 2;
-  long long waves = rows;  // at least one row pair per wave
-  int G = di.num_cu * 4;
-  if ((long long)G * (MOE_LM_WG / 64) > waves) G = (int)((waves + (MOE_LM_WG / 64) - 1) / (MOE_LM_WG / 64));
+  // two workgroups per CU (each wave keeps two row pairs in flight; the second
+  // workgroup hides the reduction of the first at larger M), fewer for a small
+  // vocabulary: at least one row pair per wave.  No workgroup waits on another
+  // until the last one collects the slots, so they need not be co-resident.
+  const long long pairs = ((long long)V + 1) / 2;
+  int G = 2 * di.num_cu < MOE_LM_MAX_GRID ? 2 * di.num_cu : MOE_LM_MAX_GRID;
+  if ((long long)G * MOE_LM_WAVES > pairs) G = (int)((pairs + MOE_LM_WAVES - 1) / MOE_LM_WAVES);
   if (G < 1) G = 1;
   hipLaunchKernelGGL(kern, dim3(G), dim3(MOE_LM_WG), lds, (hipStream_t)stream, p);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;

@@ -16,7 +16,9 @@
 #define MOE_WG 512                  // threads per workgroup of the fused layer kernel
 #define MOE_WAVES (MOE_WG / 64)
 #define MOE_MAXM 8                  // at most eight token rows
-#define MOE_LM_WG 256               // threads per workgroup of the lm_head kernel
+#define MOE_LM_WG 512               // threads per workgroup of the lm_head kernel
+#define MOE_LM_WAVES (MOE_LM_WG / 64)
+#define MOE_LM_MAX_GRID 1024        // lm_head workgroups, at most (one result slot each)
 
 namespace moe {
 
@@ -30,15 +32,18 @@ enum : int {
   HDR_STATUS = 96,      // sticky device status (moe_status)
   HDR_FLAGS = 128,      // debug flags
   HDR_DEADLINE = 129,   // wait budget in 100 MHz ticks (0 = default)
-  HDR_LM_DONE = 160,    // lm_head: workgroups finished
-  HDR_LM_KEYS = 192,    // lm_head: MOE_MAXM packed (logit, index) keys, u64 each
+  HDR_LM_DONE = 160,    // lm_head: groups of workgroups finished
+  HDR_LM_EPOCH = 192,   // lm_head: calls completed; tag of a call = epoch + 1
   HDR_DONE_GRP = 224,   // end of call: workgroups finished per group of g % 8 (8 words, 32 apart)
   HDR_DONE_ALL = 480,   // end of call: groups finished
+  HDR_LM_DONE_GRP = 512,  // lm_head: workgroups finished per group of g % 8 (8 words, 32 apart)
   HDR_WORDS = 1024,     // control words: 4 KiB
   HDR_STAMPS = 1024,    // phase stamps: [256 workgroups][32] u64 after the control words
   STAMP_WG = 256,
   STAMP_SLOTS = 32,
-  HDR_BYTES = HDR_WORDS * 4 + STAMP_WG * STAMP_SLOTS * 8
+  // lm_head result slots after the stamps: [MOE_LM_MAX_GRID][MOE_MAXM] x 2 tagged words
+  HDR_LM_SLOT_BYTE = HDR_WORDS * 4 + STAMP_WG * STAMP_SLOTS * 8,
+  HDR_BYTES = HDR_LM_SLOT_BYTE + MOE_LM_MAX_GRID * MOE_MAXM * 2 * 8
 };
 
 enum : uint32_t { DBG_NO_ROUTER_PUBLISH = 1u, DBG_STAMPS = 2u };

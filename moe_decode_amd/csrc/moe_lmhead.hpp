@@ -1,13 +1,16 @@
 // bf16 lm_head GEMV with the greedy argmax folded in (gfx950).
 //
-// Every wave streams a contiguous range of vocabulary row pairs (one row per
-// 32-lane half, 16-byte loads, v_dot2_f32_bf16) against the M hidden rows held
-// in LDS and keeps, per token row, its best (logit, lowest index).  The
-// workgroups' bests meet in a 64-bit atomic max on (order-preserving logit key
-// << 32 | ~index), so the largest logit wins and equal logits go to the lowest
-// vocabulary index; the last workgroup to finish writes the tokens and resets
-// the keys for the next call ("bf16 router gate and lm_head", Ling-3.0-flash
-// on 4 Blackwell GPUs; greedy decoding).
+// Two workgroups per CU, 8 waves each.  Every wave streams a contiguous range of
+// vocabulary row pairs (one row per 32-lane half, 16-byte loads,
+// v_dot2_f32_bf16) against the M hidden rows held in LDS, with the next pair's
+// loads in flight while the current pair is reduced, and keeps per token row
+// its best (logit, lowest index).  A workgroup's bests are published as
+// step-tagged words in its own slot of the workspace; the last workgroup to
+// finish (two-level counters, so the finishing workgroups' atomics spread
+// over eight addresses) collects every slot, takes the largest logit with the
+// lowest index, writes the tokens and advances the step
+// ("bf16 router gate and lm_head", Ling-3.0-flash on 4 Blackwell GPUs; greedy
+// decoding).
 #pragma once
 
 #include "moe_device.hpp"
@@ -23,16 +26,23 @@ struct LmParams {
   uint32_t* hdr;
 };
 
+// 64-bit order of (logit, index): larger logit first, then lower index
+__device__ __forceinline__ uint64_t lm_key(float z, int v) {
+  return ((uint64_t)f_key(z) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)v);
+}
+
 template <int CPLH>
-__global__ __launch_bounds__(MOE_LM_WG) void moe_lmhead_kernel(LmParams p) {
+__global__ __launch_bounds__(MOE_LM_WG, 1) void moe_lmhead_kernel(LmParams p) {
   extern __shared__ __align__(16) unsigned char lds[];
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
   const uint4* xs4 = reinterpret_cast<const uint4*>(xs);
   uint64_t* wbest = reinterpret_cast<uint64_t*>(lds + ((p.M * p.H * 2 + 15) & ~15));
+  int* flag = reinterpret_cast<int*>(wbest + MOE_LM_WAVES * MOE_MAXM);
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int nwaves = MOE_LM_WG / 64;
+  const int G = gridDim.x, g = blockIdx.x;
   const int M = p.M, H = p.H, H8 = H >> 3;
+  const uint32_t tag = ld_u32(p.hdr + HDR_LM_EPOCH) + 1u;
   {
     const uint4* src = reinterpret_cast<const uint4*>(p.h);
     uint4* dst = reinterpret_cast<uint4*>(xs);
@@ -41,8 +51,8 @@ __global__ __launch_bounds__(MOE_LM_WG) void moe_lmhead_kernel(LmParams p) {
   __syncthreads();
 
   const long long NRP = ((long long)p.V + 1) >> 1;
-  const long long NW = (long long)gridDim.x * nwaves;
-  const long long gw = (long long)blockIdx.x * nwaves + wv;
+  const long long NW = (long long)G * MOE_LM_WAVES;
+  const long long gw = (long long)g * MOE_LM_WAVES + wv;
   const long long rp0 = gw * NRP / NW, rp1 = (gw + 1) * NRP / NW;
   const int grp = lane >> 5, li = lane & 31;
 
@@ -51,13 +61,15 @@ __global__ __launch_bounds__(MOE_LM_WG) void moe_lmhead_kernel(LmParams p) {
 #pragma unroll
   for (int m = 0; m < MOE_MAXM; ++m) { best[m] = 0.0f; besti[m] = -1; }
 
-  for (long long rp = rp0; rp < rp1; ++rp) {
+  auto load = [&](uint4 (&w)[CPLH], long long rp) __attribute__((always_inline)) {
     const long long v = 2 * rp + grp;
-    const bool valid = v < p.V;
-    const uint4* row = reinterpret_cast<const uint4*>(p.w + (size_t)(valid ? v : 0) * H);
-    uint4 w[CPLH];
+    const uint4* row = reinterpret_cast<const uint4*>(p.w + (size_t)(v < p.V ? v : 0) * H);
 #pragma unroll
     for (int q = 0; q < CPLH; ++q) w[q] = row[li + 32 * q];
+  };
+  auto reduce = [&](const uint4 (&w)[CPLH], long long rp) __attribute__((always_inline)) {
+    const long long v = 2 * rp + grp;
+    const bool valid = v < p.V;
 #pragma unroll
     for (int m = 0; m < MOE_MAXM; ++m) {
       if (m < M) {
@@ -68,42 +80,82 @@ __global__ __launch_bounds__(MOE_LM_WG) void moe_lmhead_kernel(LmParams p) {
         if (valid && (besti[m] < 0 || a > best[m])) { best[m] = a; besti[m] = (int)v; }
       }
     }
+  };
+  // two row pairs in flight per wave: the next pair's loads are issued before
+  // the current pair is reduced
+  uint4 wa[CPLH], wb[CPLH];
+  if (rp0 < rp1) load(wa, rp0);
+  for (long long rp = rp0; rp < rp1; rp += 2) {
+    if (rp + 1 < rp1) load(wb, rp + 1);
+    reduce(wa, rp);
+    if (rp + 1 < rp1) {
+      if (rp + 2 < rp1) load(wa, rp + 2);
+      reduce(wb, rp + 1);
+    }
   }
-  // combine the two row groups of the wave, then the waves of the workgroup
+
+  // the wave's best per token row (both halves), then the workgroup's
 #pragma unroll
   for (int m = 0; m < MOE_MAXM; ++m) {
     if (m < M) {
-      const uint64_t key = besti[m] < 0 ? 0ull
-                                        : (((uint64_t)f_key(best[m]) << 32) |
-                                           (uint64_t)(0xFFFFFFFFu - (uint32_t)besti[m]));
+      const uint64_t key = besti[m] < 0 ? 0ull : lm_key(best[m], besti[m]);
       const uint64_t k0 = readlane_u64(key, 0), k1 = readlane_u64(key, 32);
       if (lane == 0) wbest[wv * MOE_MAXM + m] = k0 > k1 ? k0 : k1;
     }
   }
   __syncthreads();
-  // One thread publishes the workgroup's keys and then counts itself done with
-  // release ordering; the last workgroup's acquire sees every key.
+  uint64_t* slots = reinterpret_cast<uint64_t*>(reinterpret_cast<unsigned char*>(p.hdr) +
+                                                HDR_LM_SLOT_BYTE);
+  if (tid < M) {
+    uint64_t k = 0;
+    for (int w = 0; w < MOE_LM_WAVES; ++w) {
+      const uint64_t c = wbest[w * MOE_MAXM + tid];
+      k = c > k ? c : k;
+    }
+    uint64_t* s = slots + ((size_t)g * MOE_MAXM + tid) * 2;
+    st_tag(s, (uint32_t)(k >> 32), tag);
+    st_tag(s + 1, (uint32_t)k, tag);
+  }
+  __syncthreads();
+  // count this workgroup done: its group of g % 8, then the groups
   if (tid == 0) {
-    uint64_t* keys = reinterpret_cast<uint64_t*>(p.hdr + HDR_LM_KEYS);
-    for (int m = 0; m < M; ++m) {
-      uint64_t k = 0;
-      for (int w = 0; w < nwaves; ++w) {
-        const uint64_t c = wbest[w * MOE_MAXM + m];
-        k = c > k ? c : k;
-      }
-      if (k) __hip_atomic_fetch_max(keys + m, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int grp8 = g & 7, in_grp = (G - grp8 + 7) >> 3;
+    bool last = false;
+    if (add_u32(p.hdr + HDR_LM_DONE_GRP + 32 * grp8, 1u) == (uint32_t)(in_grp - 1))
+      last = add_u32(p.hdr + HDR_LM_DONE, 1u) == (uint32_t)((G < 8 ? G : 8) - 1);
+    *flag = last ? 1 : 0;
+  }
+  __syncthreads();
+  if (*flag == 0) return;
+
+  // last workgroup: every slot carries this call's tag (bounded wait)
+  if (tid < MOE_MAXM) wbest[tid] = 0ull;
+  __syncthreads();
+  const uint32_t budget = ld_u32(p.hdr + HDR_DEADLINE);
+  Waiter wt{p.hdr, now_ticks() + (budget ? budget : kDefaultDeadlineTicks)};
+  for (int s = tid; s < G * M; s += MOE_LM_WG) {
+    const int gg = s / M, m = s - gg * M;
+    const uint64_t* src = slots + ((size_t)gg * MOE_MAXM + m) * 2;
+    uint64_t hi = ld_tag(src), lo = ld_tag(src + 1);
+    while ((uint32_t)(hi >> 32) != tag || (uint32_t)(lo >> 32) != tag) {
+      if (wt.expired()) { record_status(p.hdr, -6 /* MOE_E_TIMEOUT */); break; }
+      __builtin_amdgcn_s_sleep(1);
+      hi = ld_tag(src);
+      lo = ld_tag(src + 1);
     }
-    const uint32_t old = __hip_atomic_fetch_add(p.hdr + HDR_LM_DONE, 1u, __ATOMIC_ACQ_REL,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    if (old == gridDim.x - 1) {
-      for (int m = 0; m < M; ++m) {
-        const uint64_t k = __hip_atomic_load(keys + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        p.token[m] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
-        if (p.max_logit) p.max_logit[m] = key_f((uint32_t)(k >> 32));
-        __hip_atomic_store(keys + m, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      st_u32(p.hdr + HDR_LM_DONE, 0u);
-    }
+    const uint64_t k = ((hi & 0xFFFFFFFFull) << 32) | (lo & 0xFFFFFFFFull);
+    atomicMax(reinterpret_cast<unsigned long long*>(wbest + m), (unsigned long long)k);
+  }
+  __syncthreads();
+  if (tid < M) {
+    const uint64_t k = wbest[tid];
+    p.token[tid] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
+    if (p.max_logit) p.max_logit[tid] = key_f((uint32_t)(k >> 32));
+  }
+  if (tid == 0) {
+    for (int c = 0; c < 8; ++c) st_u32(p.hdr + HDR_LM_DONE_GRP + 32 * c, 0u);
+    st_u32(p.hdr + HDR_LM_DONE, 0u);
+    st_u32(p.hdr + HDR_LM_EPOCH, tag);
   }
 }
 

@@ -65,7 +65,7 @@ def test_workspace_size_layout_and_errors():
     def up(v):
         return (v + 255) // 256 * 256
     M, L, E, H, I, K, S = 6, 16, 512, 2560, 768, 8, 1
-    lg = 4096 + 256 * 32 * 8          # control words + phase-stamp area
+    lg = 4096 + 256 * 32 * 8 + 1024 * 8 * 2 * 8   # control words, phase stamps, lm_head slots
     hs = up(lg + L * M * E * 8)       # logits
     hr = up(hs + L * M * (I // 2) * 8)          # shared SwiGLU pairs
     y = up(hr + L * M * K * (I // 2) * 8)       # routed SwiGLU pairs
