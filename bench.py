@@ -56,7 +56,8 @@ PROFILE_WORKLOADS = {"m1": ("ling_moe_layer_m1", 1, False),
                      "tp4": ("ling_tp4_shard_moe_layer_m6", 6, True),
                      "front": ("ling_moe_layer_front_m6", 6, False),
                      "fp8m1": ("ling_fp8_moe_layer_m1", 1, False),
-                     "fp8m6": ("ling_fp8_moe_layer_m6", 6, False)}
+                     "fp8m6": ("ling_fp8_moe_layer_m6", 6, False),
+                     "lmhead": ("lmhead_v157184_m6", 6, False)}
 COPY_BYTES = 256 << 20   # reference copy for the counter scale
 PROFILE_CALLS = 64
 
@@ -322,6 +323,8 @@ def profile_run(key):
     from datagen import workloads as W
 
     name, M, f32 = PROFILE_WORKLOADS[key]
+    if key == "lmhead":
+        return profile_run_lmhead(name, M)
     wl = {w.name: w for w in (W.C2, W.C3, W.C4, W.C7, W.C9, W.C10)}[name]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -364,6 +367,39 @@ def profile_run(key):
           flush=True)
 
 
+def profile_run_lmhead(name, M):
+    """One reference copy, then PROFILE_CALLS lm_head argmax launches (V = 157184, H = 2560;
+    the 805 MB weight is larger than every cache, so each launch reads it from HBM)."""
+    import torch
+
+    import benchsupport as bs
+    import moe_decode_amd as md
+    from datagen import device as D
+    from datagen import workloads as W
+
+    wl = W.C5
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lm = D.make_lmhead(wl)
+    ws = md.new_workspace(md.dims(wl.H, wl.E, wl.K, wl.I, wl.S), M, 1)
+    hs = torch.stack([D.to_device(W.x_rows(wl, [s * M + m for m in range(M)]))
+                      for s in range(PROFILE_CALLS)])
+    tok = torch.empty((M,), dtype=torch.int32, device=dev)
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    bs.copy(src, dst, 2048, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for i in range(PROFILE_CALLS):
+        md.check(md.lmhead_argmax(M, wl.H, wl.V, hs[i], lm, tok, None, ws))
+    torch.cuda.synchronize()
+    md.check(md.moe_last_device_status(ws))
+    print("profile run %s: 1 copy of %d bytes, %d lm_head launches" % (name, COPY_BYTES,
+                                                                        PROFILE_CALLS))
+    print("algorithmic bytes per launch: %.0f (the V x H bf16 weight, once)"
+          % (wl.V * wl.H * 2), flush=True)
+
+
 def _csv_rows(root, suffix):
     import csv
     import glob
@@ -388,6 +424,7 @@ def ingest_profiles(root):
     traffic = {"kernel_source_sha": kernel_source_sha(), "copy_bytes": COPY_BYTES,
                "workloads": {}}
     for key, (name, M, _) in sorted(PROFILE_WORKLOADS.items()):
+        kname = "moe_lmhead_kernel" if key == "lmhead" else "moe_layer_kernel"
         cmd_kt = ("rocprofv3 --kernel-trace --stats --output-format csv -d %s/kt_%s -o kt "
                   "-- python3 bench.py --profile-run %s" % (root, key, key))
         alg = None
@@ -400,10 +437,10 @@ def ingest_profiles(root):
         st_files, stats = _csv_rows(os.path.join(root, "kt_" + key), "kernel_stats.csv")
         if not kt_files:
             continue
-        lay = [r for r in kt if "moe_layer_kernel" in r.get("Kernel_Name", "")]
+        lay = [r for r in kt if kname in r.get("Kernel_Name", "")]
         durs = np.array([int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in lay],
                         dtype=np.float64) * 1e-3
-        lines = ["# %s: moe_layer_kernel, %d cold single-layer launches" % (name, len(durs)),
+        lines = ["# %s: %s, %d cold launches" % (name, kname, len(durs)),
                  "command: %s" % cmd_kt,
                  "per-launch kernel duration (us, kernel_trace.csv): mean %.2f  median %.2f  "
                  "min %.2f  max %.2f" % (durs.mean(), np.median(durs), durs.min(), durs.max()),
@@ -421,7 +458,7 @@ def ingest_profiles(root):
             ref = [float(r["Counter_Value"]) for r in rows
                    if "bs_copy" in r["Kernel_Name"] and r["Counter_Name"] == ctr]
             vals = [float(r["Counter_Value"]) for r in rows
-                    if "moe_layer_kernel" in r["Kernel_Name"] and r["Counter_Name"] == ctr]
+                    if kname in r["Kernel_Name"] and r["Counter_Name"] == ctr]
             if not ref or not vals:
                 continue
             scale = COPY_BYTES / ref[0]          # bytes per counter unit
@@ -442,8 +479,9 @@ def ingest_profiles(root):
         if alg:
             w["algorithmic_bytes_per_launch"] = alg
             lines.append("")
-            lines.append("algorithmic bytes per launch (router + union + shared expert, each once): "
-                         "%.3f MB" % (alg / 1e6))
+            what = ("the V x H weight, once" if key == "lmhead"
+                    else "router + union + shared expert, each once")
+            lines.append("algorithmic bytes per launch (%s): %.3f MB" % (what, alg / 1e6))
             if "bytes_per_launch" in w:
                 lines.append("measured HBM traffic / algorithmic bytes: %.4f"
                              % (w["bytes_per_launch"] / alg))
@@ -451,7 +489,7 @@ def ingest_profiles(root):
                          % (alg / (durs.mean() * 1e-6) / 1e9,
                             100 * alg / (durs.mean() * 1e-6) / 1e9 / HBM_PEAK_GBS))
         traffic["workloads"][name] = w
-        with open(os.path.join(out_dir, "moe_layer_kernel_%s.txt" % name), "w") as f:
+        with open(os.path.join(out_dir, "%s_%s.txt" % (kname, name)), "w") as f:
             f.write("\n".join(lines) + "\n")
     with open(os.path.join(out_dir, "traffic.json"), "w") as f:
         json.dump(traffic, f, indent=1)

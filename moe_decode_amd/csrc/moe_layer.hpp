@@ -909,19 +909,16 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     const int U = sm->nU;
     MOE_STAMP(4);
 
-    // ---------------- P6: this workgroup's slice of the routed gate/up rows
-    // Task f over the slice's intermediate pairs (wave wv takes f = wv,
-    // wv + WAVES, ...): gate/up rows j = 2jp (unit A) and 2jp + 1 (unit B) are
-    // both requested before either is used.
+    // ---------------- P6: routed gate/up rows
+    // A task is one intermediate pair jp of one routed slot: gate/up rows
+    // j = 2jp (unit A) and 2jp + 1 (unit B), both requested before either is
+    // used.  This workgroup's slice (pieces of at most two slots) still fixes
+    // its down-projection work below.
     uint64_t* hr_l = p.hr_buf + (size_t)l * MK * I2;
     Piece pc0, pc1;
     const bool has0 = slice_piece(g, G, U, I, H, 0, pc0);
     const bool has1 = slice_piece(g, G, U, I, H, 1, pc1);
-    const int F0 = has0 ? (pc0.j1 - pc0.j0) >> 1 : 0;
-    const int F1 = has1 ? (pc1.j1 - pc1.j0) >> 1 : 0;
     {
-      const int r0s = has0 ? pc0.r : 0, r1s = has1 ? pc1.r : 0;
-      const int jb0 = has0 ? pc0.j0 >> 1 : 0, jb1 = has1 ? (pc1.j0 >> 1) - F0 : 0;
       const int H8 = H >> 3;
       // one task: SwiGLU of gate/up row pairs (2jp, 2jp + 1) for every row that chose slot rr
       auto emit_task = [&](const RowRegs<CPLH>& X, const RowRegs<CPLH>& Y,
@@ -948,11 +945,16 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
           ++t;
         }
       };
+      // Tasks t = (slot, pair) over the whole union, dealt round-robin: workgroup
+      // g takes t = g, g + G, ..., its wave wv every WAVES-th of those.  Every
+      // workgroup then streams from every selected expert, which evens out the
+      // per-workgroup finish times far better than contiguous slices.
+      const int T = U * I2;
       if constexpr (W8) {
         const size_t HB = (size_t)(H >> 7);
-        for (int f = wv; f < F0 + F1; f += MOE_WAVES) {
-          const int jp = f + (f < F0 ? jb0 : jb1);
-          const int rr = f < F0 ? r0s : r1s;
+        for (int t = g + G * wv; t < T; t += G * MOE_WAVES) {
+          const int rr = t / I2;
+          const int jp = t - rr * I2;
           const size_t j0 = 2 * (size_t)jp;
           const uint8_t* base = static_cast<const uint8_t*>(p.lw[l].wgu) +
                                 (size_t)sm->uexp[rr] * (2 * (size_t)I) * H;
@@ -963,9 +965,9 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
           emit_task(A, B, SC, jp, rr);
         }
       } else {
-        for (int f = wv; f < F0 + F1; f += MOE_WAVES) {
-          const int jp = f + (f < F0 ? jb0 : jb1);
-          const int rr = f < F0 ? r0s : r1s;
+        for (int t = g + G * wv; t < T; t += G * MOE_WAVES) {
+          const int rr = t / I2;
+          const int jp = t - rr * I2;
           const size_t j0 = 2 * (size_t)jp;
           const uint16_t* base = static_cast<const uint16_t*>(p.lw[l].wgu) +
                                  (size_t)sm->uexp[rr] * (2 * (size_t)I) * H;
