@@ -199,21 +199,26 @@ struct LdsPlan {
   int xs, lg, hs, ysh, ysr, small, gn, total, nr_max;
 };
 
-// LDS of the layer kernel: x [M][H] bf16, logits [M][E] fp32, the SwiGLU rows
-// of the shared expert and of up to two routed slice pieces [3][M][I] bf16, the shared expert's outputs for the owned rows
-// [M][nr_max] fp32, the routed (expert, row) outputs of the owned rows
-// [M*K][nr_max] fp32, the small tables and the norm's gain [H] bf16.
+// LDS of the layer kernel: x [M][H] bf16, aliased by the SwiGLU rows of the
+// shared expert and of up to two routed slice pieces [3][M][I] bf16 once the
+// routed gate/up rows are done; logits [M][E] fp32; the shared expert's
+// outputs for the owned rows [M][nr_max] fp32; the routed (expert, row)
+// outputs of the owned rows [M*K][nr_max] fp32; the small tables and the
+// norm's gain [H] bf16.
 int plan_lds(const moe_dims& d, int M, int G, int max_lds, LdsPlan* lp) {
   const int H = d.hidden, E = d.n_experts, I = d.inter;
   lp->nr_max = 2 * (((H / 2) + G - 1) / G);
   if (lp->nr_max > 64) return MOE_E_UNSUPPORTED;  // residual rows kept in LDS
+  // x (read until the routed gate/up rows are done) and the SwiGLU rows of the
+  // down tasks (shared | first piece | second piece, written after) share a region
   size_t o = 0;
   lp->xs = (int)o;
-  o = align_up(o + (size_t)M * H * 2, 16);
+  lp->hs = (int)o;
+  const size_t xh = (size_t)M * H * 2 > (size_t)3 * M * I * 2 ? (size_t)M * H * 2
+                                                                 : (size_t)3 * M * I * 2;
+  o = align_up(o + xh, 16);
   lp->lg = (int)o;
   o = align_up(o + (size_t)M * E * 4, 16);
-  lp->hs = (int)o;  // SwiGLU rows of the down tasks: shared | first piece | second piece
-  o = align_up(o + (size_t)3 * M * I * 2, 16);
   lp->ysh = (int)o;
   o = align_up(o + (size_t)M * lp->nr_max * 4, 16);
   lp->ysr = (int)o;

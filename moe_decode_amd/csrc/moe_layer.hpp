@@ -1012,6 +1012,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       const uint64_t* hsrc = p.hs_buf + (size_t)l * M * I2;
       const uint64_t* r0src = hr_l + (size_t)(has0 ? sm->pbase[pc0.r] : 0) * I2;
       const uint64_t* r1src = hr_l + (size_t)(has1 ? sm->pbase[pc1.r] : 0) * I2;
+      __syncthreads();  // the SwiGLU rows overwrite x, which the routed gate/up rows read
       if (!stage_tagged<4>(ws0 + ws1 + ws2, hs32, tag, wt, tid, [&](int i) {
             return i < ws0 ? hsrc + i : (i < ws0 + ws1 ? r0src + (i - ws0) : r1src + (i - ws0 - ws1));
           }))
