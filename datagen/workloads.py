@@ -91,12 +91,19 @@ C9 = Workload("ling_fp8_moe_layer_m1", 9, FAMILY_LING, H=2560, E=512, K=8, I=768
               x_seed=909, fp8=True)
 C10 = Workload("ling_fp8_moe_layer_m6", 10, FAMILY_LING, H=2560, E=512, K=8, I=768, S=1, M=6,
                x_seed=1010, fp8=True)
+# A 16-token verify ("Muse Spark Open Ultrafast", "Speculative decoding": the
+# target checks 16 tokens per step), bf16 and fp8 experts.
+C12 = Workload("ling_moe_layer_m16", 12, FAMILY_LING, H=2560, E=512, K=8, I=768, S=1, M=16,
+               x_seed=1313)
+C13 = Workload("ling_fp8_moe_layer_m16", 13, FAMILY_LING, H=2560, E=512, K=8, I=768, S=1, M=16,
+               x_seed=1414, fp8=True)
 C11 = Workload("ling_fp8_chain16_lmhead_m6", 11, FAMILY_LING, H=2560, E=512, K=8, I=768, S=1,
                M=6, x_seed=1111, n_layers=16, V=157184, residual=True, prenorm=True, fp8=True)
 
 ALL = (C1, C2, C3, C4, C5)
 FRONT = (C6, C7)
 FP8 = (C8, C9, C10, C11)
+WIDE = (C12, C13)
 
 
 # ---- host slices ------------------------------------------------------------

@@ -1,7 +1,8 @@
 /* libmoedecode: the small-M mixture-of-experts decoder step on one AMD Instinct
  * MI355X (gfx950).
  *
- * The step, for M = 1..8 token rows (batch-1 decode and speculative verify):
+ * The step, for M = 1..16 token rows (batch-1 decode, speculative verify of up
+ * to 8 draft tokens, and a 16-token tree verify):
  * a bf16 router GEMV, softmax top-k with renormalised gates, a gather of the
  * selected experts' weights, fused gate/up GEMV with SwiGLU, the down GEMV,
  * a gate-weighted combine plus the always-on shared expert, and optionally a
@@ -15,6 +16,8 @@
  *          "Low-Latency-Specific Optimizations" (item 3: at most eight rows,
  *          bitmap placement) and "AMD Low-Latency Kernels" (step-tagged values,
  *          a deadline on every wait, routing-independent weights loaded early).
+ *  [MUSE]  "Muse Spark Open Ultrafast: Pushing beyond 1,000 Tokens per second",
+ *          section "Speculative decoding" (the target verifies 16 tokens per step).
  *
  * Conventions for every call:
  *  - Tensor pointers are DEVICE pointers owned by the caller, row-major and
@@ -116,7 +119,9 @@ enum {
   MOE_CHAIN_PRENORM_LAYER_ONLY = 3
 };
 
-#define MOE_MAX_ROWS 8      /* [LLM] item 3: at most eight rows per tile */
+#define MOE_MAX_ROWS 16     /* [LLM] item 3 keeps at most eight rows per tile; the kernels take
+                               up to sixteen, for a 16-token verify ([MUSE] "Speculative
+                               decoding": one pass of the target over 16 tokens) */
 #define MOE_MAX_LAYERS 64
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16

@@ -44,7 +44,7 @@ MOE_CHAIN_PRENORM_LAYER_ONLY = 3
 MOE_EXPERT_BF16 = 0
 MOE_EXPERT_FP8_B128 = 1
 
-MOE_MAX_ROWS = 8
+MOE_MAX_ROWS = 16
 MOE_MAX_LAYERS = 64
 
 DBG_NO_ROUTER_PUBLISH = 1

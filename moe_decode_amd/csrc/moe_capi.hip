@@ -134,15 +134,19 @@ int prepare_kernel(const void* fn, int lds, int block) {
 }
 
 typedef void (*LmKern)(LmParams);
-LmKern pick_lm_kernel(int cplh) {
+template <int MM>
+LmKern pick_lm_kernel_mm(int cplh) {
   switch (cplh) {
-    case 1: return moe_lmhead_kernel<1>;
-    case 2: return moe_lmhead_kernel<2>;
-    case 4: return moe_lmhead_kernel<4>;
-    case 8: return moe_lmhead_kernel<8>;
-    case 10: return moe_lmhead_kernel<10>;
+    case 1: return moe_lmhead_kernel<1, MM>;
+    case 2: return moe_lmhead_kernel<2, MM>;
+    case 4: return moe_lmhead_kernel<4, MM>;
+    case 8: return moe_lmhead_kernel<8, MM>;
+    case 10: return moe_lmhead_kernel<10, MM>;
     default: return nullptr;
   }
+}
+LmKern pick_lm_kernel(int cplh, int M) {
+  return M <= 8 ? pick_lm_kernel_mm<8>(cplh) : pick_lm_kernel_mm<MOE_MAXM>(cplh);
 }
 
 int check_dims(const moe_dims* d) {
@@ -460,7 +464,7 @@ int lmhead_argmax(int32_t M, int32_t H, int32_t V, const uint16_t* h, const uint
   if (((uintptr_t)token & 3u) || (max_logit && ((uintptr_t)max_logit & 3u))) return MOE_E_ALIGN;
   RowPlan ph;
   if (!plan_h_rows(H, &ph)) return MOE_E_UNSUPPORTED;
-  LmKern kern = pick_lm_kernel(ph.cpl);
+  LmKern kern = pick_lm_kernel(ph.cpl, M);
   if (!kern) return MOE_E_UNSUPPORTED;
   DevInfo di;
   int rc = device_info(&di);

@@ -15,10 +15,10 @@
 
 #define MOE_WG 512                  // threads per workgroup of the fused layer kernel
 #define MOE_WAVES (MOE_WG / 64)
-#define MOE_MAXM 8                  // at most eight token rows
+#define MOE_MAXM 16                 // at most sixteen token rows (a 16-token tree verify)
 #define MOE_LM_WG 512               // threads per workgroup of the lm_head kernel
 #define MOE_LM_WAVES (MOE_LM_WG / 64)
-#define MOE_LM_MAX_GRID 1024        // lm_head workgroups, at most (one result slot each)
+#define MOE_LM_MAX_GRID 512         // lm_head workgroups, at most (one result slot each)
 
 namespace moe {
 

@@ -52,6 +52,7 @@ namespace moe {
 #endif
 
 constexpr int kMaxPK = MOE_MAXM * 16;  // max (routed expert, row) pairs = M * K
+constexpr int kFastRows = 8;           // rows of the threshold-and-rank top-k
 
 struct LayerW {
   const uint16_t* wr;    // [E][H]
@@ -113,9 +114,9 @@ struct Small {
   uint32_t bm[32];           // expert bitmap (E <= 1024)
   int bpre[32];              // population-count prefix per bitmap word
   float rn[MOE_MAXM];        // RMSNorm scale per token row
-  alignas(16) uint32_t gmax[MOE_MAXM * MOE_WAVES];  // top-k: group maxima per row
-  int ccount[MOE_MAXM];                 // top-k: candidates per row
-  alignas(16) uint64_t cand[MOE_MAXM * 64];  // top-k: (key << 32 | ~expert) candidates
+  alignas(16) uint32_t gmax[kFastRows * MOE_WAVES];  // top-k: group maxima per row
+  int ccount[kFastRows];                 // top-k: candidates per row
+  alignas(16) uint64_t cand[kFastRows * 64];  // top-k: (key << 32 | ~expert) candidates
   uint16_t hres[MOE_MAXM * 64];  // residual input h_l of this workgroup's output rows
 };
 
@@ -560,7 +561,7 @@ __device__ __forceinline__ void topk_fast(const float* lgs, float bv, Small* sm,
     mine = lane == m ? gm : mine;
   }
   if (lane < MM) sm->gmax[lane * MOE_WAVES + wv] = mine;
-  if (tid < MOE_MAXM) sm->ccount[tid] = 0;
+  if (tid < kFastRows) sm->ccount[tid] = 0;
   __syncthreads();
   // (b) lane m: tau of row m = its smallest group maximum; every row's
   //     candidates (key >= tau) are packed as (key << 32 | ~expert), so that
@@ -602,7 +603,7 @@ __device__ __forceinline__ void topk_rows(const P& p, const float* lgs, float bv
                                           int lane) {
   const int M = p.M, E = p.E, K = p.K;
   const int nW = (E + 63) >> 6;
-  const bool fast = E <= MOE_WG && K <= nW;
+  const bool fast = M <= kFastRows && E <= MOE_WG && K <= nW;
   if (fast) {
     switch (M) {
       case 1: topk_fast<1>(lgs, bv, sm, E, K, nW, tid, wv, lane); break;
@@ -647,15 +648,18 @@ __device__ __forceinline__ void topk_rows(const P& p, const float* lgs, float bv
 // workgroup barrier publishes the tables.
 template <class P>
 __device__ __forceinline__ void build_union(const P& p, Small* sm, int wv, int lane) {
+  constexpr int NE = kMaxPK / 64;  // entries (row, rank) per lane: i = lane + 64 j
   if (wv == 0) {
-    const int MK = p.M * p.K;  // <= 128: entries (row, rank) i = lane and lane + 64
+    const int MK = p.M * p.K;
     if (lane < 32) sm->bm[lane] = 0u;
-    sm->umask[lane] = 0u;
-    sm->umask[lane + 64] = 0u;
-    const int ea = lane < MK ? sm->tk_idx[lane] : -1;
-    const int eb = lane + 64 < MK ? sm->tk_idx[lane + 64] : -1;
-    if (ea >= 0) atomicOr(&sm->bm[ea >> 5], 1u << (ea & 31));
-    if (eb >= 0) atomicOr(&sm->bm[eb >> 5], 1u << (eb & 31));
+#pragma unroll
+    for (int j = 0; j < NE; ++j) sm->umask[lane + 64 * j] = 0u;
+    int e[NE];
+#pragma unroll
+    for (int j = 0; j < NE; ++j) {
+      e[j] = lane + 64 * j < MK ? sm->tk_idx[lane + 64 * j] : -1;
+      if (e[j] >= 0) atomicOr(&sm->bm[e[j] >> 5], 1u << (e[j] & 31));
+    }
     const uint32_t w = lane < 32 ? sm->bm[lane] : 0u;
     const int c = __builtin_popcount(w);
     const int incl = wave_incl_scan(c);
@@ -663,30 +667,28 @@ __device__ __forceinline__ void build_union(const P& p, Small* sm, int wv, int l
     if (lane < 32) sm->bpre[lane] = incl - c;
     if (lane == 0) sm->nU = U;
     // routed slot of each entry = number of selected experts below it
-    int ra = -1, rb = -1;
-    if (ea >= 0) {
-      ra = sm->bpre[ea >> 5] + __builtin_popcount(sm->bm[ea >> 5] & ((1u << (ea & 31)) - 1u));
-      sm->uexp[ra] = ea;
-      atomicOr(&sm->umask[ra], 1u << (lane / p.K));
+#pragma unroll
+    for (int j = 0; j < NE; ++j) {
+      int r = -1;
+      if (e[j] >= 0) {
+        r = sm->bpre[e[j] >> 5] + __builtin_popcount(sm->bm[e[j] >> 5] & ((1u << (e[j] & 31)) - 1u));
+        sm->uexp[r] = e[j];
+        atomicOr(&sm->umask[r], 1u << ((lane + 64 * j) / p.K));
+      }
+      if (lane + 64 * j < MK) sm->upos[lane + 64 * j] = r;
     }
-    if (eb >= 0) {
-      rb = sm->bpre[eb >> 5] + __builtin_popcount(sm->bm[eb >> 5] & ((1u << (eb & 31)) - 1u));
-      sm->uexp[rb] = eb;
-      atomicOr(&sm->umask[rb], 1u << ((lane + 64) / p.K));
-    }
-    if (lane < MK) sm->upos[lane] = ra;
-    if (lane + 64 < MK) sm->upos[lane + 64] = rb;
     // first (slot, row) pair of every slot
-    const int c0 = lane < U ? __builtin_popcount(sm->umask[lane]) : 0;
-    const int c1 = lane + 64 < U ? __builtin_popcount(sm->umask[lane + 64]) : 0;
-    const int i0 = wave_incl_scan(c0);
-    const int t0 = __builtin_amdgcn_readlane(i0, 63);
-    const int i1 = wave_incl_scan(c1);
-    sm->pbase[lane] = i0 - c0;
-    sm->pbase[lane + 64] = t0 + i1 - c1;
+    int run = 0;
+#pragma unroll
+    for (int j = 0; j < NE; ++j) {
+      const int cj = lane + 64 * j < U ? __builtin_popcount(sm->umask[lane + 64 * j]) : 0;
+      const int ij = wave_incl_scan(cj);
+      sm->pbase[lane + 64 * j] = run + ij - cj;
+      run += __builtin_amdgcn_readlane(ij, 63);
+    }
     if (lane == 63) {
-      sm->nP = t0 + i1;
-      sm->pbase[kMaxPK] = t0 + i1;
+      sm->nP = run;
+      sm->pbase[kMaxPK] = run;
     }
   }
   __syncthreads();

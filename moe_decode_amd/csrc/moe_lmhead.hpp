@@ -31,8 +31,10 @@ __device__ __forceinline__ uint64_t lm_key(float z, int v) {
   return ((uint64_t)f_key(z) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)v);
 }
 
-template <int CPLH>
-__global__ __launch_bounds__(MOE_LM_WG, 1) void moe_lmhead_kernel(LmParams p) {
+// MM: token rows the kernel is built for (8 keeps the per-row bests of the
+// common case small; 16 for the wider verify)
+template <int CPLH, int MM>
+__global__ __launch_bounds__(MOE_LM_WG, 2) void moe_lmhead_kernel(LmParams p) {
   extern __shared__ __align__(16) unsigned char lds[];
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
   const uint4* xs4 = reinterpret_cast<const uint4*>(xs);
@@ -56,10 +58,10 @@ __global__ __launch_bounds__(MOE_LM_WG, 1) void moe_lmhead_kernel(LmParams p) {
   const long long rp0 = gw * NRP / NW, rp1 = (gw + 1) * NRP / NW;
   const int grp = lane >> 5, li = lane & 31;
 
-  float best[MOE_MAXM];
-  int besti[MOE_MAXM];
+  float best[MM];
+  int besti[MM];
 #pragma unroll
-  for (int m = 0; m < MOE_MAXM; ++m) { best[m] = 0.0f; besti[m] = -1; }
+  for (int m = 0; m < MM; ++m) { best[m] = 0.0f; besti[m] = -1; }
 
   auto load = [&](uint4 (&w)[CPLH], long long rp) __attribute__((always_inline)) {
     const long long v = 2 * rp + grp;
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(MOE_LM_WG, 1) void moe_lmhead_kernel(LmParams p) {
     const long long v = 2 * rp + grp;
     const bool valid = v < p.V;
 #pragma unroll
-    for (int m = 0; m < MOE_MAXM; ++m) {
+    for (int m = 0; m < MM; ++m) {
       if (m < M) {
         float a = 0.0f;
 #pragma unroll
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(MOE_LM_WG, 1) void moe_lmhead_kernel(LmParams p) {
 
   // the wave's best per token row (both halves), then the workgroup's
 #pragma unroll
-  for (int m = 0; m < MOE_MAXM; ++m) {
+  for (int m = 0; m < MM; ++m) {
     if (m < M) {
       const uint64_t key = besti[m] < 0 ? 0ull : lm_key(best[m], besti[m]);
       const uint64_t k0 = readlane_u64(key, 0), k1 = readlane_u64(key, 32);

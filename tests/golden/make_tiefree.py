@@ -21,8 +21,9 @@ from datagen import workloads as W  # noqa: E402
 from oracle import rmsnorm, router_topk, runner  # noqa: E402
 
 DELTA = 1e-3
-ROWS = {W.C1.name: 8, W.C2.name: 8, W.C3.name: 6, W.C4.name: 6, W.C5.name: 6,
-        W.C6.name: 8, W.C7.name: 8, W.C8.name: 8, W.C9.name: 8, W.C10.name: 8, W.C11.name: 6}
+ROWS = {W.C1.name: 16, W.C2.name: 8, W.C3.name: 6, W.C4.name: 6, W.C5.name: 6,
+        W.C6.name: 8, W.C7.name: 8, W.C8.name: 8, W.C9.name: 8, W.C10.name: 8, W.C11.name: 6,
+        W.C12.name: 16, W.C13.name: 16}
 
 
 def row_ok_single(wl, xrow, wr):
@@ -48,7 +49,7 @@ def main():
     if only and os.path.exists(path):
         with open(path) as f:
             out = json.load(f)
-    for wl in W.ALL + W.FRONT + W.FP8:
+    for wl in W.ALL + W.FRONT + W.FP8 + W.WIDE:
         if only and wl.name not in only:
             continue
         n = ROWS[wl.name]

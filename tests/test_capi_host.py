@@ -65,7 +65,7 @@ def test_workspace_size_layout_and_errors():
     def up(v):
         return (v + 255) // 256 * 256
     M, L, E, H, I, K, S = 6, 16, 512, 2560, 768, 8, 1
-    lg = 4096 + 256 * 32 * 8 + 1024 * 8 * 2 * 8   # control words, phase stamps, lm_head slots
+    lg = 4096 + 256 * 32 * 8 + 512 * 16 * 2 * 8   # control words, phase stamps, lm_head slots
     hs = up(lg + L * M * E * 8)       # logits
     hr = up(hs + L * M * (I // 2) * 8)          # shared SwiGLU pairs
     y = up(hr + L * M * K * (I // 2) * 8)       # routed SwiGLU pairs
@@ -73,7 +73,8 @@ def test_workspace_size_layout_and_errors():
     assert b6 == up(res + (L + 1) * M * (H // 2) * 8)
     assert md.moe_workspace_size(None, 1, 1)[0] == md.MOE_E_ARG
     assert md.moe_workspace_size(d, 0, 1)[0] == md.MOE_E_ARG
-    assert md.moe_workspace_size(d, 9, 1)[0] == md.MOE_E_UNSUPPORTED
+    assert md.moe_workspace_size(d, 17, 1)[0] == md.MOE_E_UNSUPPORTED
+    assert md.moe_workspace_size(d, 16, 1)[0] == md.MOE_OK
     assert md.moe_workspace_size(d, 1, 65)[0] == md.MOE_E_UNSUPPORTED
 
 
@@ -97,7 +98,7 @@ def test_router_topk_validation():
     d = md.dims(**LING)
     big = 1 << 30
     assert md.moe_router_topk(d, 0, A, A, None, A, A, None, A, big, stream=0) == md.MOE_E_ARG
-    assert md.moe_router_topk(d, 9, A, A, None, A, A, None, A, big, stream=0) == md.MOE_E_UNSUPPORTED
+    assert md.moe_router_topk(d, 17, A, A, None, A, A, None, A, big, stream=0) == md.MOE_E_UNSUPPORTED
     assert md.moe_router_topk(d, 1, None, A, None, A, A, None, A, big, stream=0) == md.MOE_E_ARG
     assert md.moe_router_topk(d, 1, A, None, None, A, A, None, A, big, stream=0) == md.MOE_E_ARG
     assert md.moe_router_topk(d, 1, A, A, None, None, A, None, A, big, stream=0) == md.MOE_E_ARG
@@ -200,7 +201,7 @@ def test_lmhead_validation():
     f = md.lmhead_argmax
     big = 1 << 30
     assert f(0, 2560, 100, A, A, A, None, A, big, stream=0) == md.MOE_E_ARG
-    assert f(9, 2560, 100, A, A, A, None, A, big, stream=0) == md.MOE_E_UNSUPPORTED
+    assert f(17, 2560, 100, A, A, A, None, A, big, stream=0) == md.MOE_E_UNSUPPORTED
     assert f(1, 2560, 0, A, A, A, None, A, big, stream=0) == md.MOE_E_ARG
     assert f(1, 2560, 100, None, A, A, None, A, big, stream=0) == md.MOE_E_ARG
     assert f(1, 2560, 100, A, A, A, None, None, big, stream=0) == md.MOE_E_WORKSPACE
