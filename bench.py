@@ -57,6 +57,7 @@ PROFILE_WORKLOADS = {"m1": ("ling_moe_layer_m1", 1, False),
                      "front": ("ling_moe_layer_front_m6", 6, False),
                      "fp8m1": ("ling_fp8_moe_layer_m1", 1, False),
                      "fp8m6": ("ling_fp8_moe_layer_m6", 6, False),
+                     "m16": ("ling_moe_layer_m16", 16, False),
                      "lmhead": ("lmhead_v157184_m6", 6, False)}
 COPY_BYTES = 256 << 20   # reference copy for the counter scale
 PROFILE_CALLS = 64
@@ -168,6 +169,11 @@ def main():
         print("M=6: %.2f us/layer, %.0f GB/s (%.1f %%), U=%.1f"
               % (s3["us_per_layer"], s3["effective_gbs"], s3["pct_of_hbm_peak"],
                  s3["mean_union_experts"]), file=sys.stderr, flush=True)
+        s12 = time_layer(W.C12, lw, 16, args.steps, args.warmup)
+        secondary[W.C12.name] = s12
+        print("M=16: %.2f us/layer, %.0f GB/s (%.1f %%), U=%.1f"
+              % (s12["us_per_layer"], s12["effective_gbs"], s12["pct_of_hbm_peak"],
+                 s12["mean_union_experts"]), file=sys.stderr, flush=True)
         shards = [D.make_layer(W.C4, l) for l in range(N_LAYERS)]
         lws = [md.layer_weights(L.w_router, L.w_gate_up, L.w_down) for L in shards]
         s4 = time_layer(W.C4, lws, 6, args.steps, args.warmup, out_f32=True)
@@ -192,7 +198,7 @@ def main():
         f8 = [D.make_layer_fp8(W.C9, l) for l in range(N_LAYERS)]
         lw8 = [md.layer_weights(L.w_router, L.w_gate_up, L.w_down, None, None, L.s_gate_up,
                                 L.s_down) for L in f8]
-        for wl8, M8 in ((W.C9, 1), (W.C10, 6)):
+        for wl8, M8 in ((W.C9, 1), (W.C10, 6), (W.C13, 16)):
             r8 = time_layer(wl8, lw8, M8, args.steps, args.warmup)
             secondary[wl8.name] = r8
             print("fp8 M=%d: %.2f us/layer, %.0f GB/s (%.1f %%)"
@@ -325,7 +331,7 @@ def profile_run(key):
     name, M, f32 = PROFILE_WORKLOADS[key]
     if key == "lmhead":
         return profile_run_lmhead(name, M)
-    wl = {w.name: w for w in (W.C2, W.C3, W.C4, W.C7, W.C9, W.C10)}[name]
+    wl = {w.name: w for w in (W.C2, W.C3, W.C4, W.C7, W.C9, W.C10, W.C12)}[name]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     make = D.make_layer_fp8 if wl.fp8 else D.make_layer
