@@ -229,3 +229,16 @@ def test_one_hip_runtime_per_process():
     out = subprocess.run(["python", "-c", code], capture_output=True, text=True, cwd=ROOT,
                          check=True).stdout
     assert out.strip() == "1"
+
+
+def test_plain_c_caller(tmp_path):
+    """The boundary is usable from C alone: tests/capi_smoke.c includes only the
+    header, links only the library, and checks host validation through it."""
+    exe = tmp_path / "capi_smoke"
+    lib_dir = os.path.dirname(md.LIB_PATH)
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror",
+                    "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "capi_smoke.c"), "-L", lib_dir, "-lmoedecode",
+                    "-Wl,-rpath," + lib_dir, "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
+    assert out.strip() == "ok"
