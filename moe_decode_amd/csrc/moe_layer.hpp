@@ -53,6 +53,7 @@ namespace moe {
 
 constexpr int kMaxPK = MOE_MAXM * 16;  // max (routed expert, row) pairs = M * K
 constexpr int kFastRows = 8;           // rows of the threshold-and-rank top-k
+constexpr int kOwnSlots = kMaxPK + 1;  // first per-wave slot table entry (one token row)
 
 struct LayerW {
   const uint16_t* wr;    // [E][H]
@@ -108,9 +109,11 @@ struct Small {
   int tk_idx[kMaxPK];
   float tk_gate[kMaxPK];
   int upos[kMaxPK];          // routed slot of (row, rank), -1 if skipped
-  int uexp[kMaxPK];          // expert id of routed slot r
-  uint32_t umask[kMaxPK];    // rows that chose routed slot r
-  int pbase[kMaxPK + 1];     // first (slot, row) pair of slot r
+  // Slot tables: entries [0, kMaxPK] are the workgroup's; with one token row,
+  // each wave also keeps its own copy of its slots at kOwnSlots + 8 * wave
+  int uexp[kOwnSlots + MOE_WAVES * 8];        // expert id of routed slot r
+  uint32_t umask[kOwnSlots + MOE_WAVES * 8];  // rows that chose routed slot r
+  int pbase[kOwnSlots + MOE_WAVES * 8];       // first (slot, row) pair of slot r
   uint32_t bm[32];           // expert bitmap (E <= 1024)
   int bpre[32];              // population-count prefix per bitmap word
   float rn[MOE_MAXM];        // RMSNorm scale per token row
@@ -907,8 +910,42 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     }
 
     // ---------------- P5: routed slots
-    build_union(p, sm, wv, lane);
-    const int U = sm->nU;
+    // One token row (K <= 8): the routed slots are the ranks (slot r = rank r,
+    // one row each), so there is nothing to merge.  Each wave copies the
+    // selection into its own slot table, which only it reads, so no barrier
+    // stands between the selection and the routed gate/up stream; wave 0 fills
+    // the workgroup's tables, which the down projection and the combine read
+    // after the barrier that opens the down projection.
+    const bool one_row = M == 1 && K <= 8 && !topk_in;
+    int U;
+    if (one_row) {
+      // the lane number, opaque to the compiler: the addresses built from it
+      // are made here, not hoisted out of the layer loop and held in registers
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int e = ln < K ? sm->tk_idx[ln] : -1;  // valid ranks form a prefix
+      U = (int)__builtin_popcountll(__ballot(e >= 0));
+      if (ln < U) {
+        sm->uexp[kOwnSlots + wv * 8 + ln] = e;
+        sm->umask[kOwnSlots + wv * 8 + ln] = 1u;
+        sm->pbase[kOwnSlots + wv * 8 + ln] = ln;
+      }
+      if (wv == 0) {
+        if (ln < U) {
+          sm->uexp[ln] = e;
+          sm->umask[ln] = 1u;
+          sm->pbase[ln] = ln;
+        }
+        if (ln < K) sm->upos[ln] = ln < U ? ln : -1;
+        if (ln == 0) {
+          sm->nU = U;
+          sm->nP = U;
+        }
+      }
+    } else {
+      build_union(p, sm, wv, lane);
+      U = sm->nU;
+    }
     MOE_STAMP(4);
 
     // ---------------- P6: routed gate/up rows
@@ -923,11 +960,13 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     {
       const int H8 = H >> 3;
       // one task: SwiGLU of gate/up row pairs (2jp, 2jp + 1) for every row that chose slot rr
+      // the slot tables: the workgroup's, or with one token row this wave's own
+      const int so = one_row ? kOwnSlots + wv * 8 : 0;
       auto emit_task = [&](const RowRegs<CPLH>& X, const RowRegs<CPLH>& Y,
                            const float (&S)[Fp8Row<CPLH>::C], int jp, int rr)
                            __attribute__((always_inline)) {
-        uint64_t* dst = hr_l + (size_t)sm->pbase[rr] * I2 + jp;
-        uint32_t bits = sm->umask[rr];
+        uint64_t* dst = hr_l + (size_t)sm->pbase[so + rr] * I2 + jp;
+        uint32_t bits = sm->umask[so + rr];
         int t = 0;
 #pragma unroll 1
         while (bits) {
@@ -959,10 +998,10 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
           const int jp = t - rr * I2;
           const size_t j0 = 2 * (size_t)jp;
           const uint8_t* base = static_cast<const uint8_t*>(p.lw[l].wgu) +
-                                (size_t)sm->uexp[rr] * (2 * (size_t)I) * H;
+                                (size_t)sm->uexp[so + rr] * (2 * (size_t)I) * H;
           load_rows8<CPLH>(A, base + j0 * H, base + ((size_t)I + j0) * H, H, lane);
           load_rows8<CPLH>(B, base + (j0 + 1) * H, base + ((size_t)I + j0 + 1) * H, H, lane);
-          const float* sb = p.lw[l].sgu + (size_t)sm->uexp[rr] * ((2 * (size_t)I) >> 7) * HB;
+          const float* sb = p.lw[l].sgu + (size_t)sm->uexp[so + rr] * ((2 * (size_t)I) >> 7) * HB;
           load_scales8<CPLH>(SC, sb + (j0 >> 7) * HB, sb + (((size_t)I + j0) >> 7) * HB, H, lane);
           emit_task(A, B, SC, jp, rr);
         }
@@ -972,7 +1011,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
           const int jp = t - rr * I2;
           const size_t j0 = 2 * (size_t)jp;
           const uint16_t* base = static_cast<const uint16_t*>(p.lw[l].wgu) +
-                                 (size_t)sm->uexp[rr] * (2 * (size_t)I) * H;
+                                 (size_t)sm->uexp[so + rr] * (2 * (size_t)I) * H;
           load_rows<CPLH>(A, base + j0 * H, base + ((size_t)I + j0) * H, lane);
           load_rows<CPLH>(B, base + (j0 + 1) * H, base + ((size_t)I + j0 + 1) * H, lane);
           emit_task(A, B, SC, jp, rr);
@@ -987,6 +1026,10 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     // inputs of all of them are staged in LDS with one batched wait.
     uint64_t* y_l = p.y_buf + (size_t)l * MK * H;
     {
+      // the SwiGLU rows staged below overwrite x, which the routed gate/up rows
+      // read; and the slot tables read below may come from wave 0 alone (one
+      // token row)
+      __syncthreads();
       const int BR = 8 * DB;
       const int nbs = (S && NR > 0) ? (NR + BR - 1) / BR : 0;
       const int nb0 = has0 ? (pc0.n1 - pc0.n0 + BR - 1) / BR : 0;
@@ -1014,7 +1057,6 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       const uint64_t* hsrc = p.hs_buf + (size_t)l * M * I2;
       const uint64_t* r0src = hr_l + (size_t)(has0 ? sm->pbase[pc0.r] : 0) * I2;
       const uint64_t* r1src = hr_l + (size_t)(has1 ? sm->pbase[pc1.r] : 0) * I2;
-      __syncthreads();  // the SwiGLU rows overwrite x, which the routed gate/up rows read
       if (!stage_tagged<4>(ws0 + ws1 + ws2, hs32, tag, wt, tid, [&](int i) {
             return i < ws0 ? hsrc + i : (i < ws0 + ws1 ? r0src + (i - ws0) : r1src + (i - ws0 - ws1));
           }))

@@ -137,6 +137,39 @@ def test_router_bias_planted_ties_exact(gpu, E, K, M):
     assert not np.array_equal(np.sort(ri, 1), np.sort(r0, 1))
 
 
+@pytest.mark.parametrize("E,K", [(16, 2), (200, 5), (512, 8)])
+def test_layer_one_row_planted_ties_exact(gpu, E, K):
+    """One token row through the fused layer, where every wave selects the row
+    on its own: with planted ties and a bias the selection (and its order) is
+    exactly the oracle's; zero experts make the layer's output exactly zero."""
+    import torch
+    rng = np.random.default_rng(3000 + E)
+    H, I = 256, 64
+    lgt, b = _planted(rng, 1, E)
+    x = np.zeros((1, H))
+    w = np.zeros((E, H))
+    x[0, 0] = 1.0
+    w[:, 0] = lgt[0]
+    xb = oracle.f32_to_bf16(x.astype(np.float32)).reshape(1, H)
+    wb = oracle.f32_to_bf16(w.astype(np.float32)).reshape(E, H)
+    d = md.dims(H, E, K, I, 1)
+    ws = md.new_workspace(d, 1, 1)
+    # every expert weight tensor holds E routed + S shared experts ([E+S][2I][H], [E+S][H][I])
+    gu = torch.zeros((E + 1, 2 * I, H), dtype=torch.int16, device=gpu)
+    dn = torch.zeros((E + 1, H, I), dtype=torch.int16, device=gpu)
+    assert gu.shape[0] == E + d.n_shared and dn.shape[0] == E + d.n_shared
+    lw = md.layer_weights(D.to_device(wb), gu, dn, D.to_device(b))
+    out = _empty((1, H), torch.int16, gpu)
+    idx = _empty((1, K), torch.int32, gpu)
+    say("layer_chain one row, bias planted E=%d K=%d" % (E, K))
+    md.check(md.moe_layer_chain(d, 1, [lw], D.to_device(xb), out, md.MOE_OUT_BF16,
+                                md.MOE_CHAIN_LAYER_ONLY, idx, ws))
+    md.check(md.moe_last_device_status(ws))
+    ri, _, _ = oracle.router_topk(xb, wb, K, b)
+    assert np.array_equal(idx.cpu().numpy(), ri)
+    assert not out.cpu().numpy().any()
+
+
 @pytest.mark.parametrize("wl,M", [(W.C7, 6), (W.C7, 1), (W.C6, 3)])
 def test_router_bias_on_normed_rows(gpu, dw, wl, M):
     """The router alone on the normed input u (tie-free on the biased scores)."""

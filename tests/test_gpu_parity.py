@@ -375,6 +375,24 @@ def test_chain_residual_tiny(gpu, dw):
     assert _check_chain_teacher_forced(wl, x, idx, h, hs, 3, prenorm=False) == 12
 
 
+def test_chain_residual_tiny_one_row(gpu, dw):
+    wl = W.C1
+    x = x_tiefree(wl, 1)
+    idx, h, hs = _chain_gpu(wl, dw, gpu, x, 3, md.MOE_CHAIN_RESIDUAL)
+    assert _check_chain_teacher_forced(wl, x, idx, h, hs, 3, prenorm=False) == 3
+
+
+def test_chain_prenorm_ling_one_row(gpu, dw):
+    """Four Ling layers at M=1 (the selection made by every wave on its own, per
+    layer), teacher-forced against the oracle."""
+    wl = W.C5
+    x = x_tiefree(wl, 1)
+    n = 4
+    idx, h, hs = _chain_gpu(wl, dw, gpu, x, n, md.MOE_CHAIN_PRENORM_RESIDUAL)
+    routers = [W.router(wl, l) for l in range(n)]
+    assert _check_chain_teacher_forced(wl, x, idx, h, hs, n, prenorm=True, routers=routers) == n
+
+
 def test_chain_prenorm_tiny_inplace_matches_out_of_place(gpu, dw):
     wl = W.C1
     x = x_tiefree(wl, 8)
