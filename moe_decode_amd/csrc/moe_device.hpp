@@ -170,6 +170,23 @@ __device__ __forceinline__ void st_tag(uint64_t* p, uint32_t lo, uint32_t tag) {
   __hip_atomic_store(p, ((uint64_t)tag << 32) | (uint64_t)lo, __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
 }
+// Weight rows are read once per call: their 16-byte loads carry the
+// non-temporal (streaming) policy, so the stream passes through L2 without
+// pushing out what has to stay there between calls, the kernel's own code
+// above all ("Instruction cache" and the evict-first weight streams, Ling-3.0
+// flash megakernel notes).
+#ifndef MOE_WEIGHT_NT
+#define MOE_WEIGHT_NT 1
+#endif
+__device__ __forceinline__ uint4 ld_weight(const uint4* p) {
+#if MOE_WEIGHT_NT
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *p;
+#endif
+}
 __device__ __forceinline__ uint64_t ld_tag(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -200,7 +200,7 @@ __device__ __forceinline__ void load_rows(RowRegs<CPLH>& r, const uint16_t* row0
   const uint4* src = reinterpret_cast<const uint4*>((lane >> 5) ? row1 : row0);
   const int li = lane & 31;
 #pragma unroll
-  for (int q = 0; q < CPLH; ++q) r.w[q] = src[li + 32 * q];
+  for (int q = 0; q < CPLH; ++q) r.w[q] = ld_weight(src + li + 32 * q);
 }
 
 // Dot product of each half-wave's row with token row m (all lanes of a half
@@ -256,7 +256,7 @@ __device__ __forceinline__ void load_rows8(RowRegs<CPLH>& r, const uint8_t* row0
 #pragma unroll
   for (int q = 0; q < Fp8Row<CPLH>::C; ++q) {
     const int c = li + 32 * q;
-    r.w[q] = Fp8Row<CPLH>::valid(c, H) ? src[c] : make_uint4(0u, 0u, 0u, 0u);
+    r.w[q] = Fp8Row<CPLH>::valid(c, H) ? ld_weight(src + c) : make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
@@ -403,7 +403,7 @@ __device__ __forceinline__ void load_down(DownRegs<CPLI, DBLK>& r, const P& p, i
     const uint4* src = reinterpret_cast<const uint4*>(
         static_cast<const uint16_t*>(p.lw[l].wd) + ((size_t)e * p.H + (row < n_end ? row : n)) * p.I);
 #pragma unroll
-    for (int q = 0; q < CPLI; ++q) r.w[b][q] = src[li + 8 * q];
+    for (int q = 0; q < CPLI; ++q) r.w[b][q] = ld_weight(src + li + 8 * q);
   }
 }
 
@@ -449,7 +449,7 @@ __device__ __forceinline__ void load_down8(DownRegs8<C, DB>& r, const P& p, int 
     const float* srow = p.lw[l].sd + ((size_t)e * HB + (size_t)(row >> 7)) * IB;
 #pragma unroll
     for (int q = 0; q < C; ++q) {
-      r.w[b][q] = src[li + 8 * q];
+      r.w[b][q] = ld_weight(src + li + 8 * q);
       r.s[b][q] = srow[q];
     }
   }
@@ -653,6 +653,11 @@ template <class P>
 __device__ __forceinline__ void build_union(const P& p, Small* sm, int wv, int lane) {
   constexpr int NE = kMaxPK / 64;  // entries (row, rank) per lane: i = lane + 64 j
   if (wv == 0) {
+    // the lane number, opaque to the compiler: the lane-dependent values below
+    // are made here, not hoisted out of the layer loop and held in registers
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));
+    const int lane = lane_o;
     const int MK = p.M * p.K;
     if (lane < 32) sm->bm[lane] = 0u;
 #pragma unroll

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(MOE_LM_WG, 2) void moe_lmhead_kernel(LmParams p) {
     const long long v = 2 * rp + grp;
     const uint4* row = reinterpret_cast<const uint4*>(p.w + (size_t)(v < p.V ? v : 0) * H);
 #pragma unroll
-    for (int q = 0; q < CPLH; ++q) w[q] = row[li + 32 * q];
+    for (int q = 0; q < CPLH; ++q) w[q] = ld_weight(row + li + 32 * q);
   };
   auto reduce = [&](const uint4 (&w)[CPLH], long long rp) __attribute__((always_inline)) {
     const long long v = 2 * rp + grp;
