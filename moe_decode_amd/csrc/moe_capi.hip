@@ -145,8 +145,21 @@ LmKern pick_lm_kernel_mm(int cplh) {
     default: return nullptr;
   }
 }
-LmKern pick_lm_kernel(int cplh, int M) {
-  return M <= 8 ? pick_lm_kernel_mm<8>(cplh) : pick_lm_kernel_mm<MOE_MAXM>(cplh);
+LmKern pick_lm_kernel(int cplh, int M) { return M <= 8 ? pick_lm_kernel_mm<8>(cplh) : nullptr; }
+// The matrix-core lm_head from this many token rows on (H a multiple of 256).
+// Up to 8 rows the dot-product kernel streams faster (its half-wave rows read
+// 512 contiguous bytes per instruction, the matrix-core tiles 16 rows x 64
+// bytes): 120 against 166 us at M = 1, 142 against 170 us at M = 6, even at
+// M = 8; at M = 16 the dot products bind it (278-294 us) and the matrix cores
+// take 173 us.
+#ifndef MOE_LM_MFMA_ROWS
+#define MOE_LM_MFMA_ROWS 9
+#endif
+LmKern pick_lm_mfma_kernel(int H) {
+  const int sc = H >> 6;  // 64-element super-chunks per row
+  if (sc % 8 == 0) return moe_lmhead_mfma_kernel<8>;
+  if (sc % 4 == 0) return moe_lmhead_mfma_kernel<4>;
+  return nullptr;
 }
 
 int check_dims(const moe_dims* d) {
@@ -464,12 +477,16 @@ int lmhead_argmax(int32_t M, int32_t H, int32_t V, const uint16_t* h, const uint
   if (((uintptr_t)token & 3u) || (max_logit && ((uintptr_t)max_logit & 3u))) return MOE_E_ALIGN;
   RowPlan ph;
   if (!plan_h_rows(H, &ph)) return MOE_E_UNSUPPORTED;
-  LmKern kern = pick_lm_kernel(ph.cpl, M);
+  const bool mfma = M >= MOE_LM_MFMA_ROWS;
+  LmKern kern = mfma ? pick_lm_mfma_kernel(H) : pick_lm_kernel(ph.cpl, M);
   if (!kern) return MOE_E_UNSUPPORTED;
   DevInfo di;
   int rc = device_info(&di);
   if (rc) return rc;
-  const int lds = (int)align_up((size_t)M * H * 2, 16) + MOE_LM_WAVES * MOE_MAXM * 8 + 16;
+  // x in LDS (the matrix-core kernel pads each row by 8 elements), then the
+  // per-wave bests and the last-workgroup flag
+  const size_t xrow = (size_t)H * 2 + (mfma ? 16 : 0);
+  const int lds = (int)align_up((size_t)M * xrow, 16) + MOE_LM_WAVES * MOE_MAXM * 8 + 16;
   if (lds > di.max_lds) return MOE_E_UNSUPPORTED;
   rc = prepare_kernel((const void*)kern, lds, MOE_LM_WG);
   if (rc) return rc;
@@ -486,9 +503,18 @@ int lmhead_argmax(int32_t M, int32_t H, int32_t V, const uint16_t* h, const uint
   // workgroup hides the reduction of the first at larger M), fewer for a small
   // vocabulary: at least one row pair per wave.  No workgroup waits on another
   // until the last one collects the slots, so they need not be co-resident.
-  const long long pairs = ((long long)V + 1) / 2;
-  int G = 2 * di.num_cu < MOE_LM_MAX_GRID ? 2 * di.num_cu : MOE_LM_MAX_GRID;
-  if ((long long)G * MOE_LM_WAVES > pairs) G = (int)((pairs + MOE_LM_WAVES - 1) / MOE_LM_WAVES);
+  int G;
+  if (mfma) {
+    // one workgroup per CU (its waves hold two batches of 16 rows in flight),
+    // at least one 16-row tile per wave
+    const long long tiles = ((long long)V + 15) / 16;
+    G = di.num_cu < MOE_LM_MAX_GRID ? di.num_cu : MOE_LM_MAX_GRID;
+    if ((long long)G * MOE_LM_WAVES > tiles) G = (int)((tiles + MOE_LM_WAVES - 1) / MOE_LM_WAVES);
+  } else {
+    const long long pairs = ((long long)V + 1) / 2;
+    G = 2 * di.num_cu < MOE_LM_MAX_GRID ? 2 * di.num_cu : MOE_LM_MAX_GRID;
+    if ((long long)G * MOE_LM_WAVES > pairs) G = (int)((pairs + MOE_LM_WAVES - 1) / MOE_LM_WAVES);
+  }
   if (G < 1) G = 1;
   hipLaunchKernelGGL(kern, dim3(G), dim3(MOE_LM_WG), lds, (hipStream_t)stream, p);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;

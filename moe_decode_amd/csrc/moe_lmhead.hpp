@@ -31,81 +31,14 @@ __device__ __forceinline__ uint64_t lm_key(float z, int v) {
   return ((uint64_t)f_key(z) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)v);
 }
 
-// MM: token rows the kernel is built for (8 keeps the per-row bests of the
-// common case small; 16 for the wider verify)
-template <int CPLH, int MM>
-__global__ __launch_bounds__(MOE_LM_WG, 2) void moe_lmhead_kernel(LmParams p) {
-  extern __shared__ __align__(16) unsigned char lds[];
-  uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
-  const uint4* xs4 = reinterpret_cast<const uint4*>(xs);
-  uint64_t* wbest = reinterpret_cast<uint64_t*>(lds + ((p.M * p.H * 2 + 15) & ~15));
-  int* flag = reinterpret_cast<int*>(wbest + MOE_LM_WAVES * MOE_MAXM);
-
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int G = gridDim.x, g = blockIdx.x;
-  const int M = p.M, H = p.H, H8 = H >> 3;
-  const uint32_t tag = ld_u32(p.hdr + HDR_LM_EPOCH) + 1u;
-  {
-    const uint4* src = reinterpret_cast<const uint4*>(p.h);
-    uint4* dst = reinterpret_cast<uint4*>(xs);
-    for (int i = tid; i < (M * H) >> 3; i += MOE_LM_WG) dst[i] = src[i];
-  }
-  __syncthreads();
-
-  const long long NRP = ((long long)p.V + 1) >> 1;
-  const long long NW = (long long)G * MOE_LM_WAVES;
-  const long long gw = (long long)g * MOE_LM_WAVES + wv;
-  const long long rp0 = gw * NRP / NW, rp1 = (gw + 1) * NRP / NW;
-  const int grp = lane >> 5, li = lane & 31;
-
-  float best[MM];
-  int besti[MM];
-#pragma unroll
-  for (int m = 0; m < MM; ++m) { best[m] = 0.0f; besti[m] = -1; }
-
-  auto load = [&](uint4 (&w)[CPLH], long long rp) __attribute__((always_inline)) {
-    const long long v = 2 * rp + grp;
-    const uint4* row = reinterpret_cast<const uint4*>(p.w + (size_t)(v < p.V ? v : 0) * H);
-#pragma unroll
-    for (int q = 0; q < CPLH; ++q) w[q] = ld_weight(row + li + 32 * q);
-  };
-  auto reduce = [&](const uint4 (&w)[CPLH], long long rp) __attribute__((always_inline)) {
-    const long long v = 2 * rp + grp;
-    const bool valid = v < p.V;
-#pragma unroll
-    for (int m = 0; m < MM; ++m) {
-      if (m < M) {
-        float a = 0.0f;
-#pragma unroll
-        for (int q = 0; q < CPLH; ++q) a = dot8(w[q], xs4[m * H8 + li + 32 * q], a);
-        a = group_sum(a, 32);
-        if (valid && (besti[m] < 0 || a > best[m])) { best[m] = a; besti[m] = (int)v; }
-      }
-    }
-  };
-  // two row pairs in flight per wave: the next pair's loads are issued before
-  // the current pair is reduced
-  uint4 wa[CPLH], wb[CPLH];
-  if (rp0 < rp1) load(wa, rp0);
-  for (long long rp = rp0; rp < rp1; rp += 2) {
-    if (rp + 1 < rp1) load(wb, rp + 1);
-    reduce(wa, rp);
-    if (rp + 1 < rp1) {
-      if (rp + 2 < rp1) load(wa, rp + 2);
-      reduce(wb, rp + 1);
-    }
-  }
-
-  // the wave's best per token row (both halves), then the workgroup's
-#pragma unroll
-  for (int m = 0; m < MM; ++m) {
-    if (m < M) {
-      const uint64_t key = besti[m] < 0 ? 0ull : lm_key(best[m], besti[m]);
-      const uint64_t k0 = readlane_u64(key, 0), k1 = readlane_u64(key, 32);
-      if (lane == 0) wbest[wv * MOE_MAXM + m] = k0 > k1 ? k0 : k1;
-    }
-  }
-  __syncthreads();
+// The grid-wide argmax once every wave has left its per-token-row best in
+// wbest[wave][row]: each workgroup publishes its bests as step-tagged words in
+// its own slot of the workspace and counts itself done in two levels of
+// relaxed counters (8 group counters, then one); the last workgroup collects
+// every slot (bounded wait), writes token and max logit, and advances the step.
+__device__ __forceinline__ void lm_finish(const LmParams& p, uint64_t* wbest, int* flag,
+                                          uint32_t tag, int tid) {
+  const int G = gridDim.x, g = blockIdx.x, M = p.M;
   uint64_t* slots = reinterpret_cast<uint64_t*>(reinterpret_cast<unsigned char*>(p.hdr) +
                                                 HDR_LM_SLOT_BYTE);
   if (tid < M) {
@@ -159,6 +92,214 @@ __global__ __launch_bounds__(MOE_LM_WG, 2) void moe_lmhead_kernel(LmParams p) {
     st_u32(p.hdr + HDR_LM_DONE, 0u);
     st_u32(p.hdr + HDR_LM_EPOCH, tag);
   }
+}
+
+// MM: token rows the kernel is built for (up to 8; wider calls take the
+// matrix-core kernel below)
+template <int CPLH, int MM>
+__global__ __launch_bounds__(MOE_LM_WG, 2) void moe_lmhead_kernel(LmParams p) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
+  const uint4* xs4 = reinterpret_cast<const uint4*>(xs);
+  uint64_t* wbest = reinterpret_cast<uint64_t*>(lds + ((p.M * p.H * 2 + 15) & ~15));
+  int* flag = reinterpret_cast<int*>(wbest + MOE_LM_WAVES * MOE_MAXM);
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int G = gridDim.x, g = blockIdx.x;
+  const int M = p.M, H = p.H, H8 = H >> 3;
+  const uint32_t tag = ld_u32(p.hdr + HDR_LM_EPOCH) + 1u;
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(p.h);
+    uint4* dst = reinterpret_cast<uint4*>(xs);
+    for (int i = tid; i < (M * H) >> 3; i += MOE_LM_WG) dst[i] = src[i];
+  }
+  __syncthreads();
+
+  const long long NRP = ((long long)p.V + 1) >> 1;
+  const long long NW = (long long)G * MOE_LM_WAVES;
+  const long long gw = (long long)g * MOE_LM_WAVES + wv;
+  const long long rp0 = gw * NRP / NW, rp1 = (gw + 1) * NRP / NW;
+  const int grp = lane >> 5, li = lane & 31;
+
+  float best[MM];
+  int besti[MM];
+#pragma unroll
+  for (int m = 0; m < MM; ++m) { best[m] = 0.0f; besti[m] = -1; }
+
+  auto load = [&](uint4 (&w)[CPLH], long long rp) __attribute__((always_inline)) {
+    const long long v = 2 * rp + grp;
+    const uint4* row = reinterpret_cast<const uint4*>(p.w + (size_t)(v < p.V ? v : 0) * H);
+#pragma unroll
+    for (int q = 0; q < CPLH; ++q) w[q] = ld_weight(row + li + 32 * q);
+  };
+  auto reduce = [&](const uint4 (&w)[CPLH], long long rp) __attribute__((always_inline)) {
+    const long long v = 2 * rp + grp;
+    const bool valid = v < p.V;
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      if (m < M) {
+        float a = 0.0f;
+#pragma unroll
+        for (int q = 0; q < CPLH; ++q) a = dot8(w[q], xs4[m * H8 + li + 32 * q], a);
+        a = group_sum(a, 32);
+        if (valid && (besti[m] < 0 || a > best[m])) { best[m] = a; besti[m] = (int)v; }
+      }
+    }
+  };
+  // two row pairs in flight per wave: the next pair's loads are issued before
+  // the current pair is reduced, unconditionally in the steady-state loop (a
+  // load behind a condition would make the waits count only the loads of the
+  // path without it, and so wait for the pair in flight too)
+  uint4 wa[CPLH], wb[CPLH];
+  long long rp = rp0;
+  if (rp0 < rp1) load(wa, rp0);
+  for (; rp + 2 < rp1; rp += 2) {
+    load(wb, rp + 1);
+    reduce(wa, rp);
+    load(wa, rp + 2);
+    reduce(wb, rp + 1);
+  }
+  if (rp + 1 < rp1) {
+    load(wb, rp + 1);
+    reduce(wa, rp);
+    reduce(wb, rp + 1);
+  } else if (rp < rp1) {
+    reduce(wa, rp);
+  }
+
+  // the wave's best per token row (both halves), then the workgroup's
+#pragma unroll
+  for (int m = 0; m < MM; ++m) {
+    if (m < M) {
+      const uint64_t key = besti[m] < 0 ? 0ull : lm_key(best[m], besti[m]);
+      const uint64_t k0 = readlane_u64(key, 0), k1 = readlane_u64(key, 32);
+      if (lane == 0) wbest[wv * MOE_MAXM + m] = k0 > k1 ? k0 : k1;
+    }
+  }
+  __syncthreads();
+  lm_finish(p, wbest, flag, tag, tid);
+}
+
+// The same GEMV and argmax on the matrix cores, for several token rows: the
+// logits of M token rows over V vocabulary rows are a dense [V x H] x [H x M]
+// contraction, M FLOP per weight byte, which at M >= 6 keeps the vector ALUs
+// busier than the weight stream allows.  One workgroup per CU, 8 waves; each
+// wave takes a contiguous range of 16-row vocabulary tiles and multiplies
+// each tile by the token rows with v_mfma_f32_16x16x32_bf16: the tile's rows
+// are the 16 rows of A (lane l: vocabulary row l % 16), the token rows the 16
+// columns of B (lane l: token row l % 16, repeating row 0 past M; those
+// columns are ignored).  A row is read in 64-element super-chunks, one 128-byte
+// line: lane group q = l / 16 loads its 16 bytes at elements 8q and 32 + 8q,
+// which feed two MFMAs; B is read from LDS at the same elements, so both
+// operands sum over the same k in the same order for every row.  NB
+// super-chunks form one batch of loads, and the next batch is in flight while
+// the current one is multiplied.  x sits in LDS with a row stride of H + 8
+// elements, which keeps the 16 token rows' 16-byte reads on distinct banks.
+template <int NB>
+__global__ __launch_bounds__(MOE_LM_WG, 1) void moe_lmhead_mfma_kernel(LmParams p) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int M = p.M, H = p.H, V = p.V, XS = H + 8;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
+  uint64_t* wbest = reinterpret_cast<uint64_t*>(lds + ((M * XS * 2 + 15) & ~15));
+  int* flag = reinterpret_cast<int*>(wbest + MOE_LM_WAVES * MOE_MAXM);
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int G = gridDim.x, g = blockIdx.x;
+  const uint32_t tag = ld_u32(p.hdr + HDR_LM_EPOCH) + 1u;
+  {
+    const int H8 = H >> 3;
+    const uint4* src = reinterpret_cast<const uint4*>(p.h);
+    for (int i = tid; i < M * H8; i += MOE_LM_WG) {
+      const int m = i / H8, c = i - m * H8;
+      *reinterpret_cast<uint4*>(xs + m * XS + 8 * c) = src[i];
+    }
+  }
+  __syncthreads();
+
+  const int NT = (V + 15) >> 4;            // 16-row tiles
+  const int NBT = (H >> 6) / NB;           // batches per tile
+  const long long NW = (long long)G * MOE_LM_WAVES;
+  const long long gw = (long long)g * MOE_LM_WAVES + wv;
+  const int t0 = (int)(gw * NT / NW), t1 = (int)((gw + 1) * NT / NW);
+  const int S = (t1 - t0) * NBT;           // batches of this wave
+  const int i16 = lane & 15, q = lane >> 4;
+  const uint16_t* xr = xs + (i16 < M ? i16 : 0) * XS + 8 * q;
+
+  auto load = [&](uint4 (&w)[2 * NB], int s) __attribute__((always_inline)) {
+    const int tl = s / NBT, bt = s - tl * NBT;
+    const int v = 16 * (t0 + tl) + i16;
+    const uint4* row = reinterpret_cast<const uint4*>(p.w + (size_t)(v < V ? v : V - 1) * H) +
+                       (size_t)bt * NB * 8 + q;
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      w[2 * c] = ld_weight(row + 8 * c);
+      w[2 * c + 1] = ld_weight(row + 8 * c + 4);
+    }
+  };
+  f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+  uint64_t best = 0ull;
+  auto mul = [&](const uint4 (&w)[2 * NB], int s) __attribute__((always_inline)) {
+    const int tl = s / NBT, bt = s - tl * NBT;
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      const uint16_t* xb = xr + 64 * (bt * NB + c);
+      const uint4 b0 = *reinterpret_cast<const uint4*>(xb);
+      const uint4 b1 = *reinterpret_cast<const uint4*>(xb + 32);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w[2 * c]),
+                                                      __builtin_bit_cast(bf16x8, b0), acc0, 0, 0,
+                                                      0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w[2 * c + 1]),
+                                                      __builtin_bit_cast(bf16x8, b1), acc1, 0, 0,
+                                                      0);
+    }
+    if (bt == NBT - 1) {
+      // tile done: lane l holds rows 4q .. 4q + 3 of the tile for token row l % 16
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int v = 16 * (t0 + tl) + 4 * q + j;
+        const float z = acc0[j] + acc1[j];
+        if (i16 < M && v < V) {
+          const uint64_t k = lm_key(z, v);
+          best = k > best ? k : best;
+        }
+      }
+      acc0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      acc1 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  };
+  // two batches in flight: the steady-state loop issues its loads
+  // unconditionally (a load behind a condition would make every wait in the
+  // loop count only the loads of the path without it, and so wait for the
+  // batch in flight too); the last one or two batches follow it
+  uint4 wa[2 * NB], wb[2 * NB];
+  int s = 0;
+  if (S > 0) load(wa, 0);
+  for (; s + 2 < S; s += 2) {
+    load(wb, s + 1);
+    mul(wa, s);
+    load(wa, s + 2);
+    mul(wb, s + 1);
+  }
+  if (s + 1 < S) {
+    load(wb, s + 1);
+    mul(wa, s);
+    mul(wb, s + 1);
+  } else if (s < S) {
+    mul(wa, s);
+  }
+
+  // the wave's best per token row: lanes r, r + 16, r + 32, r + 48 hold row r
+  {
+    uint64_t o = __shfl_xor(best, 16);
+    best = o > best ? o : best;
+    o = __shfl_xor(best, 32);
+    best = o > best ? o : best;
+    if (lane < M) wbest[wv * MOE_MAXM + lane] = best;
+  }
+  __syncthreads();
+  lm_finish(p, wbest, flag, tag, tid);
 }
 
 }  // namespace moe
