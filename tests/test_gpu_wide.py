@@ -172,3 +172,31 @@ def test_lmhead_m16(gpu, V):
         if marg[m] >= 1e-4 or V == 1:
             assert got[m] == t_ref[m], (m, got[m], t_ref[m])
     assert np.all(np.abs(mx.cpu().numpy() - m_ref) <= 1e-4 * np.abs(m_ref) + 1e-5)
+
+
+@pytest.mark.parametrize("wl,M,V", [(W.C5, 9, 4097), (W.C5, 12, 157), (W.C1, 12, 1000),
+                                    (W.C1, 16, 17)])
+def test_lmhead_matrix_cores_ragged(gpu, wl, M, V):
+    """From 9 token rows the lm_head runs on the matrix cores (16-row tiles):
+    ragged vocabularies (a partial last tile), hidden sizes of 40 and 4
+    super-chunks, and a planted exact tie that the lower index must win."""
+    import torch
+    h = W.x_rows(wl, list(range(M)))
+    w = W.lmhead_rows(wl, 0, V).copy()
+    z = f32(h[0]).astype(np.float64) @ f32(w).astype(np.float64).T
+    best = int(np.argmax(z))
+    w[V - 1] = w[best]          # exact duplicate of row 0's winner at the highest index
+    ws = md.new_workspace(_dims(wl), M, 1)
+    tok = _empty((M,), torch.int32, gpu)
+    mx = _empty((M,), torch.float32, gpu)
+    say("lmhead_argmax matrix cores %s M=%d V=%d" % (wl.name, M, V))
+    md.check(md.lmhead_argmax(M, wl.H, V, D.to_device(h), D.to_device(w), tok, mx, ws))
+    md.check(md.moe_last_device_status(ws))
+    t_ref, m_ref = oracle.lmhead_argmax(h, w)
+    marg = runner.lmhead_margin(h, w)
+    got = tok.cpu().numpy()
+    assert got[0] == t_ref[0] == min(best, V - 1)
+    for m in range(M):
+        if marg[m] >= 1e-4:
+            assert got[m] == t_ref[m], (m, got[m], t_ref[m])
+    assert np.all(np.abs(mx.cpu().numpy() - m_ref) <= 1e-4 * np.abs(m_ref) + 1e-5)
