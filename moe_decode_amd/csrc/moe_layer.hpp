@@ -598,6 +598,25 @@ __device__ __forceinline__ void topk_fast(const float* lgs, float bv, Small* sm,
   __syncthreads();
 }
 
+// Lane c < n takes candidate c of a row (cr: its n packed candidates) and
+// counts the candidates that precede it in the selection order: its rank.
+__device__ __forceinline__ int rank_candidates(const uint64_t* cr, int n, int lane,
+                                               uint64_t& mine) {
+  mine = lane < n ? cr[lane] : 0ull;
+  int rank = 0;
+#pragma unroll 1
+  for (int j = 0; j < n; j += 8) {
+    const ulonglong2 c0 = *reinterpret_cast<const ulonglong2*>(cr + j);
+    const ulonglong2 c1 = *reinterpret_cast<const ulonglong2*>(cr + j + 2);
+    const ulonglong2 c2 = *reinterpret_cast<const ulonglong2*>(cr + j + 4);
+    const ulonglong2 c3 = *reinterpret_cast<const ulonglong2*>(cr + j + 6);
+    const uint64_t c8[8] = {c0.x, c0.y, c1.x, c1.y, c2.x, c2.y, c3.x, c3.y};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) rank += (j + q < n && c8[q] > mine) ? 1 : 0;
+  }
+  return rank;
+}
+
 // bv: the selection bias of expert tid (0 without a bias), loaded before the
 // logits arrive; bias: the bias vector for the plain path (or null).
 template <class P>
@@ -623,19 +642,8 @@ __device__ __forceinline__ void topk_rows(const P& p, const float* lgs, float bv
   for (int m = wv; m < M; m += MOE_WAVES) {
     const int n = fast ? sm->ccount[m] : 0;
     if (n >= K && n <= 64) {
-      const uint64_t* cr = sm->cand + m * 64;
-      const uint64_t mine = lane < n ? cr[lane] : 0ull;
-      int rank = 0;
-#pragma unroll 1
-      for (int j = 0; j < n; j += 8) {
-        const ulonglong2 c0 = *reinterpret_cast<const ulonglong2*>(cr + j);
-        const ulonglong2 c1 = *reinterpret_cast<const ulonglong2*>(cr + j + 2);
-        const ulonglong2 c2 = *reinterpret_cast<const ulonglong2*>(cr + j + 4);
-        const ulonglong2 c3 = *reinterpret_cast<const ulonglong2*>(cr + j + 6);
-        const uint64_t c8[8] = {c0.x, c0.y, c1.x, c1.y, c2.x, c2.y, c3.x, c3.y};
-#pragma unroll
-        for (int q = 0; q < 8; ++q) rank += (j + q < n && c8[q] > mine) ? 1 : 0;
-      }
+      uint64_t mine;
+      const int rank = rank_candidates(sm->cand + m * 64, n, lane, mine);
       if (lane < n && rank < K) sm->tk_idx[m * K + rank] = (int)~(uint32_t)mine;
       // gates in rank order (the candidates' lane order depends on timing)
       gates_from_idx(lgs + m * E, K, sm, m, lane);
@@ -877,6 +885,9 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     }
 
     // ---------------- P4: routing
+    // one token row (K <= 8): the routed slots are the ranks (see P5)
+    const bool one_row = M == 1 && K <= 8 && !topk_in && !router_only;
+    bool ranked = false;  // one row ranked by every wave, slot tables filled
     if (topk_in) {
       for (int i = tid; i < MK; i += MOE_WG) {
         int e = p.tk_idx_in[i];
@@ -899,19 +910,68 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       __syncthreads();
       MOE_STAMP(3);
       if (sm->abort_flag == 1) break;
-      topk_rows(p, lgs, bv, bias, sm, tid, wv, lane);
-      __syncthreads();
-      MOE_STAMP(9);
-      if (g == 0 || router_only) {
-        int32_t* oi = p.tk_idx_out ? p.tk_idx_out + (size_t)l * MK : nullptr;
-        for (int i = tid; i < MK; i += MOE_WG) {
-          if (oi) oi[i] = sm->tk_idx[i];
-          if (p.tk_gate_out && l == 0) p.tk_gate_out[i] = sm->tk_gate[i];
+      // One token row on the threshold path: every wave ranks the candidates
+      // itself and fills its own slot table (slot r = rank r); only wave 0
+      // goes on to the gates and the workgroup's tables (read after the
+      // barrier that opens the down projection), so no barrier follows the
+      // selection.  A row with more than 64 candidates takes the plain path.
+      const int nWg = (E + 63) >> 6;
+      if (one_row && E <= MOE_WG && K <= nWg) {
+        topk_fast<1>(lgs, bv, sm, E, K, nWg, tid, wv, lane);
+        const int n = sm->ccount[0];
+        if (n >= K && n <= 64) {
+          ranked = true;
+          int ln = lane;  // opaque lane number (no hoisted lane-dependent addresses)
+          asm volatile("" : "+v"(ln));
+          uint64_t mine;
+          const int rank = rank_candidates(sm->cand, n, ln, mine);
+          const bool sel = ln < n && rank < K;
+          const int e = (int)~(uint32_t)mine;
+          if (sel) {
+            sm->uexp[kOwnSlots + wv * 8 + rank] = e;
+            sm->umask[kOwnSlots + wv * 8 + rank] = 1u;
+            sm->pbase[kOwnSlots + wv * 8 + rank] = rank;
+          }
+          if (wv == 0) {
+            if (sel) {
+              sm->tk_idx[rank] = e;
+              sm->uexp[rank] = e;
+              sm->umask[rank] = 1u;
+              sm->pbase[rank] = rank;
+            }
+            gates_from_idx(lgs, K, sm, 0, ln);
+            if (ln < K) sm->upos[ln] = ln;
+            if (ln == 0) {
+              sm->nU = K;
+              sm->nP = K;
+            }
+            if (g == 0 && ln < K) {
+              if (p.tk_idx_out) p.tk_idx_out[(size_t)l * MK + ln] = sm->tk_idx[ln];
+              if (p.tk_gate_out && l == 0) p.tk_gate_out[ln] = sm->tk_gate[ln];
+            }
+          }
+          if (g == 0 && p.logits_out && l == 0)
+            for (int i = tid; i < E; i += MOE_WG) p.logits_out[i] = lgs[i];
+          MOE_STAMP(9);
+        } else {
+          __syncthreads();  // every wave has read the candidate count
         }
-        if (p.logits_out && l == 0)
-          for (int i = tid; i < M * E; i += MOE_WG) p.logits_out[i] = lgs[i];
       }
-      if (router_only) break;
+      if (!ranked) {
+        topk_rows(p, lgs, bv, bias, sm, tid, wv, lane);
+        __syncthreads();
+        MOE_STAMP(9);
+        if (g == 0 || router_only) {
+          int32_t* oi = p.tk_idx_out ? p.tk_idx_out + (size_t)l * MK : nullptr;
+          for (int i = tid; i < MK; i += MOE_WG) {
+            if (oi) oi[i] = sm->tk_idx[i];
+            if (p.tk_gate_out && l == 0) p.tk_gate_out[i] = sm->tk_gate[i];
+          }
+          if (p.logits_out && l == 0)
+            for (int i = tid; i < M * E; i += MOE_WG) p.logits_out[i] = lgs[i];
+        }
+        if (router_only) break;
+      }
     }
 
     // ---------------- P5: routed slots
@@ -921,9 +981,10 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     // stands between the selection and the routed gate/up stream; wave 0 fills
     // the workgroup's tables, which the down projection and the combine read
     // after the barrier that opens the down projection.
-    const bool one_row = M == 1 && K <= 8 && !topk_in;
     int U;
-    if (one_row) {
+    if (ranked) {
+      U = K;
+    } else if (one_row) {
       // the lane number, opaque to the compiler: the addresses built from it
       // are made here, not hoisted out of the layer loop and held in registers
       int ln = lane;
