@@ -216,6 +216,11 @@ def main():
         print("chain16+lm_head M=6: %.1f us (floor %.1f us, ratio %.2f)"
               % (c["us_per_step"], c["floor_us_at_peak"], c["ratio_to_floor"]),
               file=sys.stderr, flush=True)
+        lmr = time_lmhead(md, D, W, np, torch, dev)
+        secondary["lmhead_v%d" % W.C5.V] = lmr
+        print("lm_head alone: " + ", ".join("M=%s %.1f us (%.0f GB/s)" % (k[2:], v["us"], v["gbs"])
+                                              for k, v in lmr.items()),
+              file=sys.stderr, flush=True)
 
     traffic = None
     if os.path.exists(args.traffic):
@@ -316,6 +321,37 @@ def time_chain(md, D, W, np, torch, dev, lw, steps, warmup, wl=None):
         "floor_us_at_peak": float(floor_us),
         "ratio_to_floor": float(tot_us / floor_us),
     }
+
+
+def time_lmhead(md, D, W, np, torch, dev, rows=(1, 6, 16), calls=30, warmup=3):
+    """The lm_head argmax alone (V = 157184, H = 2560), back-to-back calls at each
+    row count: the dot-product kernel up to 8 rows, the matrix-core kernel above.
+    The 805 MB matrix exceeds every cache, so every call streams it from HBM."""
+    wl = W.C5
+    lm = D.make_lmhead(wl)
+    d = md.dims(wl.H, wl.E, wl.K, wl.I, wl.S)
+    ws = md.new_workspace(d, max(rows), 1)
+    out = {}
+    for M in rows:
+        hs = [D.to_device(W.x_rows(wl, [s * M + m for m in range(M)]))
+              for s in range(calls + warmup)]
+        tok = torch.empty((M,), dtype=torch.int32, device=dev)
+        for i in range(warmup):
+            md.check(md.lmhead_argmax(M, wl.H, wl.V, hs[i], lm, tok, None, ws))
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(warmup, warmup + calls):
+            md.check(md.lmhead_argmax(M, wl.H, wl.V, hs[i], lm, tok, None, ws))
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / calls
+        out["M=%d" % M] = {"us": float(us), "gbs": float(wl.V * wl.H * 2 / us / 1e3),
+                           "pct_of_hbm_peak": float(100.0 * wl.V * wl.H * 2 / us / 1e3
+                                                    / HBM_PEAK_GBS)}
+    md.check(md.moe_last_device_status(ws))
+    del lm
+    return out
 
 
 def profile_run(key):
