@@ -6,7 +6,7 @@
 //   P0  stage the layer input x [M][H] in LDS (layer 0 from the caller's
 //       buffer, later layers from step-tagged residual words); under the
 //       pre-norm chain keep this workgroup's rows of h_l for the residual and
-//       replace x by bf16(RMSNorm(h_l)).
+//       replace x by bf16(RMSNorm(h_l) * gain).
 //   P1  router GEMV rows and the shared expert's gate/up rows, spread over every
 //       wave of the GPU.  The shared expert does not depend on routing, so its
 //       weights stream while the logits travel ("weights that do not depend on
@@ -15,25 +15,26 @@
 //       published as step-tagged words.
 //   P4  every workgroup reads all logits and computes the softmax top-k
 //       itself, so no second device-wide hop is needed.
-//   P5  union of the rows' choices: a bitmap over experts plus population
-//       counts gives each selected expert its slot with no scan over experts or
-//       sort (SGLang Low-Latency Mode, item 3: at most eight rows).
-//   P6  routed experts, in teams: the routed work (every expert's gate/up rows
-//       plus its down rows, the same amount per expert) is laid on a line and
-//       cut into one equal slice per workgroup.  A slice covers a fraction of at
-//       most two experts; for each it computes the matching share of the
-//       intermediate dimension (gate/up GEMV + SwiGLU, published as tagged bf16
-//       pairs) ...
-//   P7  ... and, once the team has published the expert's whole SwiGLU output,
-//       the same share of the expert's down-projection rows, published as
-//       tagged fp32 values.  The shared expert's down rows are done first by the
-//       owners of those output rows, while the teams finish.
+//   P5  routed slots: the union of the rows' choices, from a bitmap over experts
+//       plus population counts, with no scan over experts or sort (SGLang
+//       Low-Latency Mode, item 3).  One token row needs no union: slot r is
+//       rank r, and every wave keeps its own slot table.
+//   P6  routed gate/up + SwiGLU: the tasks (one intermediate row pair of one
+//       slot) of the whole union are dealt round-robin over every wave of the
+//       GPU, so each workgroup streams from every selected expert; SwiGLU
+//       outputs are published as tagged bf16 pairs.
+//   P7  down projection: the (slot, output row) space is cut into one equal
+//       slice per workgroup (pieces of at most two slots); each workgroup stages
+//       the SwiGLU rows of its pieces and of the shared expert in LDS with one
+//       batched wait, then streams the shared expert's down rows for its own
+//       output rows and its pieces' routed down rows, published as tagged fp32.
 //   P8  each workgroup owns a slice of output rows and combines
-//       y_shared + sum_k g_k y_k in fp32 in rank order, then rounds once (or adds
-//       the residual with one rounding, or writes the fp32 partial).
+//       y_shared + s * sum_k g_k y_k in fp32 in rank order, then rounds once (or
+//       adds the residual with one rounding, or writes the fp32 partial).
 //
 // Every selected expert's weights stream from HBM exactly once per call, for
-// all the token rows that chose it; no workgroup reads another's weights.
+// all the token rows that chose it, with the non-temporal policy (read once,
+// they pass through L2 without evicting the kernel's code).
 #pragma once
 
 #include <type_traits>
