@@ -499,10 +499,10 @@ int lmhead_argmax(int32_t M, int32_t H, int32_t V, const uint16_t* h, const uint
   p.token = token;
   p.max_logit = max_logit;
   p.hdr = (uint32_t*)ws;
-  // two workgroups per CU (each wave keeps two row pairs in flight; the second
-  // workgroup hides the reduction of the first at larger M), fewer for a small
-  // vocabulary: at least one row pair per wave.  No workgroup waits on another
-  // until the last one collects the slots, so they need not be co-resident.
+  // The dot-product kernel: two workgroups per CU (they run in two rounds, one
+  // fits a CU at a time), fewer for a small vocabulary: at least one row pair
+  // per wave.  No workgroup waits on another until the last one collects the
+  // slots, so they need not be co-resident.
   int G;
   if (mfma) {
     // one workgroup per CU (its waves hold two batches of 16 rows in flight),

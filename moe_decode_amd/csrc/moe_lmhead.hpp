@@ -1,6 +1,9 @@
 // bf16 lm_head GEMV with the greedy argmax folded in (gfx950).
 //
-// Two workgroups per CU, 8 waves each.  Every wave streams a contiguous range of
+// 512-thread workgroups, 8 waves each (about 144 VGPRs: one workgroup per CU at a
+// time, the grid of two per CU runs in two rounds; holding the kernel to 128
+// VGPRs for two resident workgroups spills in the row loop and is 18 % slower).
+// Every wave streams a contiguous range of
 // vocabulary row pairs (one row per 32-lane half, 16-byte loads,
 // v_dot2_f32_bf16) against the M hidden rows held in LDS, with the next pair's
 // loads in flight while the current pair is reduced, and keeps per token row
