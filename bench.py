@@ -58,7 +58,10 @@ PROFILE_WORKLOADS = {"m1": ("ling_moe_layer_m1", 1, False),
                      "fp8m1": ("ling_fp8_moe_layer_m1", 1, False),
                      "fp8m6": ("ling_fp8_moe_layer_m6", 6, False),
                      "m16": ("ling_moe_layer_m16", 16, False),
-                     "lmhead": ("lmhead_v157184_m6", 6, False)}
+                     "lmhead": ("lmhead_v157184_m6", 6, False),
+                     "lmhead16": ("lmhead_v157184_m16", 16, False)}
+# kernel profiled by each workload (the layer kernel unless named here)
+PROFILE_KERNELS = {"lmhead": "moe_lmhead_kernel", "lmhead16": "moe_lmhead_mfma_kernel"}
 COPY_BYTES = 256 << 20   # reference copy for the counter scale
 PROFILE_CALLS = 64
 
@@ -365,7 +368,7 @@ def profile_run(key):
     from datagen import workloads as W
 
     name, M, f32 = PROFILE_WORKLOADS[key]
-    if key == "lmhead":
+    if key in PROFILE_KERNELS:
         return profile_run_lmhead(name, M)
     wl = {w.name: w for w in (W.C2, W.C3, W.C4, W.C7, W.C9, W.C10, W.C12)}[name]
     dev = torch.device("cuda:0")
@@ -466,7 +469,7 @@ def ingest_profiles(root):
     traffic = {"kernel_source_sha": kernel_source_sha(), "copy_bytes": COPY_BYTES,
                "workloads": {}}
     for key, (name, M, _) in sorted(PROFILE_WORKLOADS.items()):
-        kname = "moe_lmhead_kernel" if key == "lmhead" else "moe_layer_kernel"
+        kname = PROFILE_KERNELS.get(key, "moe_layer_kernel")
         cmd_kt = ("rocprofv3 --kernel-trace --stats --output-format csv -d %s/kt_%s -o kt "
                   "-- python3 bench.py --profile-run %s" % (root, key, key))
         alg = None
@@ -514,14 +517,14 @@ def ingest_profiles(root):
                                                                           key))
             lines.append("  reference copy of %d bytes (read once, written once): %.1f units "
                          "-> %.2f bytes per unit" % (COPY_BYTES, ref[0], scale))
-            lines.append("  layer kernel: %.1f units per launch (mean of %d) = %.3f MB per launch"
-                         % (np.mean(vals), len(vals), per / 1e6))
+            lines.append("  %s: %.1f units per launch (mean of %d) = %.3f MB per launch"
+                         % (kname, np.mean(vals), len(vals), per / 1e6))
         if "fetch_bytes_per_launch" in w:
             w["bytes_per_launch"] = w["fetch_bytes_per_launch"] + w.get("write_bytes_per_launch", 0.0)
         if alg:
             w["algorithmic_bytes_per_launch"] = alg
             lines.append("")
-            what = ("the V x H weight, once" if key == "lmhead"
+            what = ("the V x H weight, once" if key in PROFILE_KERNELS
                     else "router + union + shared expert, each once")
             lines.append("algorithmic bytes per launch (%s): %.3f MB" % (what, alg / 1e6))
             if "bytes_per_launch" in w:
