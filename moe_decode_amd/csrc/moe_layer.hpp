@@ -417,14 +417,21 @@ __device__ __forceinline__ void compute_down(const DownRegs<CPLI, DBLK>& r, int 
   const int gl = lane >> 3, li = lane & 7;
 #pragma unroll 1
   for (int t = 0; t < nrows; ++t) {
+    // each 16-byte chunk of h is read once and serves every block
+    float acc[DBLK];
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b) acc[b] = 0.0f;
+#pragma unroll
+    for (int q = 0; q < CPLI; ++q) {
+      const uint4 x = hv4[t * I8 + li + 8 * q];
+#pragma unroll
+      for (int b = 0; b < DBLK; ++b) acc[b] = dot8(r.w[b][q], x, acc[b]);
+    }
 #pragma unroll
     for (int b = 0; b < DBLK; ++b) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int q = 0; q < CPLI; ++q) acc = dot8(r.w[b][q], hv4[t * I8 + li + 8 * q], acc);
-      acc = group_sum(acc, 8);
+      const float y = group_sum(acc[b], 8);
       const int row = n + 8 * b + gl;
-      if (li == 0 && row < n_end) emit(t, row, acc);
+      if (li == 0 && row < n_end) emit(t, row, y);
     }
   }
 }
@@ -785,6 +792,13 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
   const int n0 = 2 * r0, NR = 2 * (r1 - r0);
 
   for (int l = 0; l < p.L; ++l) {
+    // the thread number, opaque to the compiler: values derived from it are
+    // made again in every layer instead of being hoisted out of the layer loop
+    // and held in registers through every phase
+    int tid_o = tid;
+    asm volatile("" : "+v"(tid_o));
+    const int tid = tid_o;
+    const int lane = tid & 63;
     sbase = l == 0 ? 0 : (l == 1 ? 10 : (l == p.L - 1 ? 20 : -1));
     MOE_STAMP(0);
     // ---------------- P1 prefetch: this wave's first router / shared gate-up rows
@@ -1093,6 +1107,12 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     // inputs of all of them are staged in LDS with one batched wait.
     uint64_t* y_l = p.y_buf + (size_t)l * MK * H;
     {
+      // (the thread number made opaque again: the lane-dependent values of the
+      // down projection are made here, not hoisted into the gate/up phase)
+      int tid_p7 = tid;
+      asm volatile("" : "+v"(tid_p7));
+      const int tid = tid_p7;
+      const int lane = tid & 63;
       // the SwiGLU rows staged below overwrite x, which the routed gate/up rows
       // read; and the slot tables read below may come from wave 0 alone (one
       // token row)
