@@ -72,7 +72,7 @@ def main():
         ingest_profiles(args.ingest_profiles)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     if args.profile_run:
