@@ -59,9 +59,11 @@ PROFILE_WORKLOADS = {"m1": ("ling_moe_layer_m1", 1, False),
                      "fp8m6": ("ling_fp8_moe_layer_m6", 6, False),
                      "m16": ("ling_moe_layer_m16", 16, False),
                      "lmhead": ("lmhead_v157184_m6", 6, False),
-                     "lmhead16": ("lmhead_v157184_m16", 16, False)}
+                     "lmhead16": ("lmhead_v157184_m16", 16, False),
+                     "prefetch": ("ling_moe_layer_m1_prefetch", 1, False)}
 # kernel profiled by each workload (the layer kernel unless named here)
-PROFILE_KERNELS = {"lmhead": "moe_lmhead_kernel", "lmhead16": "moe_lmhead_mfma_kernel"}
+PROFILE_KERNELS = {"lmhead": "moe_lmhead_kernel", "lmhead16": "moe_lmhead_mfma_kernel",
+                   "prefetch": "moe_prefetch_kernel"}
 COPY_BYTES = 256 << 20   # reference copy for the counter scale
 PROFILE_CALLS = 64
 
@@ -166,7 +168,19 @@ def main():
           file=sys.stderr, flush=True)
 
     secondary = {}
+
+    def report_prefetch(name, r):
+        secondary[name] = r
+        print("%s: layer %.1f us cold, %.1f / %.1f / %.1f us after a prefetch at 100 / 75 / 0 %% "
+              "routed hits; prefetch %.1f us (%.0f GB/s)"
+              % (name, r["cold"]["layer_us_mean"], r["hit100"]["layer_us_mean"],
+                 r["hit75"]["layer_us_mean"], r["hit0"]["layer_us_mean"],
+                 r["hit100"]["prefetch_us_mean"], r["hit100"]["prefetch_gbs"]),
+              file=sys.stderr, flush=True)
+
     if not args.no_secondary:
+        report_prefetch(W.C2.name + "_prefetch",
+                        time_prefetch(md, np, torch, dev, W.C2, lw, x_pool(W.C2, 176, 1)))
         s3 = time_layer(W.C3, lw, 6, args.steps, args.warmup)
         secondary[W.C3.name] = s3
         print("M=6: %.2f us/layer, %.0f GB/s (%.1f %%), U=%.1f"
@@ -207,6 +221,8 @@ def main():
             print("fp8 M=%d: %.2f us/layer, %.0f GB/s (%.1f %%)"
                   % (M8, r8["us_per_layer"], r8["effective_gbs"], r8["pct_of_hbm_peak"]),
                   file=sys.stderr, flush=True)
+        report_prefetch(W.C9.name + "_prefetch",
+                        time_prefetch(md, np, torch, dev, W.C9, lw8, x_pool(W.C9, 176, 1)))
         c8 = time_chain(md, D, W, np, torch, dev, lw8, steps=10, warmup=2, wl=W.C11)
         secondary[W.C11.name] = c8
         print("fp8 chain16+lm_head M=6: %.1f us (floor %.1f us, ratio %.2f)"
@@ -326,6 +342,73 @@ def time_chain(md, D, W, np, torch, dev, lw, steps, warmup, wl=None):
     }
 
 
+def time_prefetch(md, np, torch, dev, wl, lws, xs, calls=160, warmup=16):
+    """Layer time after a speculative prefetch of its experts, against cold.
+
+    Calls rotate over the distinct layers in `lws`, so each call's weights were
+    last read many gigabytes ago.  A first untimed pass records every call's
+    routing; then, per call, the guess lists the chosen experts with a share
+    replaced by experts the call does not pick (routed hit rate 100, 75 or 0 %),
+    plus the shared expert.  moe_expert_prefetch runs just before the layer on
+    the same stream; events around each kernel give the layer's and the
+    prefetch's time.  "cold" is the same loop with no prefetch."""
+    M = xs.shape[1]
+    d = md.dims(wl.H, wl.E, wl.K, wl.I, wl.S, wl.routed_scale,
+                md.MOE_EXPERT_FP8_B128 if wl.fp8 else md.MOE_EXPERT_BF16)
+    ws = md.new_workspace(d, M, 1)
+    n = calls + warmup
+    nl = len(lws)
+    out = torch.empty((M, wl.H), dtype=torch.int16, device=dev)
+    idx = torch.empty((n, M, wl.K), dtype=torch.int32, device=dev)
+
+    def layer(i):
+        md.check(md.moe_layer_chain(d, M, [lws[i % nl]], xs[i], out, md.MOE_OUT_BF16,
+                                    md.MOE_CHAIN_LAYER_ONLY, idx[i], ws))
+
+    for i in range(n):
+        layer(i)
+    torch.cuda.synchronize()
+    md.check(md.moe_last_device_status(ws))
+    chosen = [np.unique(r) for r in idx.cpu().numpy()]
+    rng = np.random.default_rng(20240607)
+    res = {}
+    for label, hit in (("cold", None), ("hit100", 1.0), ("hit75", 0.75), ("hit0", 0.0)):
+        ids = None
+        if hit is not None:
+            lists = []
+            for ch in chosen:
+                keep = int(round(hit * len(ch)))
+                pool = np.setdiff1d(np.arange(wl.E), ch)
+                wrong = rng.choice(pool, len(ch) - keep, replace=False)
+                lists.append(np.concatenate([ch[:keep], wrong, np.arange(wl.E, wl.E + wl.S)]))
+            width = max(len(l) for l in lists)
+            pad = np.full((n, width), -1, dtype=np.int32)   # -1 is skipped by the prefetch
+            for i, l in enumerate(lists):
+                pad[i, :len(l)] = l
+            ids = torch.from_numpy(pad).to(dev)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        torch.cuda.synchronize()
+        for i in range(n):
+            evs[i][0].record()
+            if ids is not None:
+                md.check(md.moe_expert_prefetch(d, lws[i % nl], ids[i], ids.shape[1]))
+            evs[i][1].record()
+            layer(i)
+            evs[i][2].record()
+        torch.cuda.synchronize()
+        md.check(md.moe_last_device_status(ws))
+        lay = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(warmup, n)]) * 1e3
+        pf = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(warmup, n)]) * 1e3
+        r = {"layer_us_mean": float(lay.mean()), "layer_us_median": float(np.median(lay))}
+        if ids is not None:
+            nb = float(np.mean([len(l) for l in lists])) * wl.expert_bytes()
+            r.update({"prefetch_us_mean": float(pf.mean()), "prefetch_bytes": nb,
+                      "prefetch_gbs": float(nb / (pf.mean() * 1e-6) / 1e9)})
+        res[label] = r
+    res["saving_us_at_hit100"] = res["cold"]["layer_us_mean"] - res["hit100"]["layer_us_mean"]
+    return res
+
+
 def time_lmhead(md, D, W, np, torch, dev, rows=(1, 6, 16), calls=30, warmup=3):
     """The lm_head argmax alone (V = 157184, H = 2560), back-to-back calls at each
     row count: the dot-product kernel up to 8 rows, the matrix-core kernel above.
@@ -368,6 +451,8 @@ def profile_run(key):
     from datagen import workloads as W
 
     name, M, f32 = PROFILE_WORKLOADS[key]
+    if key == "prefetch":
+        return profile_run_prefetch(name)
     if key in PROFILE_KERNELS:
         return profile_run_lmhead(name, M)
     wl = {w.name: w for w in (W.C2, W.C3, W.C4, W.C7, W.C9, W.C10, W.C12)}[name]
@@ -410,6 +495,56 @@ def profile_run(key):
                                                                       PROFILE_CALLS))
     print("algorithmic bytes per launch: %.0f (mean union %.2f experts)" % (alg, sum(U) / len(U)),
           flush=True)
+
+
+def profile_run_prefetch(name):
+    """One reference copy, PROFILE_CALLS cold Ling layer launches at M=1 to learn
+    each call's routing, then PROFILE_CALLS pairs of (moe_expert_prefetch of that
+    call's 8 routed experts and the shared expert, the layer launch), rotating over
+    16 distinct layers."""
+    import numpy as np
+    import torch
+
+    import benchsupport as bs
+    import moe_decode_amd as md
+    from datagen import device as D
+    from datagen import workloads as W
+
+    wl = W.C2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layers = [D.make_layer(wl, l) for l in range(N_LAYERS)]
+    lws = [md.layer_weights(L.w_router, L.w_gate_up, L.w_down) for L in layers]
+    d = md.dims(wl.H, wl.E, wl.K, wl.I, wl.S, wl.routed_scale)
+    ws = md.new_workspace(d, 1, 1)
+    xs = torch.stack([D.to_device(W.x_rows(wl, [s])) for s in range(PROFILE_CALLS)])
+    out = torch.empty((1, wl.H), dtype=torch.int16, device=dev)
+    idx = torch.empty((PROFILE_CALLS, 1, wl.K), dtype=torch.int32, device=dev)
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    bs.copy(src, dst, 2048, torch.cuda.current_stream().cuda_stream)
+
+    def layer(i):
+        md.check(md.moe_layer_chain(d, 1, [lws[i % N_LAYERS]], xs[i], out, md.MOE_OUT_BF16,
+                                    md.MOE_CHAIN_LAYER_ONLY, idx[i], ws))
+
+    for i in range(PROFILE_CALLS):
+        layer(i)
+    torch.cuda.synchronize()
+    ids = torch.cat([idx.view(PROFILE_CALLS, wl.K),
+                     torch.full((PROFILE_CALLS, 1), wl.E, dtype=torch.int32, device=dev)], 1)
+    ids = ids.contiguous()
+    n = wl.K + wl.S
+    for i in range(PROFILE_CALLS):
+        md.check(md.moe_expert_prefetch(d, lws[i % N_LAYERS], ids[i], n))
+        layer(i)
+    torch.cuda.synchronize()
+    md.check(md.moe_last_device_status(ws))
+    print("profile run %s: 1 copy of %d bytes, %d prefetch + layer pairs" % (name, COPY_BYTES,
+                                                                            PROFILE_CALLS))
+    print("algorithmic bytes per launch: %.0f (%d experts, each once)"
+          % (n * wl.expert_bytes(), n), flush=True)
 
 
 def profile_run_lmhead(name, M):
@@ -524,8 +659,9 @@ def ingest_profiles(root):
         if alg:
             w["algorithmic_bytes_per_launch"] = alg
             lines.append("")
-            what = ("the V x H weight, once" if key in PROFILE_KERNELS
-                    else "router + union + shared expert, each once")
+            what = {"prefetch": "the 9 listed experts, each once"}.get(
+                key, "the V x H weight, once" if key in PROFILE_KERNELS
+                else "router + union + shared expert, each once")
             lines.append("algorithmic bytes per launch (%s): %.3f MB" % (what, alg / 1e6))
             if "bytes_per_launch" in w:
                 lines.append("measured HBM traffic / algorithmic bytes: %.4f"
@@ -544,7 +680,8 @@ def ingest_profiles(root):
 def kernel_source_sha():
     import hashlib
     h = hashlib.sha256()
-    for f in ("moe_device.hpp", "moe_layer.hpp", "moe_lmhead.hpp", "moe_capi.hip"):
+    for f in ("moe_device.hpp", "moe_layer.hpp", "moe_lmhead.hpp", "moe_prefetch.hpp",
+              "moe_capi.hip"):
         with open(os.path.join(ROOT, "moe_decode_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -17,7 +17,9 @@
  *          bitmap placement) and "AMD Low-Latency Kernels" (step-tagged values,
  *          a deadline on every wait, routing-independent weights loaded early).
  *  [MUSE]  "Muse Spark Open Ultrafast: Pushing beyond 1,000 Tokens per second",
- *          section "Speculative decoding" (the target verifies 16 tokens per step).
+ *          sections "Speculative decoding" (the target verifies 16 tokens per step)
+ *          and "Megakernel internals" (prefetching weights into the caches;
+ *          speculative expert prefetching).
  *
  * Conventions for every call:
  *  - Tensor pointers are DEVICE pointers owned by the caller, row-major and
@@ -125,6 +127,7 @@ enum {
 #define MOE_MAX_LAYERS 64
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16
+#define MOE_MAX_PREFETCH_IDS 4096
 
 /* Bytes of workspace needed for calls with up to `max_rows` rows and up to
  * `n_layers` chained layers (use n_layers = 1 for the single-layer calls).
@@ -211,6 +214,26 @@ int moe_layer_chain(const moe_dims* dims, int32_t M, int32_t n_layers,
  *   different orders, so max_logit can differ in its last bits between them. */
 int lmhead_argmax(int32_t M, int32_t H, int32_t V, const uint16_t* h, const uint16_t* w_lm,
                   int32_t* token, float* max_logit, void* ws, size_t ws_bytes, void* stream);
+
+/* Speculative expert prefetch: read the gate/up and down weights (and, for fp8
+ * experts, their block scales) of the experts listed in expert_ids into the
+ * device caches, so that a later call on the same weights finds them there.
+ * Consecutive decode steps tend to route alike, so the experts a layer chose on
+ * the previous step are the natural guess, issued while other work (attention)
+ * runs.  [MUSE] "Megakernel internals": speculative expert prefetching.  On
+ * MI355X the level that holds a layer's experts is the 256 MB Infinity Cache
+ * shared by all XCDs (an XCD's L2 is 4 MB).  The call computes and writes
+ * nothing: every result of a later call is the same with or without it.
+ *   dims, w: the layer's shape and weights (as for moe_experts_fused; the router
+ *       fields are ignored);
+ *   expert_ids [n] int32 device pointer, 4-byte aligned: ids in [0, E) name routed
+ *       experts, E the shared expert (when S = 1); an id outside [0, E+S) is
+ *       skipped without error (a guess is a hint);
+ *   0 <= n <= MOE_MAX_PREFETCH_IDS; n = 0 enqueues nothing.
+ * Needs no workspace.  Returns MOE_OK, or MOE_E_ARG / MOE_E_ALIGN /
+ * MOE_E_UNSUPPORTED / MOE_E_HIP with nothing enqueued (MOE_E_HIP: launch). */
+int moe_expert_prefetch(const moe_dims* dims, const moe_layer_weights* w,
+                        const int32_t* expert_ids, int32_t n, void* stream);
 
 /* Synchronise `stream`, return the sticky device status recorded in the
  * workspace (MOE_OK, MOE_E_TIMEOUT or MOE_E_INDEX) and clear it. */

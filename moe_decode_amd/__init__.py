@@ -46,12 +46,13 @@ MOE_EXPERT_FP8_B128 = 1
 
 MOE_MAX_ROWS = 16
 MOE_MAX_LAYERS = 64
+MOE_MAX_PREFETCH_IDS = 4096
 
 DBG_NO_ROUTER_PUBLISH = 1
 
 EXPORTED = ("moe_workspace_size", "moe_workspace_init", "moe_router_topk", "moe_experts_fused",
-            "moe_layer_chain", "lmhead_argmax", "moe_last_device_status",
-            "moe_workspace_debug", "moe_status_str")
+            "moe_layer_chain", "lmhead_argmax", "moe_expert_prefetch",
+            "moe_last_device_status", "moe_workspace_debug", "moe_status_str")
 
 
 class moe_dims(ctypes.Structure):
@@ -88,6 +89,9 @@ _lib.moe_layer_chain.argtypes = [ctypes.POINTER(moe_dims), _I32, _I32,
                                  _P, _SZ, _P]
 _lib.lmhead_argmax.restype = ctypes.c_int
 _lib.lmhead_argmax.argtypes = [_I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]
+_lib.moe_expert_prefetch.restype = ctypes.c_int
+_lib.moe_expert_prefetch.argtypes = [ctypes.POINTER(moe_dims), ctypes.POINTER(moe_layer_weights),
+                                     _P, _I32, _P]
 _lib.moe_last_device_status.restype = ctypes.c_int
 _lib.moe_last_device_status.argtypes = [_P, _SZ, _P]
 _lib.moe_workspace_debug.restype = ctypes.c_int
@@ -195,6 +199,12 @@ def moe_layer_chain(d, M, layers, x_in, out, out_dtype, mode, topk_idx_all, ws, 
 def lmhead_argmax(M, H, V, h, w_lm, token, max_logit, ws, ws_bytes=None, stream=None):
     return _lib.lmhead_argmax(M, H, V, _ptr(h), _ptr(w_lm), _ptr(token), _ptr(max_logit),
                               _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream))
+
+
+def moe_expert_prefetch(d, w, expert_ids, n, stream=None):
+    return _lib.moe_expert_prefetch(ctypes.byref(d) if d is not None else None,
+                                    ctypes.byref(w) if w is not None else None, _ptr(expert_ids),
+                                    n, _stream(stream))
 
 
 def moe_last_device_status(ws, ws_bytes=None, stream=None):

@@ -17,6 +17,7 @@
 #include "../../include/moe_decode.h"
 #include "moe_layer.hpp"
 #include "moe_lmhead.hpp"
+#include "moe_prefetch.hpp"
 
 using namespace moe;
 
@@ -517,6 +518,47 @@ int lmhead_argmax(int32_t M, int32_t H, int32_t V, const uint16_t* h, const uint
   }
   if (G < 1) G = 1;
   hipLaunchKernelGGL(kern, dim3(G), dim3(MOE_LM_WG), lds, (hipStream_t)stream, p);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
+int moe_expert_prefetch(const moe_dims* dims, const moe_layer_weights* w,
+                        const int32_t* expert_ids, int32_t n, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!w || !w->w_gate_up || !w->w_down || n < 0) return MOE_E_ARG;
+  if (n > MOE_MAX_PREFETCH_IDS) return MOE_E_UNSUPPORTED;
+  if (n > 0 && !expert_ids) return MOE_E_ARG;
+  if (!aligned16(w->w_gate_up) || !aligned16(w->w_down) || !aligned4(expert_ids))
+    return MOE_E_ALIGN;
+  rc = check_expert_scales(*dims, *w);
+  if (rc) return rc;
+  if (n == 0) return MOE_OK;
+  const moe_dims& d = *dims;
+  const bool fp8 = d.expert_format == MOE_EXPERT_FP8_B128;
+  const uint64_t H = (uint64_t)d.hidden, I = (uint64_t)d.inter, wb = fp8 ? 1 : 2;
+  PrefetchParams p;
+  p.wgu = (const uint8_t*)w->w_gate_up;
+  p.wd = (const uint8_t*)w->w_down;
+  p.sgu = (const uint8_t*)w->s_gate_up;
+  p.sd = (const uint8_t*)w->s_down;
+  p.gu_bytes = 2 * I * H * wb;
+  p.d_bytes = H * I * wb;
+  p.sgu_bytes = fp8 ? (2 * I / 128) * (H / 128) * 4 : 0;
+  p.sd_bytes = fp8 ? (H / 128) * (I / 128) * 4 : 0;
+  // H is a multiple of 256 (check_dims), so every row block is whole 16-byte chunks
+  const uint64_t units = p.gu_bytes / 16 + p.d_bytes / 16 + p.sgu_bytes / 4 + p.sd_bytes / 4;
+  if (units >= (1ull << 31)) return MOE_E_UNSUPPORTED;
+  p.u_gu = (uint32_t)(p.gu_bytes / 16);
+  p.u_d = (uint32_t)(p.d_bytes / 16);
+  p.u_sgu = (uint32_t)(p.sgu_bytes / 4);
+  p.u_sd = (uint32_t)(p.sd_bytes / 4);
+  p.ids = expert_ids;
+  p.n_valid = d.n_experts + d.n_shared;
+  const uint64_t per_block = (uint64_t)kPrefetchWG * kPrefetchBatch;
+  uint64_t gx = (p.u_gu + p.u_d + per_block - 1) / per_block;
+  if (gx > 4096) gx = 4096;
+  hipLaunchKernelGGL(moe_prefetch_kernel, dim3((unsigned)gx, (unsigned)n), dim3(kPrefetchWG), 0,
+                     (hipStream_t)stream, p);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
 }
 

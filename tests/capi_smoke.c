@@ -59,6 +59,8 @@ int main(void) {
   CHECK(moe_layer_chain(&d, 1, 2, &w, hp, A, MOE_OUT_BF16, MOE_CHAIN_LAYER_ONLY, NULL, NULL, A,
                         big, NULL) == MOE_E_UNSUPPORTED);
   CHECK(lmhead_argmax(1, 2560, 0, hp, hp, ip, NULL, A, big, NULL) == MOE_E_ARG);
+  CHECK(moe_expert_prefetch(&d, &w, ip, -1, NULL) == MOE_E_ARG);
+  CHECK(moe_expert_prefetch(&d, &w, NULL, 0, NULL) == MOE_OK);
   CHECK(strcmp(moe_status_str(MOE_E_TIMEOUT), "device wait passed its deadline") == 0);
   printf("ok\n");
   return 0;

@@ -214,6 +214,33 @@ def test_lmhead_validation():
     assert f(1, 2560, 100, A, A, A, A + 2, A, big, stream=0) == md.MOE_E_ALIGN
 
 
+def test_expert_prefetch_validation():
+    """The prefetch hint validates like the expert call; n = 0 enqueues nothing."""
+    d16 = md.dims(**LING)
+    d8 = md.dims(**LING, expert_format=md.MOE_EXPERT_FP8_B128)
+    f = md.moe_expert_prefetch
+    w = md.layer_weights(0, A, A)
+    assert f(None, w, A, 1, stream=0) == md.MOE_E_ARG
+    assert f(d16, None, A, 1, stream=0) == md.MOE_E_ARG
+    assert f(d16, md.layer_weights(0, 0, A), A, 1, stream=0) == md.MOE_E_ARG
+    assert f(d16, md.layer_weights(0, A, 0), A, 1, stream=0) == md.MOE_E_ARG
+    assert f(d16, w, A, -1, stream=0) == md.MOE_E_ARG
+    assert f(d16, w, None, 1, stream=0) == md.MOE_E_ARG
+    assert f(d16, w, A, md.MOE_MAX_PREFETCH_IDS + 1, stream=0) == md.MOE_E_UNSUPPORTED
+    assert f(d16, w, A + 2, 1, stream=0) == md.MOE_E_ALIGN
+    assert f(d16, md.layer_weights(0, BAD, A), A, 1, stream=0) == md.MOE_E_ALIGN
+    assert f(d16, md.layer_weights(0, A, BAD), A, 1, stream=0) == md.MOE_E_ALIGN
+    assert f(d8, w, A, 1, stream=0) == md.MOE_E_ARG                      # fp8 needs scales
+    assert f(d16, md.layer_weights(0, A, A, s_gate_up=A, s_down=A), A, 1,
+             stream=0) == md.MOE_E_ARG                                    # bf16 takes none
+    assert f(d8, md.layer_weights(0, A, A, s_gate_up=A, s_down=A + 2), A, 1,
+             stream=0) == md.MOE_E_ALIGN
+    assert f(md.dims(**dict(LING, hidden=2500)), w, A, 1, stream=0) == md.MOE_E_UNSUPPORTED
+    # an empty list is a valid no-op and reaches no device
+    assert f(d16, w, None, 0, stream=0) == md.MOE_OK
+    assert f(d8, md.layer_weights(0, A, A, s_gate_up=A, s_down=A), A, 0, stream=0) == md.MOE_OK
+
+
 def test_workspace_calls_validate_before_touching_the_device():
     assert md.moe_workspace_init(None, 1 << 20, stream=0) == md.MOE_E_WORKSPACE
     assert md.moe_workspace_init(BAD, 1 << 20, stream=0) == md.MOE_E_ALIGN
