@@ -58,11 +58,13 @@ PROFILE_WORKLOADS = {"m1": ("ling_moe_layer_m1", 1, False),
                      "fp8m1": ("ling_fp8_moe_layer_m1", 1, False),
                      "fp8m6": ("ling_fp8_moe_layer_m6", 6, False),
                      "m16": ("ling_moe_layer_m16", 16, False),
+                     "lmhead1": ("lmhead_v157184_m1", 1, False),
                      "lmhead": ("lmhead_v157184_m6", 6, False),
                      "lmhead16": ("lmhead_v157184_m16", 16, False),
                      "prefetch": ("ling_moe_layer_m1_prefetch", 1, False)}
 # kernel profiled by each workload (the layer kernel unless named here)
-PROFILE_KERNELS = {"lmhead": "moe_lmhead_kernel", "lmhead16": "moe_lmhead_mfma_kernel",
+PROFILE_KERNELS = {"lmhead1": "moe_lmhead_kernel", "lmhead": "moe_lmhead_mfma_kernel",
+                   "lmhead16": "moe_lmhead_mfma_kernel",
                    "prefetch": "moe_prefetch_kernel"}
 COPY_BYTES = 256 << 20   # reference copy for the counter scale
 PROFILE_CALLS = 64
@@ -411,7 +413,7 @@ def time_prefetch(md, np, torch, dev, wl, lws, xs, calls=160, warmup=16):
 
 def time_lmhead(md, D, W, np, torch, dev, rows=(1, 6, 16), calls=30, warmup=3):
     """The lm_head argmax alone (V = 157184, H = 2560), back-to-back calls at each
-    row count: the dot-product kernel up to 8 rows, the matrix-core kernel above.
+    row count: the dot-product kernel for 1 or 2 rows, the matrix-core kernel above.
     The 805 MB matrix exceeds every cache, so every call streams it from HBM."""
     wl = W.C5
     lm = D.make_lmhead(wl)

@@ -204,13 +204,13 @@ int moe_layer_chain(const moe_dims* dims, int32_t M, int32_t n_layers,
  * [LING] "bf16 router gate and lm_head"; greedy decoding.
  *   h [M][H] bf16; w_lm [V][H] bf16; token [M] int32 (out);
  *   max_logit [M] fp32 (out, optional; the z[m][token[m]] found).
- *   1 <= M <= MOE_MAX_ROWS, V >= 1, H a multiple of 256; up to 8 rows H / 256
+ *   1 <= M <= MOE_MAX_ROWS, V >= 1, H a multiple of 256; for 1 or 2 rows H / 256
  *   must be 1, 2, 4, 8 or 10 (MOE_E_UNSUPPORTED otherwise).  token and
  *   max_logit 4-byte aligned.
  *   ws: any workspace from moe_workspace_size() (the lm_head uses only its
  *   header: step tags, counters and one slot per workgroup), ws_bytes its size.
- *   Up to 8 rows the sums are formed by vector dot products, from 9 rows on by
- *   the matrix cores (16-row vocabulary tiles); both accumulate in fp32 but in
+ *   For 1 or 2 rows the sums are formed by vector dot products, from 3 rows on
+ *   by the matrix cores (16-row vocabulary tiles); both accumulate in fp32 but in
  *   different orders, so max_logit can differ in its last bits between them. */
 int lmhead_argmax(int32_t M, int32_t H, int32_t V, const uint16_t* h, const uint16_t* w_lm,
                   int32_t* token, float* max_logit, void* ws, size_t ws_bytes, void* stream);

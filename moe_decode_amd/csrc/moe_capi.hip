@@ -148,13 +148,11 @@ LmKern pick_lm_kernel_mm(int cplh) {
 }
 LmKern pick_lm_kernel(int cplh, int M) { return M <= 8 ? pick_lm_kernel_mm<8>(cplh) : nullptr; }
 // The matrix-core lm_head from this many token rows on (H a multiple of 256).
-// Up to 8 rows the dot-product kernel streams faster (its half-wave rows read
-// 512 contiguous bytes per instruction, the matrix-core tiles 16 rows x 64
-// bytes): 120 against 166 us at M = 1, 142 against 170 us at M = 6, even at
-// M = 8; at M = 16 the dot products bind it (278-294 us) and the matrix cores
-// take 173 us.
+// Its time hardly depends on the row count (V = 157184, H = 2560: 122-127 us
+// from 2 to 8 rows, 134 us at 16), while the dot products grow with it
+// (119 us at one row, 122 at two, 125 at three, 141 at six, 167 at eight).
 #ifndef MOE_LM_MFMA_ROWS
-#define MOE_LM_MFMA_ROWS 9
+#define MOE_LM_MFMA_ROWS 3
 #endif
 LmKern pick_lm_mfma_kernel(int H) {
   const int sc = H >> 6;  // 64-element super-chunks per row

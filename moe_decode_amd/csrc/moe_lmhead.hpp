@@ -227,49 +227,71 @@ __global__ __launch_bounds__(MOE_LM_WG, 1) void moe_lmhead_mfma_kernel(LmParams 
   const long long gw = (long long)g * MOE_LM_WAVES + wv;
   const int t0 = (int)(gw * NT / NW), t1 = (int)((gw + 1) * NT / NW);
   const int S = (t1 - t0) * NBT;           // batches of this wave
+  // Loads read whole 128-byte lines: lane l takes row l & 7 of a half tile and
+  // 16-byte chunk l >> 3 of each 128-byte super-chunk (w[2c]: rows 0-7 of the
+  // tile, w[2c + 1]: rows 8-15).  In the matrix instruction lane l is row
+  // l % 16 of k-group l / 16, so that register holds, for matrix rows i < 8,
+  // row i at chunk 2g and, for i >= 8, row i - 8 at chunk 2g + 1.  Each
+  // register therefore feeds two products, one with x at the even chunks
+  // (valid in matrix rows 0-7) and one at the odd chunks (valid in rows 8-15);
+  // the two halves of a row are added at the end of the tile.  Every row sums
+  // the same chunks in the same order.
+  const int i8 = lane & 7, c8 = lane >> 3;
   const int i16 = lane & 15, q = lane >> 4;
-  const uint16_t* xr = xs + (i16 < M ? i16 : 0) * XS + 8 * q;
+  const uint16_t* xr = xs + (i16 < M ? i16 : 0) * XS + 16 * q;
 
   auto load = [&](uint4 (&w)[2 * NB], int s) __attribute__((always_inline)) {
     const int tl = s / NBT, bt = s - tl * NBT;
-    const int v = 16 * (t0 + tl) + i16;
-    const uint4* row = reinterpret_cast<const uint4*>(p.w + (size_t)(v < V ? v : V - 1) * H) +
-                       (size_t)bt * NB * 8 + q;
+    const int va = 16 * (t0 + tl) + i8, vb = va + 8;
+    const uint4* ra = reinterpret_cast<const uint4*>(p.w + (size_t)(va < V ? va : V - 1) * H) +
+                      (size_t)bt * NB * 8 + c8;
+    const uint4* rb = reinterpret_cast<const uint4*>(p.w + (size_t)(vb < V ? vb : V - 1) * H) +
+                      (size_t)bt * NB * 8 + c8;
 #pragma unroll
     for (int c = 0; c < NB; ++c) {
-      w[2 * c] = ld_weight(row + 8 * c);
-      w[2 * c + 1] = ld_weight(row + 8 * c + 4);
+      w[2 * c] = ld_weight(ra + 8 * c);
+      w[2 * c + 1] = ld_weight(rb + 8 * c);
     }
   };
-  f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+  const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4 ae = zero4, ao = zero4, be = zero4, bo = zero4;
   uint64_t best = 0ull;
   auto mul = [&](const uint4 (&w)[2 * NB], int s) __attribute__((always_inline)) {
     const int tl = s / NBT, bt = s - tl * NBT;
 #pragma unroll
     for (int c = 0; c < NB; ++c) {
       const uint16_t* xb = xr + 64 * (bt * NB + c);
-      const uint4 b0 = *reinterpret_cast<const uint4*>(xb);
-      const uint4 b1 = *reinterpret_cast<const uint4*>(xb + 32);
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w[2 * c]),
-                                                      __builtin_bit_cast(bf16x8, b0), acc0, 0, 0,
-                                                      0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w[2 * c + 1]),
-                                                      __builtin_bit_cast(bf16x8, b1), acc1, 0, 0,
-                                                      0);
+      const bf16x8 xe = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xb));
+      const bf16x8 xo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xb + 8));
+      const bf16x8 wa = __builtin_bit_cast(bf16x8, w[2 * c]);
+      const bf16x8 wb = __builtin_bit_cast(bf16x8, w[2 * c + 1]);
+      ae = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xe, ae, 0, 0, 0);
+      ao = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xo, ao, 0, 0, 0);
+      be = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, xe, be, 0, 0, 0);
+      bo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb, xo, bo, 0, 0, 0);
     }
     if (bt == NBT - 1) {
-      // tile done: lane l holds rows 4q .. 4q + 3 of the tile for token row l % 16
+      // tile done.  Lane l holds matrix rows 4q .. 4q + 3 of column l % 16:
+      // even-chunk sums of half-tile rows 4q + j for q < 2, odd-chunk sums of
+      // rows 4(q - 2) + j for q >= 2; lanes l and l ^ 32 add their halves.
+      // Lanes q < 2 then report tile rows 4q + j, lanes q >= 2 rows 8 + 4(q - 2) + j.
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int v = 16 * (t0 + tl) + 4 * q + j;
-        const float z = acc0[j] + acc1[j];
+        const float pa = q < 2 ? ae[j] : ao[j];
+        const float pb = q < 2 ? be[j] : bo[j];
+        const float za = pa + __shfl_xor(pa, 32);
+        const float zb = pb + __shfl_xor(pb, 32);
+        const float z = q < 2 ? za : zb;
+        const int v = 16 * (t0 + tl) + (q < 2 ? 4 * q + j : 8 + 4 * (q - 2) + j);
         if (i16 < M && v < V) {
           const uint64_t k = lm_key(z, v);
           best = k > best ? k : best;
         }
       }
-      acc0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      acc1 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      ae = zero4;
+      ao = zero4;
+      be = zero4;
+      bo = zero4;
     }
   };
   // two batches in flight: the steady-state loop issues its loads

@@ -208,8 +208,8 @@ def test_lmhead_validation():
     assert f(1, 2560, 100, A, A, A, None, A, 100, stream=0) == md.MOE_E_WORKSPACE
     assert f(1, 2560, 100, BAD, A, A, None, A, big, stream=0) == md.MOE_E_ALIGN
     assert f(1, 2500, 100, A, A, A, None, A, big, stream=0) == md.MOE_E_UNSUPPORTED
-    # up to 8 rows the dot-product kernel is built for H / 256 in {1, 2, 4, 8, 10}
-    assert f(8, 768, 100, A, A, A, None, A, big, stream=0) == md.MOE_E_UNSUPPORTED
+    # for 1 or 2 rows the dot-product kernel is built for H / 256 in {1, 2, 4, 8, 10}
+    assert f(2, 768, 100, A, A, A, None, A, big, stream=0) == md.MOE_E_UNSUPPORTED
     assert f(1, 2560, 100, A, A, A + 2, None, A, big, stream=0) == md.MOE_E_ALIGN
     assert f(1, 2560, 100, A, A, A, A + 2, A, big, stream=0) == md.MOE_E_ALIGN
 

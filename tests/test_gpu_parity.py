@@ -432,7 +432,7 @@ def test_chain16_lmhead_full_size(gpu, dw):
 
 # ------------------------------------------------------------------ lm_head
 
-@pytest.mark.parametrize("M,V", [(1, 1), (3, 4097), (8, 20000)])
+@pytest.mark.parametrize("M,V", [(1, 1), (2, 4097), (3, 4097), (8, 20000)])
 def test_lmhead_ragged_and_planted_ties(gpu, M, V):
     import torch
     wl = W.C5

@@ -174,10 +174,11 @@ def test_lmhead_m16(gpu, V):
     assert np.all(np.abs(mx.cpu().numpy() - m_ref) <= 1e-4 * np.abs(m_ref) + 1e-5)
 
 
-@pytest.mark.parametrize("wl,M,V", [(W.C5, 9, 4097), (W.C5, 12, 157), (W.C1, 12, 1000),
+@pytest.mark.parametrize("wl,M,V", [(W.C5, 3, 4097), (W.C5, 6, 20001), (W.C5, 9, 4097),
+                                    (W.C5, 12, 157), (W.C1, 4, 33), (W.C1, 12, 1000),
                                     (W.C1, 16, 17)])
 def test_lmhead_matrix_cores_ragged(gpu, wl, M, V):
-    """From 9 token rows the lm_head runs on the matrix cores (16-row tiles):
+    """From 3 token rows the lm_head runs on the matrix cores (16-row tiles):
     ragged vocabularies (a partial last tile), hidden sizes of 40 and 4
     super-chunks, and a planted exact tie that the lower index must win."""
     import torch
