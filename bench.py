@@ -237,6 +237,16 @@ def main():
         print("chain16+lm_head M=6: %.1f us (floor %.1f us, ratio %.2f)"
               % (c["us_per_step"], c["floor_us_at_peak"], c["ratio_to_floor"]),
               file=sys.stderr, flush=True)
+        # one token row through the same 16-layer chain: the per-layer cost when
+        # the launch is paid once per step, not once per layer
+        from dataclasses import replace as _replace
+        wl1 = _replace(W.C5, name="ling_chain16_lmhead_m1", M=1)
+        c1 = time_chain(md, D, W, np, torch, dev, lw, steps=10, warmup=2, wl=wl1)
+        c1["chain_us_per_layer"] = c1["chain_us"] / wl1.n_layers
+        secondary[wl1.name] = c1
+        print("chain16+lm_head M=1: %.1f us (chain %.1f us = %.2f us per layer, lm_head %.1f us)"
+              % (c1["us_per_step"], c1["chain_us"], c1["chain_us_per_layer"], c1["lmhead_us"]),
+              file=sys.stderr, flush=True)
         lmr = time_lmhead(md, D, W, np, torch, dev)
         secondary["lmhead_v%d" % W.C5.V] = lmr
         print("lm_head alone: " + ", ".join("M=%s %.1f us (%.0f GB/s)" % (k[2:], v["us"], v["gbs"])
