@@ -131,3 +131,27 @@ def test_prefetch_whole_ling_layer_on_a_side_stream(gpu, dw):
     _layer(d, lw, x, out1, idx, ws, 1)
     md.check(md.moe_last_device_status(ws))
     assert torch.equal(out0, out1)
+
+
+def test_prefetch_without_a_shared_expert(gpu, dw):
+    """S = 0: id E names no expert and is skipped; the layer without a shared
+    expert gives the same result with and without the prefetch."""
+    import torch
+    from datagen import device as D
+    wl = W.C1
+    M = 2
+    L = dw.layer(wl, 0)
+    d = md.dims(hidden=wl.H, n_experts=wl.E, top_k=wl.K, inter=wl.I, n_shared=0)
+    lw = md.layer_weights(L.w_router, L.w_gate_up, L.w_down)
+    x = D.to_device(x_tiefree(wl, M))
+    ws = md.new_workspace(d, M, 1)
+    out0 = torch.empty((M, wl.H), dtype=torch.int16, device=gpu)
+    out1 = torch.empty_like(out0)
+    idx = torch.empty((M, wl.K), dtype=torch.int32, device=gpu)
+    say("prefetch: tiny layer without a shared expert, M=2")
+    _layer(d, lw, x, out0, idx, ws, M)
+    vals = [wl.E, 0, wl.E - 1, wl.E + 1]
+    md.check(md.moe_expert_prefetch(d, lw, _ids(gpu, vals), len(vals)))
+    _layer(d, lw, x, out1, idx, ws, M)
+    md.check(md.moe_last_device_status(ws))
+    assert torch.equal(out0, out1)
