@@ -179,6 +179,10 @@ def main():
                  r["hit75"]["layer_us_mean"], r["hit0"]["layer_us_mean"],
                  r["hit100"]["prefetch_us_mean"], r["hit100"]["prefetch_gbs"]),
               file=sys.stderr, flush=True)
+        print("%s: back-to-back %.1f us per layer, %.1f us with the next call's experts "
+              "prefetched on a second stream during each call"
+              % (name, r["pipelined_no_prefetch_us_per_layer"],
+                 r["pipelined_prefetch_next_us_per_layer"]), file=sys.stderr, flush=True)
 
     if not args.no_secondary:
         report_prefetch(W.C2.name + "_prefetch",
@@ -418,6 +422,37 @@ def time_prefetch(md, np, torch, dev, wl, lws, xs, calls=160, warmup=16):
                       "prefetch_gbs": float(nb / (pf.mean() * 1e-6) / 1e9)})
         res[label] = r
     res["saving_us_at_hit100"] = res["cold"]["layer_us_mean"] - res["hit100"]["layer_us_mean"]
+
+    # Overlapped: the next call's experts (a correct guess, plus the shared expert)
+    # prefetched on a second stream while the current call runs; the next call
+    # waits for that prefetch.  Against the same loop with no prefetch.
+    nxt = np.full((n, max(len(c) for c in chosen) + wl.S), -1, dtype=np.int32)
+    for i, ch in enumerate(chosen):
+        row = np.concatenate([ch, np.arange(wl.E, wl.E + wl.S)])
+        nxt[i, :len(row)] = row
+    nxt = torch.from_numpy(nxt).to(dev)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    for label, with_pf in (("pipelined_no_prefetch", False), ("pipelined_prefetch_next", True)):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(n):
+            if i == warmup:
+                e0.record(main)
+            go = torch.cuda.Event()
+            go.record(main)
+            layer(i)
+            if with_pf and i + 1 < n:
+                side.wait_event(go)
+                md.check(md.moe_expert_prefetch(d, lws[(i + 1) % nl], nxt[i + 1], nxt.shape[1],
+                                                stream=side.cuda_stream))
+                done = torch.cuda.Event()
+                done.record(side)
+                main.wait_event(done)
+        e1.record(main)
+        torch.cuda.synchronize()
+        md.check(md.moe_last_device_status(ws))
+        res[label + "_us_per_layer"] = e0.elapsed_time(e1) * 1e3 / calls
     return res
 
 
