@@ -661,3 +661,177 @@ def test_fp8_combine_with_unit_scales_is_the_bf16_combine(rng):
         a8 = oracle.experts_combine_fp8(x, idx, gate, gu8, d8, wl.E, 1, scale)
         a = oracle.experts_combine(x, idx, gate, gu, d, wl.E, 1, scale)
         assert np.array_equal(a8, a)
+
+
+# ---------------------------------------------------------------- chain and router-front compositions
+#
+# runner.chain and runner.front_layer decide where the norm sits, what feeds the
+# router and the experts, and what the residual adds to.  They are pinned with
+# identity-like experts, whose layer output has a closed form (every sum has one
+# nonzero term), and with zero experts, whose chain must return its input.
+
+def _identity_experts(monkeypatch, H, I, E, shared_zero=True):
+    """Every routed expert: W_g = W_u = [I_I | 0], W_d = [I_I ; 0]; the shared one zero."""
+    eye_gu = np.zeros((2 * I, H))
+    eye_gu[np.arange(I), np.arange(I)] = 1.0
+    eye_gu[I + np.arange(I), np.arange(I)] = 1.0
+    eye_d = np.zeros((H, I))
+    eye_d[np.arange(I), np.arange(I)] = 1.0
+    gu_bits, d_bits = to_bf16_bits_exact(eye_gu), to_bf16_bits_exact(eye_d)
+
+    def gu(wl, layer, e):
+        return np.zeros((2 * I, H), np.uint16) if (e == E and shared_zero) else gu_bits
+
+    def dn(wl, layer, e):
+        return np.zeros((H, I), np.uint16) if (e == E and shared_zero) else d_bits
+
+    monkeypatch.setattr(W, "expert_gate_up", gu)
+    monkeypatch.setattr(W, "expert_down", dn)
+
+
+def _swiglu_self_closed_form(u, I):
+    """bf16(silu(u_n) * u_n) for n < I, 0 beyond: the identity-like top-1 layer output,
+    in float64 rounded once to bf16 (rare 1-ulp differences from the fp32 path)."""
+    uf = f32(u).astype(np.float64)
+    s = np.zeros_like(uf)
+    s[:, :I] = uf[:, :I] / (1.0 + np.exp(-uf[:, :I])) * uf[:, :I]
+    return bf16_bits_torch(s)
+
+
+def _tiny_front_wl(**kw):
+    from dataclasses import replace
+    a = dict(name="tiny_chain_pin", K=1, M=3, n_layers=3, residual=True, prenorm=True,
+             bias_sigma=0.0, gain_sigma=0.1, routed_scale=1.0)
+    a.update(kw)
+    return replace(W.C6, **a)
+
+
+def test_runner_chain_with_zero_experts_returns_its_input(monkeypatch):
+    """All expert weights zero: every layer adds an exact +-0, so h_L = x bit for bit,
+    with and without the pre-norm (and whatever the router chooses)."""
+    wl = _tiny_front_wl(K=2, bias_sigma=0.25, routed_scale=2.5)
+    monkeypatch.setattr(W, "expert_gate_up",
+                        lambda wl_, layer, e: np.zeros((2 * wl_.I, wl_.H), np.uint16))
+    monkeypatch.setattr(W, "expert_down",
+                        lambda wl_, layer, e: np.zeros((wl_.H, wl_.I), np.uint16))
+    x = W.x_rows(wl, [0, 1, 2])
+    for prenorm in (True, False):
+        h, per = runner.chain(wl, x, prenorm=prenorm)
+        assert np.array_equal(h, x)
+        assert len(per) == wl.n_layers
+        for r in per:
+            assert np.array_equal(r["h_in"], x)
+            assert np.all(r["acc"] == 0.0)
+
+
+def test_runner_chain_identity_experts_closed_form(monkeypatch):
+    """Identity-like top-1 experts with a zero shared expert and per-layer gains: layer l
+    must (i) norm h_l with layer l's gain, (ii) feed that u_l to the router (its logits)
+    and to the experts (acc = bf16(silu(u)*u) on the first I channels), and (iii) add acc
+    to h_l, not to u_l.  The input is scaled by 3, so u_l differs from h_l and each wrong
+    composition fails."""
+    wl = _tiny_front_wl()
+    _identity_experts(monkeypatch, wl.H, wl.I, wl.E)
+    x = bf16_bits_torch(f32(W.x_rows(wl, [0, 1, 2])).astype(np.float64) * 3.0)
+    h, per = runner.chain(wl, x)
+    assert np.array_equal(per[0]["h_in"], x)
+    close = 0
+    for l, r in enumerate(per):
+        hl = r["h_in"]
+        gain = W.norm_gain(wl, l)
+        # each layer has a gain of its own, so a gain taken from the wrong layer fails
+        assert gain is not None and np.any(gain != W.norm_gain(wl, (l + 1) % wl.n_layers))
+        u = oracle.rmsnorm(hl, gain=gain)
+        assert np.array_equal(r["u_in"], u)
+        assert not np.array_equal(u, hl)
+        # the router sees u (its logits), not h
+        assert np.array_equal(r["logits"], oracle.router_logits(u, W.router(wl, l)))
+        assert not np.allclose(r["logits"], oracle.router_logits(hl, W.router(wl, l)))
+        assert np.all(r["gate"] == 1.0)
+        # the experts see u: acc is the closed form of u (to one bf16 ulp where the
+        # float64 and fp32 roundings of silu(u)*u part)
+        ref = _swiglu_self_closed_form(u, wl.I)
+        acc_bits = bf16_bits_torch(r["acc"].astype(np.float64))
+        assert np.all(f32(acc_bits[:, wl.I:]) == 0.0)
+        same = acc_bits == ref
+        assert same.mean() > 0.97
+        assert np.all(np.abs(f32(acc_bits[~same]) - f32(ref[~same])) <=
+                      np.abs(f32(ref[~same])) * 2.0 ** -7)
+        # the residual adds acc to h_l (exact sums of two bf16 values, rounded once)
+        nxt = per[l + 1]["h_in"] if l + 1 < len(per) else h
+        want = bf16_bits_torch(f32(hl).astype(np.float64) + r["acc"].astype(np.float64))
+        close += int(np.sum(nxt == want))
+        assert np.mean(nxt == want) > 0.99
+        wrong = bf16_bits_torch(f32(u).astype(np.float64) + r["acc"].astype(np.float64))
+        assert np.mean(nxt == wrong) < 0.5
+    assert close > 0
+
+
+def test_runner_chain_one_layer_and_three_layers_by_hand():
+    """With real random weights, a selection bias, per-layer gains and a routed scale:
+    chain(L=1) = residual(x, layer(rmsnorm(x, gain_0)).acc), and three layers composed
+    by hand from the pinned oracle functions equal chain(L=3) bit for bit."""
+    wl = _tiny_front_wl(K=2, bias_sigma=0.25, routed_scale=2.5)
+    x = W.x_rows(wl, [0, 1, 2])
+    h1, per1 = runner.chain(wl, x, n_layers=1)
+    u0 = oracle.rmsnorm(x, gain=W.norm_gain(wl, 0))
+    idx, gate, _ = oracle.router_topk(u0, W.router(wl, 0), wl.K, W.router_bias(wl, 0))
+    gu = {e: W.expert_gate_up(wl, 0, e) for e in range(wl.E + 1)}
+    d = {e: W.expert_down(wl, 0, e) for e in range(wl.E + 1)}
+    acc = oracle.experts_combine(u0, idx, gate, gu, d, wl.E, wl.S, wl.routed_scale)
+    assert np.array_equal(per1[0]["idx"], idx)
+    assert np.array_equal(per1[0]["acc"], acc)
+    assert np.array_equal(h1, oracle.residual(x, acc))
+    # the residual must not be taken on u
+    assert not np.array_equal(h1, oracle.residual(u0, acc))
+    h = x
+    for l in range(3):
+        u = oracle.rmsnorm(h, gain=W.norm_gain(wl, l))
+        idx, gate, _ = oracle.router_topk(u, W.router(wl, l), wl.K, W.router_bias(wl, l))
+        gu = {e: W.expert_gate_up(wl, l, e) for e in range(wl.E + 1)}
+        d = {e: W.expert_down(wl, l, e) for e in range(wl.E + 1)}
+        h = oracle.residual(h, oracle.experts_combine(u, idx, gate, gu, d, wl.E, wl.S,
+                                                      wl.routed_scale))
+    h3, _ = runner.chain(wl, x, n_layers=3)
+    assert np.array_equal(h3, h)
+    # without the pre-norm the layers see h itself
+    h_plain, per_plain = runner.chain(wl, x, n_layers=1, prenorm=False)
+    idx, gate, _ = oracle.router_topk(x, W.router(wl, 0), wl.K, W.router_bias(wl, 0))
+    gu = {e: W.expert_gate_up(wl, 0, e) for e in range(wl.E + 1)}
+    d = {e: W.expert_down(wl, 0, e) for e in range(wl.E + 1)}
+    assert np.array_equal(h_plain, oracle.residual(
+        x, oracle.experts_combine(x, idx, gate, gu, d, wl.E, wl.S, wl.routed_scale)))
+
+
+def test_runner_front_layer_feeds_the_same_normed_input_to_router_and_experts(monkeypatch):
+    """front_layer: the router's logits are those of u = bf16(RMSNorm(x) * gain), and the
+    experts read u too: with identity-like experts, channels the gain zeroes come out 0
+    while the others follow the closed form of u.  With unit gain it is layer(rmsnorm(x))."""
+    from dataclasses import replace
+    wl = _tiny_front_wl(n_layers=1)
+    _identity_experts(monkeypatch, wl.H, wl.I, wl.E)
+    x = bf16_bits_torch(f32(W.x_rows(wl, [0, 1, 2])).astype(np.float64) * 3.0)
+    gain = np.array(W.norm_gain(wl, 0), copy=True)
+    gain[:8] = 0                                    # bf16 +0: these channels of u vanish
+    monkeypatch.setattr(W, "norm_gain", lambda wl_, layer=0: gain)
+    r = runner.front_layer(wl, x)
+    u = oracle.rmsnorm(x, gain=gain)
+    assert np.array_equal(r["u_in"], u)
+    assert np.array_equal(r["logits"], oracle.router_logits(u, W.router(wl, 0)))
+    acc_bits = bf16_bits_torch(r["acc"].astype(np.float64))
+    assert np.all(r["acc"][:, :8] == 0.0)
+    assert np.all(f32(x[:, :8]) != 0.0)                # x itself is nonzero there
+    ref = _swiglu_self_closed_form(u, wl.I)
+    assert np.mean(acc_bits == ref) > 0.97
+    # unit gain: front_layer is the plain layer on rmsnorm(x); a workload without the
+    # pre-norm passes x through unchanged
+    monkeypatch.undo()
+    wl1 = replace(_tiny_front_wl(n_layers=1, K=2, bias_sigma=0.25), gain_sigma=0.0)
+    x1 = W.x_rows(wl1, [0, 1, 2])
+    a = runner.front_layer(wl1, x1)
+    b = runner.layer(wl1, oracle.rmsnorm(x1))
+    assert np.array_equal(a["idx"], b["idx"]) and np.array_equal(a["acc"], b["acc"])
+    wl0 = replace(wl1, prenorm=False)
+    c = runner.front_layer(wl0, x1)
+    assert np.array_equal(c["u_in"], x1)
+    assert np.array_equal(c["acc"], runner.layer(wl0, x1)["acc"])
