@@ -67,3 +67,43 @@ def order_agrees(gpu_idx, ref_idx, logits, min_gap=1e-5):
             if min(lo, hi) >= min_gap and gpu_idx[m, k] != ref_idx[m, k]:
                 return False
     return True
+
+
+def free_running_report(wl, x, ids_gpu, h_gpu, tok_gpu, lm_host, routers=None, tag=""):
+    """Compare a free-running GPU chain with the oracle's free-running chain from the
+    same input rows (no teacher forcing): per row, the first layer whose selected expert
+    set differs, the norm-wise error of the final hidden state, and whether the greedy
+    tokens agree.  Reported, not gated: the method gives no error bound across a chain,
+    and a single bf16 ulp that flips one selection makes the two runs part ways.
+    The report is printed and, when MOE_RESULTS_DIR is set, written there as JSON."""
+    import oracle
+    from oracle import runner
+    h_ref, per = runner.chain(wl, x, routers=routers)
+    tok_ref, _ = oracle.lmhead_argmax(h_ref, lm_host)
+    rows = []
+    for m in range(x.shape[0]):
+        first = None
+        for l in range(len(per)):
+            if set(int(e) for e in ids_gpu[l, m]) != set(int(e) for e in per[l]["idx"][m]):
+                first = l
+                break
+        rows.append({"row": m, "first_selection_difference_layer": first,
+                     "h_final_rel_err_normwise": rel_err_normwise(f32(h_gpu[m]), f32(h_ref[m])),
+                     "token_gpu": int(tok_gpu[m]), "token_oracle": int(tok_ref[m]),
+                     "token_match": bool(int(tok_gpu[m]) == int(tok_ref[m]))})
+    rep = {"workload": wl.name, "layers": len(per), "rows": rows,
+           "rows_same_routing_all_layers": sum(r["first_selection_difference_layer"] is None
+                                               for r in rows),
+           "tokens_matching": sum(r["token_match"] for r in rows)}
+    for r in rows:
+        say("chain-drift %s%s row %d: first selection difference at layer %s, |h_L err| %.3e, "
+            "token %d vs oracle %d" % (wl.name, tag, r["row"],
+                                       r["first_selection_difference_layer"],
+                                       r["h_final_rel_err_normwise"], r["token_gpu"],
+                                       r["token_oracle"]))
+    out_dir = os.environ.get("MOE_RESULTS_DIR")
+    if out_dir:
+        os.makedirs(out_dir, exist_ok=True)
+        with open(os.path.join(out_dir, "chain_drift_%s%s.json" % (wl.name, tag)), "w") as f:
+            json.dump(rep, f, indent=1)
+    return rep

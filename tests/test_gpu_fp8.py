@@ -18,8 +18,8 @@ from oracle import runner
 from datagen import workloads as W
 from datagen import device as D
 
-from gpu_support import (f32, frac_beyond_one_ulp, order_agrees, rel_err_normwise, same_sets, say,
-                         x_tiefree)
+from gpu_support import (f32, free_running_report, frac_beyond_one_ulp, order_agrees,
+                         rel_err_normwise, same_sets, say, x_tiefree)
 
 pytestmark = pytest.mark.gpu
 
@@ -245,3 +245,6 @@ def test_fp8_chain16_lmhead_full_size(gpu, dw):
     for m in range(M):
         if marg[m] >= 1e-4:
             assert got[m] == t_ref[m], (m, got[m], t_ref[m])
+    # the free-running comparison with the oracle's own 16-layer chain: reported only
+    rep = free_running_report(wl, x, ids, h, got, w_host)
+    assert len(rep["rows"]) == M

@@ -17,8 +17,8 @@ from oracle import runner
 from datagen import workloads as W
 from datagen import device as D
 
-from gpu_support import (f32, frac_beyond_one_ulp, order_agrees, rel_err_normwise, same_sets,
-                         say, tiefree_attempts, x_tiefree)
+from gpu_support import (f32, frac_beyond_one_ulp, free_running_report, order_agrees,
+                         rel_err_normwise, same_sets, say, tiefree_attempts, x_tiefree)
 
 pytestmark = pytest.mark.gpu
 
@@ -428,6 +428,9 @@ def test_chain16_lmhead_full_size(gpu, dw):
         if marg[m] >= 1e-4:
             assert got[m] == t_ref[m], (m, got[m], t_ref[m])
     assert np.all(np.abs(mx.cpu().numpy() - m_ref) <= 1e-4 * np.abs(m_ref) + 1e-5)
+    # the free-running comparison with the oracle's own 16-layer chain: reported only
+    rep = free_running_report(wl, x, idx, h, got, w_host, routers=routers)
+    assert len(rep["rows"]) == 6
 
 
 # ------------------------------------------------------------------ lm_head
