@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/moe_decode.h"
@@ -58,6 +59,41 @@ int device_info(DevInfo* out) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Per-workspace host state: the layer kernel's calls on a workspace are
+// counted here, and the count is the step tag of the next call (a launch
+// argument), so the kernel reads no control word before its first weight loads
+// and needs no end-of-call counting to advance the step.  Tags only grow (zero
+// is skipped), so no call can take a stale word of an earlier call on the same
+// workspace for its own.  moe_workspace_init resets the state with the memory;
+// moe_workspace_debug sets the flags and the deadline.
+struct WsState {
+  uint32_t epoch = 0;
+  uint32_t flags = 0;
+  uint32_t deadline = 0;  // 100 MHz ticks, 0 = default
+};
+std::mutex g_ws_mu;
+std::unordered_map<const void*, WsState> g_ws;
+
+struct CallTag {
+  uint32_t tag, flags, deadline;
+};
+
+CallTag next_call(const void* ws) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  WsState& st = g_ws[ws];
+  if (++st.epoch == 0) st.epoch = 1;
+  return CallTag{st.epoch, st.flags, st.deadline ? st.deadline : kDefaultDeadlineTicks};
+}
+
+// A launch that failed ran no kernel: its tag is given back, so that the tags
+// of the calls that did run stay consecutive (each call clears the input-read
+// counter of the other tag parity for the next one).
+void undo_call(const void* ws, uint32_t tag) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  WsState& st = g_ws[ws];
+  if (st.epoch == tag) st.epoch = tag - 1;
+}
 
 // Chunk plan of a row of `len` bf16 values split over `lpr` lanes, `cpl`
 // 16-byte loads per lane.
@@ -281,6 +317,10 @@ int launch_layer_nl(const moe_dims& d, int M, int L, uint32_t flags,
   p.flags = flags;
   p.nr_max = lp.nr_max;
   p.scale = d.routed_scale == 0.0f ? 1.0f : d.routed_scale;
+  const CallTag ct = next_call(ws);
+  p.tag = ct.tag;
+  p.dbg = ct.flags;
+  p.budget = ct.deadline;
   p.lds_xs = lp.xs;
   p.lds_lg = lp.lg;
   p.lds_hs = lp.hs;
@@ -313,7 +353,11 @@ int launch_layer_nl(const moe_dims& d, int M, int L, uint32_t flags,
     p.lw[l].sd = layers[l].s_down;
   }
   hipLaunchKernelGGL(kern, dim3(G), dim3(MOE_WG), lp.total, st, p);
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
+  if (hipGetLastError() != hipSuccess) {
+    undo_call(ws, p.tag);
+    return MOE_E_HIP;
+  }
+  return MOE_OK;
 }
 
 // Single-layer calls carry one weight slot in their (smaller, faster to
@@ -373,7 +417,10 @@ int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   if (!ws) return MOE_E_WORKSPACE;
   if (!aligned16(ws)) return MOE_E_ALIGN;
   if (ws_bytes < kHdrBytes) return MOE_E_WORKSPACE;
-  return hipMemsetAsync(ws, 0, ws_bytes, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_E_HIP;
+  if (hipMemsetAsync(ws, 0, ws_bytes, (hipStream_t)stream) != hipSuccess) return MOE_E_HIP;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  g_ws[ws] = WsState{};
+  return MOE_OK;
 }
 
 int moe_router_topk(const moe_dims* dims, int32_t M, const uint16_t* x, const uint16_t* w_router,
@@ -583,8 +630,14 @@ int moe_workspace_debug(void* ws, size_t ws_bytes, uint32_t flags, uint32_t dead
   hipStream_t st = (hipStream_t)stream;
   if (hipStreamSynchronize(st) != hipSuccess) return MOE_E_HIP;
   const uint32_t vals[2] = {flags, deadline_us * 100u};
+  // the lm_head reads its deadline from the workspace; the layer kernel takes
+  // both with its launch
   if (hipMemcpy((uint32_t*)ws + HDR_FLAGS, vals, 8, hipMemcpyHostToDevice) != hipSuccess)
     return MOE_E_HIP;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  WsState& state = g_ws[ws];
+  state.flags = flags;
+  state.deadline = deadline_us * 100u;
   return MOE_OK;
 }
 

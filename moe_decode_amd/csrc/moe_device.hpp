@@ -26,16 +26,13 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ---- workspace header (uint32 word offsets; hot words on separate 128 B lines)
 enum : int {
-  HDR_EPOCH = 0,        // calls completed on this workspace; tag of a call = epoch + 1
-  HDR_DONE = 32,        // workgroups finished in the running call
-  HDR_XREAD = 64,       // workgroups that finished reading x_in
+  HDR_XREAD0 = 32,      // layer calls with an even tag: workgroups that finished reading x_in
+  HDR_XREAD1 = 64,      // the same for odd tags (each call clears the other one for the next)
   HDR_STATUS = 96,      // sticky device status (moe_status)
   HDR_FLAGS = 128,      // debug flags
   HDR_DEADLINE = 129,   // wait budget in 100 MHz ticks (0 = default)
   HDR_LM_DONE = 160,    // lm_head: groups of workgroups finished
   HDR_LM_EPOCH = 192,   // lm_head: calls completed; tag of a call = epoch + 1
-  HDR_DONE_GRP = 224,   // end of call: workgroups finished per group of g % 8 (8 words, 32 apart)
-  HDR_DONE_ALL = 480,   // end of call: groups finished
   HDR_LM_DONE_GRP = 512,  // lm_head: workgroups finished per group of g % 8 (8 words, 32 apart)
   HDR_WORDS = 1024,     // control words: 4 KiB
   HDR_STAMPS = 1024,    // phase stamps: [256 workgroups][32] u64 after the control words

@@ -85,6 +85,9 @@ struct ParamsT {
   uint32_t flags;
   int nr_max;         // output rows owned by one workgroup, at most
   float scale;        // routed scaling factor of the combine
+  uint32_t tag;       // this call's step tag (never 0; the host counts the calls on a workspace)
+  uint32_t dbg;       // debug flags (DBG_*)
+  uint32_t budget;    // wait deadline, 100 MHz ticks
   // LDS byte offsets
   int lds_xs, lds_lg, lds_hs, lds_ysh, lds_ysr, lds_small;  // lds_hs: [3*M][I] bf16
   int lds_gn;         // [H] bf16 norm gain
@@ -107,6 +110,7 @@ struct ParamsT {
 
 struct Small {
   int nU, nP, abort_flag, pad;
+  int gu_next, dn_next, pad2[2];   // the workgroup's task tickets (gate/up, down)
   int tk_idx[kMaxPK];
   float tk_gate[kMaxPK];
   int upos[kMaxPK];          // routed slot of (row, rank), -1 if skipped
@@ -724,21 +728,22 @@ struct Piece {
   int r, j0, j1, n0, n1;
 };
 
+// (32-bit arithmetic: g, U <= 256 and a, b <= G, so every product stays below 2^31)
 __device__ __forceinline__ bool slice_piece(int g, int G, int U, int I, int H, int q, Piece& pc) {
   if (U <= 0) return false;
-  const long long s0 = (long long)g * U, s1 = (long long)(g + 1) * U;  // in units of 1/G
-  const int r = (int)(s0 / G) + q;
-  if ((long long)r * G >= s1 || r >= U) return false;
-  long long a = s0 - (long long)r * G, b = s1 - (long long)r * G;
+  const int s0 = g * U, s1 = (g + 1) * U;  // in units of 1/G
+  const int r = (int)((uint32_t)s0 / (uint32_t)G) + q;
+  if (r * G >= s1 || r >= U) return false;
+  int a = s0 - r * G, b = s1 - r * G;
   if (a < 0) a = 0;
   if (b > G) b = G;
   if (b <= a) return false;
-  const int I2 = I >> 1, H2 = H >> 1;
+  const uint32_t I2 = (uint32_t)I >> 1, H2 = (uint32_t)H >> 1, uG = (uint32_t)G;
   pc.r = r;
-  pc.j0 = 2 * (int)((a * I2 + G / 2) / G);
-  pc.j1 = 2 * (int)((b * I2 + G / 2) / G);
-  pc.n0 = 2 * (int)((a * H2 + G / 2) / G);
-  pc.n1 = 2 * (int)((b * H2 + G / 2) / G);
+  pc.j0 = 2 * (int)(((uint32_t)a * I2 + uG / 2) / uG);
+  pc.j1 = 2 * (int)(((uint32_t)b * I2 + uG / 2) / uG);
+  pc.n0 = 2 * (int)(((uint32_t)a * H2 + uG / 2) / uG);
+  pc.n1 = 2 * (int)(((uint32_t)b * H2 + uG / 2) / uG);
   return true;
 }
 
@@ -767,10 +772,12 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int NW = G * MOE_WAVES;
   const int gw = wv * G + g;  // consecutive wave ids land on different CUs
-  const uint32_t tag = ld_u32(p.hdr + HDR_EPOCH) + 1u;
-  const uint32_t dbg = ld_u32(p.hdr + HDR_FLAGS);
-  const uint32_t budget = ld_u32(p.hdr + HDR_DEADLINE);
-  Waiter wt{p.hdr, now_ticks() + (budget ? budget : kDefaultDeadlineTicks)};
+  // The step tag, debug flags and deadline come with the launch: no word of
+  // the workspace is read before the first weight loads are issued, and no
+  // end-of-call counting is needed to advance the step.
+  const uint32_t tag = p.tag;
+  const uint32_t dbg = p.dbg;
+  Waiter wt{p.hdr, now_ticks() + p.budget};
   const int M = p.M, H = p.H, I = p.I, K = p.K, S = p.S, E = p.E;
   const int I2 = I >> 1, H2 = H >> 1, I8 = I >> 3;
   const int MK = M * K;
@@ -778,6 +785,11 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
   const bool topk_in = (p.flags & F_TOPK_IN) != 0u;
 
   if (tid == 0) sm->abort_flag = 0;
+  // the input-read counter of this call's tag parity; the other one, which the
+  // next call on this workspace uses, is cleared now (the previous call that
+  // used it has completed)
+  const int xread = (tag & 1u) ? HDR_XREAD1 : HDR_XREAD0;
+  if (g == 0 && tid == 0) st_u32(p.hdr + ((tag & 1u) ? HDR_XREAD0 : HDR_XREAD1), 0u);
   uint64_t* stamps = ((dbg & DBG_STAMPS) && g < STAMP_WG)
                          ? reinterpret_cast<uint64_t*>(p.hdr + HDR_STAMPS) + (size_t)g * STAMP_SLOTS
                          : nullptr;
@@ -788,10 +800,16 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
   } while (0)
 
   // output rows owned by this workgroup (whole row pairs)
-  const int r0 = (int)(((long long)g * H2) / G), r1 = (int)(((long long)(g + 1) * H2) / G);
+  const int r0 = (int)((uint32_t)(g * H2) / (uint32_t)G);
+  const int r1 = (int)((uint32_t)((g + 1) * H2) / (uint32_t)G);
   const int n0 = 2 * r0, NR = 2 * (r1 - r0);
 
-  for (int l = 0; l < p.L; ++l) {
+  // A single-layer launch (one weight slot) has no layer loop: the compiler
+  // then tracks every load and store of the call exactly and waits only for
+  // the ones a value depends on, where a loop's back edge makes it wait for all
+  // of them (stores included) at many points.
+  const int L = NL == 1 ? 1 : p.L;
+  for (int l = 0; l < L; ++l) {
     // the thread number, opaque to the compiler: values derived from it are
     // made again in every layer instead of being hoisted out of the layer loop
     // and held in registers through every phase
@@ -799,7 +817,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     asm volatile("" : "+v"(tid_o));
     const int tid = tid_o;
     const int lane = tid & 63;
-    sbase = l == 0 ? 0 : (l == 1 ? 10 : (l == p.L - 1 ? 20 : -1));
+    sbase = l == 0 ? 0 : (l == 1 ? 10 : (l == L - 1 ? 20 : -1));
     MOE_STAMP(0);
     // ---------------- P1 prefetch: this wave's first router / shared gate-up rows
     // do not depend on x, so their loads fly while x is staged
@@ -814,6 +832,10 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     const uint16_t* gain = (p.flags & F_PRENORM) ? p.lw[l].gain : nullptr;
     uint4 gpre = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);  // bf16 ones
     if (gain && tid < (H >> 3)) gpre = reinterpret_cast<const uint4*>(gain)[tid];
+    if (tid == 0) {
+      sm->gu_next = 0;  // read after the barriers of the routing phase
+      sm->dn_next = 0;
+    }
     if (l == 0) {
       const uint4* src = reinterpret_cast<const uint4*>(p.x_in);
       uint4* dst = reinterpret_cast<uint4*>(xs);
@@ -825,7 +847,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
         sm->abort_flag = 1;
     }
     __syncthreads();
-    if (l == 0 && tid == 0 && (p.flags & F_ALIAS)) add_u32(p.hdr + HDR_XREAD, 1u);
+    if (l == 0 && tid == 0 && (p.flags & F_ALIAS)) add_u32(p.hdr + xread, 1u);
     if (sm->abort_flag) break;
     if (p.flags & F_RESIDUAL) {
       for (int i = tid; i < M * NR; i += MOE_WG) {
@@ -888,16 +910,9 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     }
     MOE_STAMP(2);
 
-    if (router_only) {
-      // the last workgroup to finish its rows computes the top-k
-      __syncthreads();
-      if (tid == 0) {
-        const uint32_t old = add_u32(p.hdr + HDR_DONE, 1u);
-        sm->abort_flag = (old == (uint32_t)(G - 1)) ? 2 : 3;
-      }
-      __syncthreads();
-      if (sm->abort_flag != 2) return;
-    }
+    // router only: workgroup 0 gathers every workgroup's logits and computes
+    // the top-k; the others are done
+    if (router_only && g != 0) return;
 
     // ---------------- P4: routing
     // one token row (K <= 8): the routed slots are the ranks (see P5)
@@ -1068,13 +1083,25 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
         }
       };
       // Tasks t = (slot, pair) over the whole union, dealt round-robin: workgroup
-      // g takes t = g, g + G, ..., its wave wv every WAVES-th of those.  Every
-      // workgroup then streams from every selected expert, which evens out the
-      // per-workgroup finish times far better than contiguous slices.
+      // g takes t = g, g + G, ...  Every workgroup then streams from every
+      // selected expert, which evens out the per-workgroup finish times far
+      // better than contiguous slices.  Inside the workgroup the waves take
+      // those tasks in order from a ticket counter in LDS: the two waves that
+      // share a SIMD do not issue at the same rate (the older one goes first),
+      // so a fixed deal per wave leaves half the waves a task or more behind.
+      // The next ticket is taken while the current task's rows are in flight.
       const int T = U * I2;
+      auto ticket = [&]() __attribute__((always_inline)) {
+        int v = 0;
+        if (lane == 0) v = atomicAdd(&sm->gu_next, 1);
+        return v;
+      };
       if constexpr (W8) {
         const size_t HB = (size_t)(H >> 7);
-        for (int t = g + G * wv; t < T; t += G * MOE_WAVES) {
+        int tk = ticket();
+        for (;;) {
+          const int t = g + G * __builtin_amdgcn_readfirstlane(tk);
+          if (t >= T) break;
           const int rr = t / I2;
           const int jp = t - rr * I2;
           const size_t j0 = 2 * (size_t)jp;
@@ -1084,10 +1111,14 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
           load_rows8<CPLH>(B, base + (j0 + 1) * H, base + ((size_t)I + j0 + 1) * H, H, lane);
           const float* sb = p.lw[l].sgu + (size_t)sm->uexp[so + rr] * ((2 * (size_t)I) >> 7) * HB;
           load_scales8<CPLH>(SC, sb + (j0 >> 7) * HB, sb + (((size_t)I + j0) >> 7) * HB, H, lane);
+          tk = ticket();
           emit_task(A, B, SC, jp, rr);
         }
       } else {
-        for (int t = g + G * wv; t < T; t += G * MOE_WAVES) {
+        int tk = ticket();
+        for (;;) {
+          const int t = g + G * __builtin_amdgcn_readfirstlane(tk);
+          if (t >= T) break;
           const int rr = t / I2;
           const int jp = t - rr * I2;
           const size_t j0 = 2 * (size_t)jp;
@@ -1095,6 +1126,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
                                  (size_t)sm->uexp[so + rr] * (2 * (size_t)I) * H;
           load_rows<CPLH>(A, base + j0 * H, base + ((size_t)I + j0) * H, lane);
           load_rows<CPLH>(B, base + (j0 + 1) * H, base + ((size_t)I + j0 + 1) * H, lane);
+          tk = ticket();
           emit_task(A, B, SC, jp, rr);
         }
       }
@@ -1174,12 +1206,18 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
           });
         }
       };
-      for (int f = wv; f < ntask; f += MOE_WAVES) {
+      // the down tasks, too, go to the waves in order from a ticket counter
+      int tk = 0;
+      if (lane == 0) tk = atomicAdd(&sm->dn_next, 1);
+      for (;;) {
+        const int f = __builtin_amdgcn_readfirstlane(tk);
+        if (f >= ntask) break;
         task(f, e, n, n_end, kind);
         if constexpr (W8)
           load_down8<C8I, DB8>(DA, p, l, e, n, n_end, lane);
         else
           load_down<CPLI, DBLK>(DA, p, l, e, n, n_end, lane);
+        if (lane == 0) tk = atomicAdd(&sm->dn_next, 1);
         run(f, DA);
       }
       __syncthreads();
@@ -1187,11 +1225,11 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     MOE_STAMP(7);
 
     // ---------------- P8: combine (+ residual) and hand off
-    const bool last = (l == p.L - 1);
+    const bool last = (l == L - 1);
     if (last && (p.flags & F_ALIAS)) {
       if (tid == 0) {
         for (;;) {
-          if (ld_u32(p.hdr + HDR_XREAD) >= (uint32_t)G) break;
+          if (ld_u32(p.hdr + xread) >= (uint32_t)G) break;
           if (wt.expired()) { record_status(p.hdr, -6); sm->abort_flag = 1; break; }
           __builtin_amdgcn_s_sleep(1);
         }
@@ -1250,32 +1288,11 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     if (sm->abort_flag == 1) break;
   }
 
-  // ---------------- end of call: the last workgroup advances the step
+  // ---------------- end of call
   __syncthreads();
   sbase = 0;
   MOE_STAMP(31);
 #undef MOE_STAMP
-  // Workgroups count themselves in two levels (8 group counters, then one
-  // counter of finished groups) so the atomics of 256 workgroups finishing
-  // together queue on 8 addresses instead of one.
-  if (tid == 0) {
-    bool last = router_only;  // router-only: the workgroup that ran the top-k
-    if (!router_only) {
-      const int grp = g & 7, in_grp = (G - grp + 7) >> 3;
-      const uint32_t old = add_u32(p.hdr + HDR_DONE_GRP + 32 * grp, 1u);
-      if (old == (uint32_t)(in_grp - 1)) {
-        const int groups = G < 8 ? G : 8;
-        last = add_u32(p.hdr + HDR_DONE_ALL, 1u) == (uint32_t)(groups - 1);
-      }
-    }
-    if (last) {
-      for (int c = 0; c < 8; ++c) st_u32(p.hdr + HDR_DONE_GRP + 32 * c, 0u);
-      st_u32(p.hdr + HDR_DONE_ALL, 0u);
-      st_u32(p.hdr + HDR_DONE, 0u);
-      st_u32(p.hdr + HDR_XREAD, 0u);
-      st_u32(p.hdr + HDR_EPOCH, tag);
-    }
-  }
 }
 
 }  // namespace moe
