@@ -128,6 +128,7 @@ enum {
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 16
 #define MOE_MAX_PREFETCH_IDS 4096
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20) /* the static workspace of moe_layer_chain_noalloc */
 
 /* Bytes of workspace needed for calls with up to `max_rows` rows and up to
  * `n_layers` chained layers (use n_layers = 1 for the single-layer calls).
@@ -198,6 +199,25 @@ int moe_layer_chain(const moe_dims* dims, int32_t M, int32_t n_layers,
                     const moe_layer_weights* layers, const uint16_t* x_in, void* out,
                     int32_t out_dtype, int32_t mode, int32_t* topk_idx_all, uint16_t* h_all,
                     void* ws, size_t ws_bytes, void* stream);
+
+/* moe_layer_chain for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation, arguments and results, with no workspace argument.
+ * The library's own static device buffer of MOE_NOALLOC_SCRATCH_BYTES (32 MiB)
+ * per GPU, held until the process ends, serves as the workspace.
+ *   Limit: the call's workspace, moe_workspace_size(dims, M, n_layers), must
+ *   fit in it (e.g. the Ling-shaped layer up to 16 rows, or 16 chained layers
+ *   at 6 rows): MOE_E_WORKSPACE otherwise, with nothing enqueued.
+ *   The call allocates nothing.  The first call on a device looks up the
+ *   buffer's address and clears it once with a fill kernel on `stream`.
+ *   Every call on one GPU shares the buffer: calls that overlap in time on one
+ *   GPU (other streams, other host threads) race and must not be issued.
+ *   Device-side status (MOE_E_TIMEOUT, MOE_E_INDEX) stays in that buffer and
+ *   is not reported. */
+int moe_layer_chain_noalloc(const moe_dims* dims, int32_t M, int32_t n_layers,
+                            const moe_layer_weights* layers, const uint16_t* x_in, void* out,
+                            int32_t out_dtype, int32_t mode, int32_t* topk_idx_all,
+                            uint16_t* h_all, void* stream);
 
 /* bf16 lm_head GEMV and greedy argmax: z[m][v] = sum_h h[m][h] * w_lm[v][h]
  * (fp32 accumulation), token[m] = the smallest v with the largest z[m][v].

@@ -51,8 +51,9 @@ MOE_MAX_PREFETCH_IDS = 4096
 DBG_NO_ROUTER_PUBLISH = 1
 
 EXPORTED = ("moe_workspace_size", "moe_workspace_init", "moe_router_topk", "moe_experts_fused",
-            "moe_layer_chain", "lmhead_argmax", "moe_expert_prefetch",
+            "moe_layer_chain", "moe_layer_chain_noalloc", "lmhead_argmax", "moe_expert_prefetch",
             "moe_last_device_status", "moe_workspace_debug", "moe_status_str")
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class moe_dims(ctypes.Structure):
@@ -87,6 +88,10 @@ _lib.moe_layer_chain.restype = ctypes.c_int
 _lib.moe_layer_chain.argtypes = [ctypes.POINTER(moe_dims), _I32, _I32,
                                  ctypes.POINTER(moe_layer_weights), _P, _P, _I32, _I32, _P, _P,
                                  _P, _SZ, _P]
+_lib.moe_layer_chain_noalloc.restype = ctypes.c_int
+_lib.moe_layer_chain_noalloc.argtypes = [ctypes.POINTER(moe_dims), _I32, _I32,
+                                         ctypes.POINTER(moe_layer_weights), _P, _P, _I32, _I32,
+                                         _P, _P, _P]
 _lib.lmhead_argmax.restype = ctypes.c_int
 _lib.lmhead_argmax.argtypes = [_I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.moe_expert_prefetch.restype = ctypes.c_int
@@ -194,6 +199,19 @@ def moe_layer_chain(d, M, layers, x_in, out, out_dtype, mode, topk_idx_all, ws, 
     return _lib.moe_layer_chain(ctypes.byref(d) if d is not None else None, M, n, arr, _ptr(x_in),
                                 _ptr(out), out_dtype, mode, _ptr(topk_idx_all), _ptr(h_all),
                                 _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream))
+
+
+def moe_layer_chain_noalloc(d, M, layers, x_in, out, out_dtype, mode, topk_idx_all, stream=None,
+                            h_all=None):
+    """moe_layer_chain on the library's static workspace (no workspace argument)."""
+    if layers is None:
+        arr, n = None, 0
+    else:
+        n = len(layers)
+        arr = (moe_layer_weights * max(n, 1))(*layers)
+    return _lib.moe_layer_chain_noalloc(ctypes.byref(d) if d is not None else None, M, n, arr,
+                                        _ptr(x_in), _ptr(out), out_dtype, mode,
+                                        _ptr(topk_idx_all), _ptr(h_all), _stream(stream))
 
 
 def lmhead_argmax(M, H, V, h, w_lm, token, max_logit, ws, ws_bytes=None, stream=None):

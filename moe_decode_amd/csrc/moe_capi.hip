@@ -466,10 +466,16 @@ int moe_experts_fused(const moe_dims* dims, int32_t M, const uint16_t* x, const 
                       nullptr, nullptr, ws, (hipStream_t)stream);
 }
 
-int moe_layer_chain(const moe_dims* dims, int32_t M, int32_t n_layers,
-                    const moe_layer_weights* layers, const uint16_t* x_in, void* out,
-                    int32_t out_dtype, int32_t mode, int32_t* topk_idx_all, uint16_t* h_all,
-                    void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// moe_layer_chain's argument checks (all but the workspace): MOE_OK, or the
+// error to return with nothing enqueued; *flags receives the kernel's mode flags.
+int check_chain(const moe_dims* dims, int32_t M, int32_t n_layers,
+                const moe_layer_weights* layers, const uint16_t* x_in, void* out,
+                int32_t out_dtype, int32_t mode, int32_t* topk_idx_all, uint16_t* h_all,
+                uint32_t* flags_out) {
   int rc = check_dims(dims);
   if (rc) return rc;
   if (M < 1 || n_layers < 1) return MOE_E_ARG;
@@ -499,8 +505,6 @@ int moe_layer_chain(const moe_dims* dims, int32_t M, int32_t n_layers,
   if (h_all && (overlaps(h_all, (size_t)(n_layers + 1) * M * dims->hidden * 2, x_in,
                          (size_t)M * dims->hidden * 2)))
     return MOE_E_ARG;
-  rc = check_ws(dims, M, n_layers, ws, ws_bytes);
-  if (rc) return rc;
   uint32_t flags = 0;
   if (mode == MOE_CHAIN_RESIDUAL) flags |= F_RESIDUAL;
   if (mode == MOE_CHAIN_PRENORM_RESIDUAL) flags |= F_RESIDUAL | F_PRENORM;
@@ -508,6 +512,89 @@ int moe_layer_chain(const moe_dims* dims, int32_t M, int32_t n_layers,
   if (out_dtype == MOE_OUT_F32) flags |= F_OUT_F32;
   const size_t osz = (size_t)M * dims->hidden * (out_dtype == MOE_OUT_F32 ? 4 : 2);
   if (overlaps(out, osz, x_in, (size_t)M * dims->hidden * 2)) flags |= F_ALIAS;
+  *flags_out = flags;
+  return MOE_OK;
+}
+
+// ---- the library's own workspace, for moe_layer_chain_noalloc
+//
+// A static device array, one per GPU (each GPU that runs the call holds its
+// own copy until the process ends).  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only that
+// address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+struct ScratchDev {
+  void* ptr = nullptr;
+  bool ready = false;
+};
+ScratchDev g_scratch[64];
+
+__global__ void fill_zero_kernel(uint4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The current device's scratch address.  On the first call on a device it is
+// looked up and the whole array is cleared once, by a fill kernel on `stream`
+// (a kernel, not a memset: a caller may be capturing that stream), and the
+// host's step count for it starts at zero; later calls only read the address.
+int scratch_for_device(void** out, hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_E_HIP;
+  std::lock_guard<std::mutex> lk(g_mu);
+  ScratchDev& sd = g_scratch[dev];
+  if (!sd.ready) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_E_HIP;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(256), 0, stream, (uint4*)ptr,
+                       (size_t)MOE_NOALLOC_SCRATCH_BYTES / 16);
+    if (hipGetLastError() != hipSuccess) return MOE_E_HIP;
+    {
+      std::lock_guard<std::mutex> lk2(g_ws_mu);
+      g_ws[ptr] = WsState{};
+    }
+    sd.ptr = ptr;
+    sd.ready = true;
+  }
+  *out = sd.ptr;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_chain(const moe_dims* dims, int32_t M, int32_t n_layers,
+                    const moe_layer_weights* layers, const uint16_t* x_in, void* out,
+                    int32_t out_dtype, int32_t mode, int32_t* topk_idx_all, uint16_t* h_all,
+                    void* ws, size_t ws_bytes, void* stream) {
+  uint32_t flags = 0;
+  int rc = check_chain(dims, M, n_layers, layers, x_in, out, out_dtype, mode, topk_idx_all, h_all,
+                       &flags);
+  if (rc) return rc;
+  rc = check_ws(dims, M, n_layers, ws, ws_bytes);
+  if (rc) return rc;
+  return launch_layer(*dims, M, n_layers, flags, layers, x_in, out, nullptr, nullptr, topk_idx_all,
+                      nullptr, nullptr, h_all, ws, (hipStream_t)stream);
+}
+
+int moe_layer_chain_noalloc(const moe_dims* dims, int32_t M, int32_t n_layers,
+                            const moe_layer_weights* layers, const uint16_t* x_in, void* out,
+                            int32_t out_dtype, int32_t mode, int32_t* topk_idx_all,
+                            uint16_t* h_all, void* stream) {
+  uint32_t flags = 0;
+  int rc = check_chain(dims, M, n_layers, layers, x_in, out, out_dtype, mode, topk_idx_all, h_all,
+                       &flags);
+  if (rc) return rc;
+  // the call's workspace must fit the static one (checked before any HIP call)
+  if (ws_layout(*dims, M, n_layers).total > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return MOE_E_WORKSPACE;
+  void* ws = nullptr;
+  rc = scratch_for_device(&ws, (hipStream_t)stream);
+  if (rc) return rc;
   return launch_layer(*dims, M, n_layers, flags, layers, x_in, out, nullptr, nullptr, topk_idx_all,
                       nullptr, nullptr, h_all, ws, (hipStream_t)stream);
 }

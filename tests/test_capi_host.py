@@ -273,3 +273,20 @@ def test_plain_c_caller(tmp_path):
                     "-Wl,-rpath," + lib_dir, "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
     assert out.strip() == "ok"
+
+
+def test_noalloc_call_validates_before_touching_the_device():
+    """The static-workspace variant rejects bad arguments, and any call whose workspace
+    would not fit its MOE_NOALLOC_SCRATCH_BYTES buffer, before any HIP call."""
+    d = md.dims(**LING)
+    lw = md.layer_weights(16, 16, 16)
+    rc, need = md.moe_workspace_size(d, 16, 64)
+    assert rc == md.MOE_OK and need > md.MOE_NOALLOC_SCRATCH_BYTES
+    assert md.moe_layer_chain_noalloc(d, 16, [lw] * 64, 16, 16, md.MOE_OUT_BF16,
+                                      md.MOE_CHAIN_RESIDUAL, None, stream=0) == md.MOE_E_WORKSPACE
+    rc, need = md.moe_workspace_size(d, 6, 16)
+    assert rc == md.MOE_OK and need <= md.MOE_NOALLOC_SCRATCH_BYTES
+    assert md.moe_layer_chain_noalloc(None, 1, [lw], 16, 16, 0, 1, None, stream=0) == md.MOE_E_ARG
+    assert md.moe_layer_chain_noalloc(d, 0, [lw], 16, 16, 0, 1, None, stream=0) == md.MOE_E_ARG
+    assert md.moe_layer_chain_noalloc(d, 1, [lw], BAD, 16, 0, 1, None, stream=0) == md.MOE_E_ALIGN
+    assert md.moe_layer_chain_noalloc(d, 1, [lw], 16, 16, 0, 9, None, stream=0) == md.MOE_E_ARG
