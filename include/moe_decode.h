@@ -38,6 +38,14 @@
  *  - Device-side failures (an out-of-range expert index in caller-provided
  *    top-k input, a wait that missed its deadline) are recorded as a sticky
  *    status in the workspace; read it with moe_last_device_status().
+ *  - The layer calls (moe_router_topk, moe_experts_fused, moe_layer_chain,
+ *    moe_layer_chain_noalloc) launch one workgroup per compute unit, and those
+ *    workgroups wait on each other, so the whole grid must be resident at
+ *    once.  No other kernel may run on the device while a layer call runs
+ *    (work on other streams must be ordered before or after it, e.g. by
+ *    events).  A grid that cannot become wholly resident does not hang: every
+ *    wait has a deadline, and the call then records MOE_E_TIMEOUT.  A call
+ *    whose grid cannot fit at all (occupancy check) returns MOE_E_UNSUPPORTED.
  */
 #ifndef MOE_DECODE_H
 #define MOE_DECODE_H
@@ -271,7 +279,10 @@ int moe_last_device_status(void* ws, size_t ws_bytes, void* stream);
  *          received, 9 top-k done, 4 expert union built, 5 routed gate/up
  *          done, 6 down inputs staged, 7 down projection done, 8 combine
  *          done); slot 31 is
- *          the end of the call. */
+ *          the end of the call;
+ *   bit 2: the occupancy check of the fused layer kernel reports that its grid
+ *          would not be resident, so layer calls on this workspace return
+ *          MOE_E_UNSUPPORTED with nothing enqueued (exercises that gate). */
 int moe_workspace_debug(void* ws, size_t ws_bytes, uint32_t flags, uint32_t deadline_us,
                         void* stream);
 

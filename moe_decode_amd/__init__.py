@@ -49,6 +49,8 @@ MOE_MAX_LAYERS = 64
 MOE_MAX_PREFETCH_IDS = 4096
 
 DBG_NO_ROUTER_PUBLISH = 1
+DBG_STAMPS = 2
+DBG_NOT_RESIDENT = 4
 
 EXPORTED = ("moe_workspace_size", "moe_workspace_init", "moe_router_topk", "moe_experts_fused",
             "moe_layer_chain", "moe_layer_chain_noalloc", "lmhead_argmax", "moe_expert_prefetch",

@@ -86,6 +86,12 @@ CallTag next_call(const void* ws) {
   return CallTag{st.epoch, st.flags, st.deadline ? st.deadline : kDefaultDeadlineTicks};
 }
 
+uint32_t ws_flags(const void* ws) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  auto it = g_ws.find(ws);
+  return it == g_ws.end() ? 0u : it->second.flags;
+}
+
 // A launch that failed ran no kernel: its tag is given back, so that the tags
 // of the calls that did run stay consecutive (each call clears the input-read
 // counter of the other tag parity for the next one).
@@ -122,6 +128,19 @@ int down_blocks(int cpli) {
   return b < 1 ? 1 : (b > 4 ? 4 : b);
 }
 
+// Launch of the persistent layer kernel.  Its workgroups wait on each
+// other's tagged words, so all of them must be resident at once.  The default
+// is a plain launch behind an occupancy check (one workgroup fits a CU with
+// its registers and LDS), which holds while no other kernel shares the device
+// during the call; every wait also has a deadline, so a grid that is not
+// wholly resident ends with MOE_E_TIMEOUT instead of hanging.  Built with
+// MOE_COOP_LAUNCH=1 the kernel goes through hipLaunchCooperativeKernel, which
+// guarantees co-residency or fails the launch, at a measured cost of about
+// 18 us per launch on MI355X (a single Ling layer takes 30 us).
+#ifndef MOE_COOP_LAUNCH
+#define MOE_COOP_LAUNCH 0
+#endif
+
 // Compiled (CPLH, CPLI) variants of the layer kernel: hidden size 256 * CPLH,
 // intermediate size 64 * CPLI; NL layer weight slots in the kernel arguments.
 template <int NL>
@@ -151,10 +170,12 @@ struct KernelReady {
 std::mutex g_ready_mu;
 std::vector<KernelReady> g_ready;
 
-int prepare_kernel(const void* fn, int lds, int block) {
+// not_resident: the debug flag DBG_NOT_RESIDENT of the call's workspace; the
+// occupancy answer is then taken as zero blocks (a test of the gate below)
+int prepare_kernel(const void* fn, int lds, int block, bool not_resident = false) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MOE_E_HIP;
-  {
+  if (!not_resident) {
     std::lock_guard<std::mutex> lk(g_ready_mu);
     for (const KernelReady& r : g_ready)
       if (r.fn == fn && r.lds >= lds && r.device == dev) return MOE_OK;
@@ -164,6 +185,7 @@ int prepare_kernel(const void* fn, int lds, int block) {
   int nb = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, block, lds) != hipSuccess)
     return MOE_E_HIP;
+  if (not_resident) nb = 0;
   if (nb < 1) return MOE_E_UNSUPPORTED;  // the persistent grid would not be co-resident
   std::lock_guard<std::mutex> lk(g_ready_mu);
   g_ready.push_back(KernelReady{fn, lds, dev});
@@ -301,7 +323,8 @@ int launch_layer_nl(const moe_dims& d, int M, int L, uint32_t flags,
   LdsPlan lp;
   rc = plan_lds(d, M, G, di.max_lds, &lp);
   if (rc) return rc;
-  rc = prepare_kernel((const void*)kern, lp.total, MOE_WG);
+  rc = prepare_kernel((const void*)kern, lp.total, MOE_WG,
+                      (ws_flags(ws) & DBG_NOT_RESIDENT) != 0u);
   if (rc) return rc;
 
   const WsLayout wl = ws_layout(d, M, L);
@@ -352,10 +375,21 @@ int launch_layer_nl(const moe_dims& d, int M, int L, uint32_t flags,
     p.lw[l].sgu = layers[l].s_gate_up;
     p.lw[l].sd = layers[l].s_down;
   }
+  // The workgroups wait on each other's tagged words, so all of them must be
+  // resident at once: a cooperative launch guarantees that or fails (then
+  // nothing runs and MOE_E_UNSUPPORTED is returned).
+#if MOE_COOP_LAUNCH
+  void* args[] = {&p};
+  const hipError_t le = hipLaunchCooperativeKernel((const void*)kern, dim3(G), dim3(MOE_WG), args,
+                                                   (unsigned)lp.total, st);
+#else
   hipLaunchKernelGGL(kern, dim3(G), dim3(MOE_WG), lp.total, st, p);
-  if (hipGetLastError() != hipSuccess) {
+  const hipError_t le = hipGetLastError();
+#endif
+  if (le != hipSuccess) {
+    (void)hipGetLastError();  // clear the launch error
     undo_call(ws, p.tag);
-    return MOE_E_HIP;
+    return le == hipErrorCooperativeLaunchTooLarge ? MOE_E_UNSUPPORTED : MOE_E_HIP;
   }
   return MOE_OK;
 }

@@ -43,7 +43,9 @@ enum : int {
   HDR_BYTES = HDR_LM_SLOT_BYTE + MOE_LM_MAX_GRID * MOE_MAXM * 2 * 8
 };
 
-enum : uint32_t { DBG_NO_ROUTER_PUBLISH = 1u, DBG_STAMPS = 2u };
+// debug flags of a workspace (moe_workspace_debug); DBG_NOT_RESIDENT is seen by
+// the host only: the layer kernel's occupancy check then reports no room
+enum : uint32_t { DBG_NO_ROUTER_PUBLISH = 1u, DBG_STAMPS = 2u, DBG_NOT_RESIDENT = 4u };
 
 constexpr uint32_t kDefaultDeadlineTicks = 20000000u;  // 200 ms at 100 MHz
 

@@ -542,3 +542,27 @@ def test_missed_deadline_is_reported_and_recovers(gpu, dw):
     md.check(md.moe_workspace_debug(ws, 0, 0))
     idx, out = _layer_gpu(wl, dw, gpu, x, ws=ws)
     _check_layer(wl, x, idx, out)
+
+
+def test_occupancy_gate_refuses_a_grid_that_would_not_be_resident(gpu, dw):
+    """With the debug flag that makes the host's occupancy check report no room, a
+    layer call returns MOE_E_UNSUPPORTED and enqueues nothing (the output keeps its
+    contents, no device status is recorded); after the flag is cleared the next call
+    on the same workspace is correct."""
+    import torch
+    wl = W.C1
+    x = x_tiefree(wl, 2)
+    d = _dims(wl)
+    ws = md.new_workspace(d, 2, 1)
+    md.check(md.moe_workspace_debug(ws, md.DBG_NOT_RESIDENT, 0))
+    out = torch.full((2, wl.H), 0x1234, dtype=torch.int16, device=gpu)
+    say("occupancy gate forced closed")
+    rc = md.moe_layer_chain(d, 2, [_lw(dw.layer(wl, 0))], D.to_device(x), out, md.MOE_OUT_BF16,
+                            md.MOE_CHAIN_LAYER_ONLY, None, ws)
+    assert rc == md.MOE_E_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert bool((out == 0x1234).all())
+    assert md.moe_last_device_status(ws) == md.MOE_OK
+    md.check(md.moe_workspace_debug(ws, 0, 0))
+    idx, o = _layer_gpu(wl, dw, gpu, x, ws=ws)
+    _check_layer(wl, x, idx, o)
