@@ -169,11 +169,14 @@ __device__ __forceinline__ void st_tag(uint64_t* p, uint32_t lo, uint32_t tag) {
   __hip_atomic_store(p, ((uint64_t)tag << 32) | (uint64_t)lo, __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
 }
-// Weight rows are read once per call: their 16-byte loads carry the
-// non-temporal (streaming) policy, so the stream passes through L2 without
-// pushing out what has to stay there between calls, the kernel's own code
-// above all ("Instruction cache" and the evict-first weight streams, Ling-3.0
-// flash megakernel notes).
+// Weight rows are read once per call, so their 16-byte loads carry the
+// non-temporal (streaming) policy: tens of megabytes of weights then go by
+// without displacing the few lines that are reused from L2 within and between
+// calls, the kernel's own code first among them, then the tagged exchange
+// words.  The megakernel of "Muse Spark Open Ultrafast: Pushing beyond 1,000
+// Tokens per second", section "Megakernel internals", marks its weight
+// streams evict-first for the same reason and reports the cost of code
+// refetches in its instruction-cache part.
 #ifndef MOE_WEIGHT_NT
 #define MOE_WEIGHT_NT 1
 #endif

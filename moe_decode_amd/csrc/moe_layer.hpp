@@ -8,10 +8,12 @@
 //       pre-norm chain keep this workgroup's rows of h_l for the residual and
 //       replace x by bf16(RMSNorm(h_l) * gain).
 //   P1  router GEMV rows and the shared expert's gate/up rows, spread over every
-//       wave of the GPU.  The shared expert does not depend on routing, so its
-//       weights stream while the logits travel ("weights that do not depend on
-//       routing load before their inputs arrive", SGLang Low-Latency Mode, AMD
-//       Low-Latency Kernels).  Logits and the shared expert's SwiGLU output are
+//       wave of the GPU.  Neither depends on the routing, so their loads are
+//       issued before the input is even staged, and the shared expert's rows
+//       stream while the logits travel between workgroups (the AMD kernels of
+//       "SGLang Low-Latency Mode: Kernels and Runtime", section "AMD Low-Latency
+//       Kernels", request routing-independent weights ahead of their inputs in
+//       the same way).  Logits and the shared expert's SwiGLU output are
 //       published as step-tagged words.
 //   P4  every workgroup reads all logits and computes the softmax top-k
 //       itself, so no second device-wide hop is needed.
@@ -493,9 +495,11 @@ __device__ __forceinline__ void compute_down8(const DownRegs8<C, DB>& r, int I8,
 
 // ---------------------------------------------------------------- P4 / P5
 
-// Softmax top-k ("softmax top-k with renormalised gates", Low-Latency MoE
-// Decode, routing step).  The selection order is: larger logit first, lower
-// expert index first among equal logits.
+// Softmax top-k with gates renormalised over the chosen experts: the router's
+// second step in "Ling-3.0-flash on 4 Blackwell GPUs", section "PDL: stacking
+// the latency floors of small kernels" (the router chain ends in a top-k), with
+// K = 8 from section "The model".  The selection order is: larger logit first,
+// lower expert index first among equal logits.
 //
 // Fast path (E <= 512 experts, one per thread, and K no larger than the number
 // of 64-expert groups): every wave takes the maximum of its group of 64
