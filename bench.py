@@ -5,18 +5,24 @@ Headline (the JSON `value`): the Ling-3.0-flash-shaped MoE layer at M=1
 persistent launch per layer (router -> softmax top-k -> expert union ->
 gate/up+SwiGLU -> down -> combine), reported as effective HBM GB/s of the
 unique weight bytes the call must stream (router + every selected expert +
-the shared expert, each once), with microseconds per layer beside it.
+the shared expert, each once), with microseconds per layer beside it.  Every
+time in the record comes from HIP events on the launch stream.
 
 Cold weights: each timed step runs a different one of 16 distinct layers
 (97.7 GB in all, far beyond the 256 MB Infinity Cache) on a different input
 row set, so no step finds its weights in any cache; inputs and weights are
 resident in HBM before timing starts and nothing else runs in the timed
-region.  Secondary figures on the same protocol: the same layer at M=6, the
-tensor-parallel shard (I=192, fp32 partial) at M=6, and the 16-layer
-pre-norm residual chain at M=6 followed by the 157184-row lm_head argmax.
+region.  Beside it: the same call hot (one layer, one input, repeated: its
+109 MB stay in the Infinity Cache), and the achievable streaming-read rate of
+the chip from a plain read kernel.  Secondary figures on the cold protocol:
+the layer at M=6 (independent rows, and perturbed copies of one row), M=16,
+the tensor-parallel shard (I=192, fp32 partial) at M=6, the router front,
+fp8 experts, the 16-layer pre-norm residual chains followed by the 157184-row
+lm_head argmax, the lm_head alone, and speculative expert prefetch on a
+time-correlated decode walk guessed from the previous step's routing.
 
-The CPU oracle is timed on a bounded sample of the headline workload on the
-host's cores (cpu_baseline); it is a reported reference, not a target.
+The CPU oracle is timed on bounded samples of the same workloads on the host's
+cores (cpu_baseline); it is a reported reference, not a target.
 """
 import argparse
 import json
@@ -30,6 +36,7 @@ sys.path.insert(0, ROOT)
 METRIC = "µs/MoE layer and effective HBM GB/s (% of peak) at M=1 and M=6, cold weights"
 HBM_PEAK_GBS = 8000.0
 N_LAYERS = 16
+PERTURB_RHO = 0.9       # correlation of each perturbed row with the batch's base row
 
 
 def parse():
@@ -105,20 +112,24 @@ def main():
         rows = [W.x_rows(wl, [s * M + m for m in range(M)]) for s in range(n_steps)]
         return torch.stack([D.to_device(r) for r in rows])
 
-    def time_layer(wl, lws, M, steps, warmup, out_f32=False, mode=None):
-        """Cold rotating per-layer timing; returns dict of figures."""
+    def time_layer(wl, lws, M, steps, warmup, out_f32=False, mode=None, xs=None, hot=False):
+        """Per-layer timing, cold (call i runs layer i mod 16 on input set i) or hot
+        (every call runs layer 0 on input set 0, so its weights stay in the caches when
+        they fit); returns dict of figures, all from events on the launch stream."""
         mode = md.MOE_CHAIN_LAYER_ONLY if mode is None else mode
         d = md.dims(wl.H, wl.E, wl.K, wl.I, wl.S, wl.routed_scale,
                     md.MOE_EXPERT_FP8_B128 if wl.fp8 else md.MOE_EXPERT_BF16)
         ws = md.new_workspace(d, M, 1)
         n = steps + warmup
-        xs = x_pool(wl, n, M)
+        xs = x_pool(wl, n, M) if xs is None else xs
+        assert xs.shape[0] >= n and xs.shape[1] == M
         out = torch.empty((M, wl.H), dtype=torch.float32 if out_f32 else torch.int16, device=dev)
         idx = torch.empty((n, M, wl.K), dtype=torch.int32, device=dev)
         dt = md.MOE_OUT_F32 if out_f32 else md.MOE_OUT_BF16
 
         def call(i):
-            return md.moe_layer_chain(d, M, [lws[i % len(lws)]], xs[i], out, dt, mode, idx[i],
+            j = 0 if hot else i
+            return md.moe_layer_chain(d, M, [lws[j % len(lws)]], xs[j], out, dt, mode, idx[i],
                                       ws)
 
         for i in range(warmup):
@@ -127,13 +138,11 @@ def main():
         # timed region: exactly `steps` back-to-back launches between two events
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        t_start = time.perf_counter()
         e0.record()
         for i in range(steps):
             md.check(call(warmup + i))
         e1.record()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t_start
         md.check(md.moe_last_device_status(ws))
         us_per = e0.elapsed_time(e1) * 1e3 / steps
         # spread: a separate, untimed pass with an event after every launch
@@ -155,7 +164,6 @@ def main():
             "per_call_event_us_median": float(np.median(per)),
             "per_call_event_us_p10": float(np.percentile(per, 10)),
             "per_call_event_us_p90": float(np.percentile(per, 90)),
-            "wall_ms_per_step": wall * 1e3 / steps,
             "effective_gbs": float(gbs),
             "pct_of_hbm_peak": float(100.0 * gbs / HBM_PEAK_GBS),
             "mean_union_experts": float(U.mean()),
@@ -163,35 +171,47 @@ def main():
             "floor_us_at_peak": float(bytes_per.mean() / HBM_PEAK_GBS / 1e3),
         }
 
-    # ---------------- headline: M=1
+    # ---------------- headline: M=1, cold; the same call hot beside it
     head = time_layer(W.C2, lw, 1, args.steps, args.warmup)
-    print("M=1: %.2f us/layer, %.0f GB/s (%.1f %% of 8 TB/s)"
-          % (head["us_per_layer"], head["effective_gbs"], head["pct_of_hbm_peak"]),
+    hot = time_layer(W.C2, lw, 1, args.steps, args.warmup, hot=True)
+    head["hot_us_per_layer"] = hot["us_per_layer"]
+    print("M=1: %.2f us/layer cold (%.0f GB/s, %.1f %% of 8 TB/s), %.2f us hot"
+          % (head["us_per_layer"], head["effective_gbs"], head["pct_of_hbm_peak"],
+             hot["us_per_layer"]), file=sys.stderr, flush=True)
+    ceiling = stream_ceiling(torch, dev)
+    print("streaming-read ceiling: %.0f GB/s (%s)" % (ceiling["gbs"], ceiling["grid"]),
           file=sys.stderr, flush=True)
 
     secondary = {}
 
     def report_prefetch(name, r):
         secondary[name] = r
-        print("%s: layer %.1f us cold, %.1f / %.1f / %.1f us after a prefetch at 100 / 75 / 0 %% "
-              "routed hits; prefetch %.1f us (%.0f GB/s)"
-              % (name, r["cold"]["layer_us_mean"], r["hit100"]["layer_us_mean"],
-                 r["hit75"]["layer_us_mean"], r["hit0"]["layer_us_mean"],
-                 r["hit100"]["prefetch_us_mean"], r["hit100"]["prefetch_gbs"]),
-              file=sys.stderr, flush=True)
-        print("%s: back-to-back %.1f us per layer, %.1f us with the next call's experts "
-              "prefetched on a second stream during each call"
-              % (name, r["pipelined_no_prefetch_us_per_layer"],
-                 r["pipelined_prefetch_next_us_per_layer"]), file=sys.stderr, flush=True)
+        print("%s: rho %.2f, previous-step guess hits %.0f %%; layer %.1f us cold, %.1f us after "
+              "prefetch (+%.1f us prefetch = %.1f); exact guess %.1f + %.1f = %.1f us"
+              % (name, r["rho"], 100 * r["hit_rate_previous_step"], r["cold_layer_us"],
+                 r["previous"]["layer_us"], r["previous"]["prefetch_us"],
+                 r["previous"]["total_us"], r["exact"]["layer_us"], r["exact"]["prefetch_us"],
+                 r["exact"]["total_us"]), file=sys.stderr, flush=True)
 
+    chain_probe = None
     if not args.no_secondary:
-        report_prefetch(W.C2.name + "_prefetch",
-                        time_prefetch(md, np, torch, dev, W.C2, lw, x_pool(W.C2, 176, 1)))
+        report_prefetch(W.C2.name + "_prefetch_walk",
+                        time_prefetch(md, np, torch, dev, W.C2, lw))
         s3 = time_layer(W.C3, lw, 6, args.steps, args.warmup)
         secondary[W.C3.name] = s3
         print("M=6: %.2f us/layer, %.0f GB/s (%.1f %%), U=%.1f"
               % (s3["us_per_layer"], s3["effective_gbs"], s3["pct_of_hbm_peak"],
                  s3["mean_union_experts"]), file=sys.stderr, flush=True)
+        # six rows that are perturbed copies of one row: correlated routing, smaller union
+        n3 = args.steps + args.warmup
+        xp = torch.stack([D.to_device(W.x_perturbed(W.C3, 6, PERTURB_RHO, s)) for s in range(n3)])
+        s3p = time_layer(W.C3, lw, 6, args.steps, args.warmup, xs=xp)
+        s3p["rho"] = PERTURB_RHO
+        secondary[W.C3.name + "_perturbed"] = s3p
+        del xp
+        print("M=6 perturbed rows (rho %.2f): %.2f us/layer, %.0f GB/s (%.1f %%), U=%.1f"
+              % (PERTURB_RHO, s3p["us_per_layer"], s3p["effective_gbs"], s3p["pct_of_hbm_peak"],
+                 s3p["mean_union_experts"]), file=sys.stderr, flush=True)
         s12 = time_layer(W.C12, lw, 16, args.steps, args.warmup)
         secondary[W.C12.name] = s12
         print("M=16: %.2f us/layer, %.0f GB/s (%.1f %%), U=%.1f"
@@ -227,16 +247,15 @@ def main():
             print("fp8 M=%d: %.2f us/layer, %.0f GB/s (%.1f %%)"
                   % (M8, r8["us_per_layer"], r8["effective_gbs"], r8["pct_of_hbm_peak"]),
                   file=sys.stderr, flush=True)
-        report_prefetch(W.C9.name + "_prefetch",
-                        time_prefetch(md, np, torch, dev, W.C9, lw8, x_pool(W.C9, 176, 1)))
-        c8 = time_chain(md, D, W, np, torch, dev, lw8, steps=10, warmup=2, wl=W.C11)
+        c8, _ = time_chain(md, D, W, np, torch, dev, lw8, steps=10, warmup=2, wl=W.C11)
         secondary[W.C11.name] = c8
         print("fp8 chain16+lm_head M=6: %.1f us (floor %.1f us, ratio %.2f)"
               % (c8["us_per_step"], c8["floor_us_at_peak"], c8["ratio_to_floor"]),
               file=sys.stderr, flush=True)
         del f8, lw8
         torch.cuda.empty_cache()
-        secondary[W.C5.name] = time_chain(md, D, W, np, torch, dev, lw, steps=10, warmup=2)
+        secondary[W.C5.name], chain_probe = time_chain(md, D, W, np, torch, dev, lw, steps=10,
+                                                       warmup=2)
         c = secondary[W.C5.name]
         print("chain16+lm_head M=6: %.1f us (floor %.1f us, ratio %.2f)"
               % (c["us_per_step"], c["floor_us_at_peak"], c["ratio_to_floor"]),
@@ -245,7 +264,7 @@ def main():
         # the launch is paid once per step, not once per layer
         from dataclasses import replace as _replace
         wl1 = _replace(W.C5, name="ling_chain16_lmhead_m1", M=1)
-        c1 = time_chain(md, D, W, np, torch, dev, lw, steps=10, warmup=2, wl=wl1)
+        c1, _ = time_chain(md, D, W, np, torch, dev, lw, steps=10, warmup=2, wl=wl1)
         c1["chain_us_per_layer"] = c1["chain_us"] / wl1.n_layers
         secondary[wl1.name] = c1
         print("chain16+lm_head M=1: %.1f us (chain %.1f us = %.2f us per layer, lm_head %.1f us)"
@@ -266,7 +285,7 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(args.cpu_seconds)
+        cpu = cpu_baseline(args.cpu_seconds, chain_probe)
 
     rec = {
         "metric": METRIC,
@@ -275,7 +294,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(head["wall_ms_per_step"], 5),
+        "ms_per_step": round(head["us_per_layer"] * 1e-3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -285,11 +304,15 @@ def main():
                    "shared_experts": 1, "top_k": 8, "inter": 768, "rows": 1,
                    "cold": "rotating over 16 distinct layers, 97.7 GB"},
         "us_per_layer": round(head["us_per_layer"], 3),
+        "hot_us_per_layer": round(head["hot_us_per_layer"], 3),
         "pct_of_hbm_peak": round(head["pct_of_hbm_peak"], 2),
         "roofline": {"bound": "hbm", "achieved": round(head["effective_gbs"], 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(head["effective_gbs"] / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+                     "traffic": traffic,
+                     "achievable": round(ceiling["gbs"], 1),
+                     "frac_of_achievable": round(head["effective_gbs"] / ceiling["gbs"], 4),
+                     "achievable_kernel": ceiling["kernel"]},
         "headline_detail": head,
         "secondary": secondary,
         "cpu_baseline": cpu,
@@ -297,8 +320,38 @@ def main():
     print(json.dumps(rec))
 
 
+def stream_ceiling(torch, dev, gib=4, reps=4, grids=(256, 1024, 2048)):
+    """Achievable streaming-read rate of the chip: bs_stream_read (whole 16 KiB chunks
+    per wave, 1 KiB non-temporal loads, 16 in flight) over a buffer far larger than
+    every cache, best of a few grid sizes, timed with events on the launch stream."""
+    import benchsupport as bs
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(max(grids), dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream()
+    best = (0.0, None)
+    for g in grids:
+        bs.stream_read(buf, sink, g, st.cuda_stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            bs.stream_read(buf, sink, g, st.cuda_stream)
+        e1.record(st)
+        torch.cuda.synchronize()
+        gbs = buf.numel() * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        best = max(best, (gbs, g), key=lambda t: t[0])
+    del buf
+    torch.cuda.empty_cache()
+    return {"gbs": best[0], "grid": "%d x 512 threads" % best[1],
+            "kernel": "bs_stream_read over %d GiB: 16 KiB per wave, 1 KiB non-temporal loads, "
+                      "16 in flight" % gib}
+
+
 def time_chain(md, D, W, np, torch, dev, lw, steps, warmup, wl=None):
-    """16-layer pre-norm residual chain (one launch) + lm_head argmax (one launch)."""
+    """16-layer pre-norm residual chain (one launch) + lm_head argmax (one launch).
+
+    Returns (figures, probe): probe holds the tokens and per-layer routing of one more
+    call on the first input set (rows 0..M-1), for comparison with the CPU oracle."""
     wl = W.C5 if wl is None else wl
     M = wl.M
     d = md.dims(wl.H, wl.E, wl.K, wl.I, wl.S, wl.routed_scale,
@@ -345,6 +398,10 @@ def time_chain(md, D, W, np, torch, dev, lw, steps, warmup, wl=None):
     total_bytes = chain_bytes.mean() + lm_bytes
     floor_us = total_bytes / HBM_PEAK_GBS / 1e3
     tot_us = chain_us.mean() + lm_us.mean()
+    call(0)
+    torch.cuda.synchronize()
+    probe = {"rows": [m for m in range(M)], "tokens": tok.cpu().numpy().copy(),
+             "idx": idx[0].cpu().numpy().copy()}
     del lm
     return {
         "us_per_step": float(tot_us),
@@ -355,104 +412,78 @@ def time_chain(md, D, W, np, torch, dev, lw, steps, warmup, wl=None):
         "unique_bytes_per_step": float(total_bytes),
         "floor_us_at_peak": float(floor_us),
         "ratio_to_floor": float(tot_us / floor_us),
-    }
+    }, probe
 
 
-def time_prefetch(md, np, torch, dev, wl, lws, xs, calls=160, warmup=16):
-    """Layer time after a speculative prefetch of its experts, against cold.
+def time_prefetch(md, np, torch, dev, wl, lws, rho=0.95, n_steps=12):
+    """Speculative expert prefetch on a decode-like, time-correlated input.
 
-    Calls rotate over the distinct layers in `lws`, so each call's weights were
-    last read many gigabytes ago.  A first untimed pass records every call's
-    routing; then, per call, the guess lists the chosen experts with a share
-    replaced by experts the call does not pick (routed hit rate 100, 75 or 0 %),
-    plus the shared expert.  moe_expert_prefetch runs just before the layer on
-    the same stream; events around each kernel give the layer's and the
-    prefetch's time.  "cold" is the same loop with no prefetch."""
-    M = xs.shape[1]
+    One row per step from W.x_walk (correlation rho between consecutive steps);
+    each step runs the distinct layers of `lws` in turn on that row (layer-only
+    calls), so every call's weights were last read one step, i.e. more than
+    1.5 GB of other layers, ago.  Step 0 is untimed.  Three passes over the same
+    calls, all on one stream (no kernel may run beside a layer call):
+      cold      the layer calls alone;
+      previous  before each call, moe_expert_prefetch of the experts the same
+                layer chose at the previous step, plus the shared expert;
+      exact     the same with the call's own routing (the best any guess can do).
+    Reports per-call layer time, prefetch time and their sum against cold, the
+    realized hit rate of the previous-step guess, and whether every pass routed
+    identically (a prefetch never changes results)."""
+    from datagen import device as D
+    from datagen import workloads as W
+    nl = len(lws)
     d = md.dims(wl.H, wl.E, wl.K, wl.I, wl.S, wl.routed_scale,
                 md.MOE_EXPERT_FP8_B128 if wl.fp8 else md.MOE_EXPERT_BF16)
-    ws = md.new_workspace(d, M, 1)
-    n = calls + warmup
-    nl = len(lws)
-    out = torch.empty((M, wl.H), dtype=torch.int16, device=dev)
-    idx = torch.empty((n, M, wl.K), dtype=torch.int32, device=dev)
+    ws = md.new_workspace(d, 1, 1)
+    xs = torch.stack([D.to_device(r[None]) for r in W.x_walk(wl, n_steps, rho)])
+    out = torch.empty((1, wl.H), dtype=torch.int16, device=dev)
+    n = n_steps * nl
+    shared = np.arange(wl.E, wl.E + wl.S)
 
-    def layer(i):
-        md.check(md.moe_layer_chain(d, M, [lws[i % nl]], xs[i], out, md.MOE_OUT_BF16,
-                                    md.MOE_CHAIN_LAYER_ONLY, idx[i], ws))
-
-    for i in range(n):
-        layer(i)
-    torch.cuda.synchronize()
-    md.check(md.moe_last_device_status(ws))
-    chosen = [np.unique(r) for r in idx.cpu().numpy()]
-    rng = np.random.default_rng(20240607)
-    res = {}
-    for label, hit in (("cold", None), ("hit100", 1.0), ("hit75", 0.75), ("hit0", 0.0)):
-        ids = None
-        if hit is not None:
-            lists = []
-            for ch in chosen:
-                keep = int(round(hit * len(ch)))
-                pool = np.setdiff1d(np.arange(wl.E), ch)
-                wrong = rng.choice(pool, len(ch) - keep, replace=False)
-                lists.append(np.concatenate([ch[:keep], wrong, np.arange(wl.E, wl.E + wl.S)]))
-            width = max(len(l) for l in lists)
-            pad = np.full((n, width), -1, dtype=np.int32)   # -1 is skipped by the prefetch
-            for i, l in enumerate(lists):
-                pad[i, :len(l)] = l
-            ids = torch.from_numpy(pad).to(dev)
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    def run(guess):
+        idx = torch.empty((n, 1, wl.K), dtype=torch.int32, device=dev)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
         torch.cuda.synchronize()
         for i in range(n):
-            evs[i][0].record()
-            if ids is not None:
-                md.check(md.moe_expert_prefetch(d, lws[i % nl], ids[i], ids.shape[1]))
-            evs[i][1].record()
-            layer(i)
-            evs[i][2].record()
+            ev[i][0].record()
+            if guess is not None and i >= nl:
+                md.check(md.moe_expert_prefetch(d, lws[i % nl], guess[i], guess.shape[1]))
+            ev[i][1].record()
+            md.check(md.moe_layer_chain(d, 1, [lws[i % nl]], xs[i // nl], out, md.MOE_OUT_BF16,
+                                        md.MOE_CHAIN_LAYER_ONLY, idx[i], ws))
+            ev[i][2].record()
         torch.cuda.synchronize()
         md.check(md.moe_last_device_status(ws))
-        lay = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(warmup, n)]) * 1e3
-        pf = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(warmup, n)]) * 1e3
-        r = {"layer_us_mean": float(lay.mean()), "layer_us_median": float(np.median(lay))}
-        if ids is not None:
-            nb = float(np.mean([len(l) for l in lists])) * wl.expert_bytes()
-            r.update({"prefetch_us_mean": float(pf.mean()), "prefetch_bytes": nb,
-                      "prefetch_gbs": float(nb / (pf.mean() * 1e-6) / 1e9)})
-        res[label] = r
-    res["saving_us_at_hit100"] = res["cold"]["layer_us_mean"] - res["hit100"]["layer_us_mean"]
+        pf = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(nl, n)]) * 1e3
+        lay = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(nl, n)]) * 1e3
+        return idx.view(n, wl.K).cpu().numpy(), pf, lay
 
-    # Overlapped: the next call's experts (a correct guess, plus the shared expert)
-    # prefetched on a second stream while the current call runs; the next call
-    # waits for that prefetch.  Against the same loop with no prefetch.
-    nxt = np.full((n, max(len(c) for c in chosen) + wl.S), -1, dtype=np.int32)
-    for i, ch in enumerate(chosen):
-        row = np.concatenate([ch, np.arange(wl.E, wl.E + wl.S)])
-        nxt[i, :len(row)] = row
-    nxt = torch.from_numpy(nxt).to(dev)
-    main = torch.cuda.current_stream()
-    side = torch.cuda.Stream()
-    for label, with_pf in (("pipelined_no_prefetch", False), ("pipelined_prefetch_next", True)):
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for i in range(n):
-            if i == warmup:
-                e0.record(main)
-            go = torch.cuda.Event()
-            go.record(main)
-            layer(i)
-            if with_pf and i + 1 < n:
-                side.wait_event(go)
-                md.check(md.moe_expert_prefetch(d, lws[(i + 1) % nl], nxt[i + 1], nxt.shape[1],
-                                                stream=side.cuda_stream))
-                done = torch.cuda.Event()
-                done.record(side)
-                main.wait_event(done)
-        e1.record(main)
-        torch.cuda.synchronize()
-        md.check(md.moe_last_device_status(ws))
-        res[label + "_us_per_layer"] = e0.elapsed_time(e1) * 1e3 / calls
+    ids, _, cold = run(None)
+    chosen = [np.unique(r) for r in ids]
+
+    def guess_table(src):
+        t = np.full((n, wl.K + wl.S), -1, dtype=np.int32)   # -1 entries are skipped
+        for i in range(nl, n):
+            row = np.concatenate([chosen[src(i)], shared])
+            t[i, :len(row)] = row
+        return torch.from_numpy(t).to(dev)
+
+    hits = [len(np.intersect1d(chosen[i - nl], chosen[i])) / len(chosen[i]) for i in range(nl, n)]
+    res = {"rho": rho, "steps": n_steps, "layers": nl, "timed_calls": n - nl,
+           "hit_rate_previous_step": float(np.mean(hits)),
+           "cold_layer_us": float(cold.mean())}
+    same = True
+    for label, src in (("previous", lambda i: i - nl), ("exact", lambda i: i)):
+        g = guess_table(src)
+        ids2, pf, lay = run(g)
+        same = same and bool(np.array_equal(ids2, ids))
+        nb = wl.expert_bytes() * float(np.mean([(g[i] >= 0).sum().item() for i in range(nl, n)]))
+        res[label] = {"prefetch_us": float(pf.mean()), "layer_us": float(lay.mean()),
+                      "total_us": float(pf.mean() + lay.mean()),
+                      "saving_us": float(cold.mean() - pf.mean() - lay.mean()),
+                      "prefetch_gbs": float(nb / (pf.mean() * 1e-6) / 1e9)}
+    res["routing_identical_in_all_passes"] = same
     return res
 
 
@@ -734,51 +765,112 @@ def kernel_source_sha():
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(seconds):
-    """The oracle as it stands, on the host cores, over a bounded sample of the
-    headline workload (Ling layer, M=1); weight generation is not timed."""
+def cpu_baseline(seconds, chain_probe=None):
+    """The oracle as it stands, on the host cores, over bounded samples; weight
+    generation is never timed.
+
+    value: the headline workload (Ling layer, M=1) on every core, as GB/s of the
+    unique weight bytes a call needs.  extra: the same layer at M=6 on every core;
+    single-thread figures for the tiny layer and the Ling layer at M=1; and one
+    16-layer pre-norm chain + lm_head at M=6 on every core, on the rows of the GPU
+    chain's probe call, with the oracle's tokens and routing set against the GPU's."""
     import numpy as np
 
     import oracle
-    from oracle import runner
     from datagen import workloads as W
 
-    wl = W.C2
     cores = len(os.sched_getaffinity(0))
+
+    def pool_of(wl, n):
+        # n problems, each on its own layer and input rows, with the selected
+        # experts' weights generated once
+        pool = []
+        for l in range(n):
+            x = W.x_rows(wl, [1000 + l * wl.M + m for m in range(wl.M)])
+            wr = W.router(wl, l)
+            idx, _, _ = oracle.router_topk(x, wr, wl.K)
+            used = sorted(set(int(e) for e in idx.ravel())) + list(range(wl.E, wl.E + wl.S))
+            gu = {e: W.expert_gate_up(wl, l, e) for e in used}
+            dn = {e: W.expert_down(wl, l, e) for e in used}
+            pool.append((x, wr, gu, dn, wl.router_bytes() + len(used) * wl.expert_bytes()))
+        return pool
+
+    def run(wl, pool, budget, threads):
+        oracle.set_threads(threads)
+        times, nbytes = [], []
+        s = 0
+        while sum(times) < budget or s < 2:
+            x, wr, gu, dn, nb = pool[s % len(pool)]
+            t0 = time.perf_counter()
+            idx, gate, _ = oracle.router_topk(x, wr, wl.K)
+            acc = oracle.experts_combine(x, idx, gate, gu, dn, wl.E, wl.S)
+            oracle.cast_bf16(acc)
+            times.append(time.perf_counter() - t0)
+            nbytes.append(nb)
+            s += 1
+        t = np.array(times)
+        return {"calls": len(t), "us_per_layer": round(float(t.mean() * 1e6), 1),
+                "gbs": round(float(np.sum(nbytes) / t.sum() / 1e9), 3), "threads": threads,
+                "seconds": round(float(t.sum()), 2)}
+
+    # headline workload: ~1.7 GB of weights over 16 problems, well beyond the host caches
+    p2 = pool_of(W.C2, N_LAYERS)
+    head = run(W.C2, p2, 0.5 * seconds, cores)
+    extra = {W.C2.name + "_1thread": run(W.C2, p2, 0.2 * seconds, 1)}
+    del p2
+    p1 = pool_of(W.C1, N_LAYERS)
+    extra[W.C1.name + "_1thread"] = run(W.C1, p1, 0.05 * seconds, 1)
+    p3 = pool_of(W.C3, 4)
+    extra[W.C3.name] = run(W.C3, p3, 0.25 * seconds, cores)
+    del p3
+    if chain_probe is not None:
+        extra[W.C5.name] = _cpu_chain(W.C5, chain_probe, cores)
+    return {"value": head["gbs"], "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "us_per_layer": head["us_per_layer"],
+            "sample": "%d Ling MoE layer calls at M=1 (router, top-k, 8 routed + shared experts, "
+                      "combine) cycling over 16 pre-generated problems, %.1f s of oracle time; "
+                      "extra: the same at M=6, single-thread tiny and Ling M=1 layers, one "
+                      "16-layer chain + lm_head at M=6" % (head["calls"], head["seconds"]),
+            "extra": extra}
+
+
+def _cpu_chain(wl, probe, cores):
+    """One free-running oracle chain (pre-norm, residual, 16 layers, then the lm_head
+    argmax) on the probe's rows, composed as the oracle's own chain runner composes it;
+    only the arithmetic is timed.  Reports the first layer whose routing differs from
+    the GPU's (as sets per row) and how many of the tokens agree."""
+    import numpy as np
+
+    import oracle
+    from datagen import workloads as W
+
     oracle.set_threads(cores)
-    # a pool of 16 problems (one per layer, each with its own input row and its
-    # selected experts' weights generated once), cycled until the time budget
-    # is spent: ~1.7 GB of weights, well beyond the host caches
-    pool = []
-    for l in range(N_LAYERS):
-        x = W.x_rows(wl, [1000 + l])
-        wr = W.router(wl, l)
-        idx, _, _ = oracle.router_topk(x, wr, wl.K)
-        used = sorted(set(int(e) for e in idx.ravel())) + [wl.E]
+    h = W.x_rows(wl, probe["rows"])
+    t = 0.0
+    first_diff = None
+    for l in range(wl.n_layers):
+        gain, wr, bias = W.norm_gain(wl, l), W.router(wl, l), W.router_bias(wl, l)
+        t0 = time.perf_counter()
+        u = oracle.rmsnorm(h, gain=gain) if wl.prenorm else h
+        idx, gate, _ = oracle.router_topk(u, wr, wl.K, bias)
+        t += time.perf_counter() - t0
+        used = sorted(set(int(e) for e in idx.ravel())) + list(range(wl.E, wl.E + wl.S))
         gu = {e: W.expert_gate_up(wl, l, e) for e in used}
         dn = {e: W.expert_down(wl, l, e) for e in used}
-        pool.append((x, wr, gu, dn, wl.router_bytes() + len(used) * wl.expert_bytes()))
-    times, nbytes = [], []
-    t_total = 0.0
-    s = 0
-    while t_total < seconds:
-        x, wr, gu, dn, nb = pool[s % len(pool)]
         t0 = time.perf_counter()
-        idx, gate, _ = oracle.router_topk(x, wr, wl.K)
-        acc = oracle.experts_combine(x, idx, gate, gu, dn, wl.E, wl.S)
-        oracle.cast_bf16(acc)
-        dt = time.perf_counter() - t0
-        times.append(dt)
-        nbytes.append(nb)
-        t_total += dt
-        s += 1
-    times = np.array(times)
-    gbs = float(np.sum(nbytes) / np.sum(times) / 1e9)
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "us_per_layer": round(float(times.mean() * 1e6), 1),
-            "sample": "%d Ling MoE layer calls at M=1 (router, top-k, 8 routed + shared "
-                      "experts, combine) cycling over 16 pre-generated problems; %.1f s of "
-                      "oracle time" % (len(times), times.sum())}
+        acc = oracle.experts_combine(u, idx, gate, gu, dn, wl.E, wl.S, wl.routed_scale)
+        h = oracle.residual(h, acc)
+        t += time.perf_counter() - t0
+        if first_diff is None and not all(
+                set(idx[m].tolist()) == set(probe["idx"][l, m].tolist()) for m in range(wl.M)):
+            first_diff = l
+    lm = W.lmhead(wl)
+    t0 = time.perf_counter()
+    tok, _ = oracle.lmhead_argmax(h, lm)
+    t += time.perf_counter() - t0
+    return {"us_per_step": round(t * 1e6, 1), "threads": cores,
+            "tokens_equal_to_gpu": "%d/%d" % (int(np.sum(tok == probe["tokens"])), wl.M),
+            "first_layer_routing_differs_from_gpu": first_diff}
 
 
 if __name__ == "__main__":

@@ -188,3 +188,42 @@ def lmhead(wl):
 def lmhead_rows(wl, v0, n):
     k = key(WEIGHT_SEED, wl.family, 0, TENSOR_LMHEAD)
     return fill_host(k, n, wl.H, SIGMA_W, row0=v0, ld_full=wl.H)
+
+
+# ---- correlated inputs -------------------------------------------------------
+# The rows above are independent, which makes routing ~uniform and unrelated from
+# one call to the next: the worst case for bytes and for any guess of the next
+# routing.  Real decode is correlated in time and within a batch.  These two
+# generators mix a base row with fresh N(0, 1) rows, x = bf16(rho * base +
+# sqrt(1 - rho^2) * z), which keeps every row ~N(0, 1); they draw on attempts
+# far above any used by x_rows.
+
+_WALK_ATTEMPT = 1 << 20
+_BATCH_ATTEMPT = 1 << 21
+
+
+def _mix(base_bits, z_bits, rho):
+    import numpy as np
+    f = lambda b: (b.astype(np.uint32) << 16).view(np.float32)  # noqa: E731
+    return round_bf16_bits(np.float32(rho) * f(base_bits)
+                           + np.float32(np.sqrt(1.0 - rho * rho)) * f(z_bits))
+
+
+def x_walk(wl, n_steps, rho, walk=0):
+    """[n_steps][H] bf16 bits: a decode-like sequence of single rows whose step s is
+    the mix of step s-1 with a fresh row (correlation rho between consecutive steps)."""
+    import numpy as np
+    base = _WALK_ATTEMPT + walk * 4096
+    rows = [x_row(wl, 0, base)]
+    for s in range(1, n_steps):
+        rows.append(_mix(rows[-1], x_row(wl, 0, base + s), rho))
+    return np.stack(rows)
+
+
+def x_perturbed(wl, M, rho, batch=0):
+    """[M][H] bf16 bits: one base row and M perturbed copies of it (correlation rho
+    with the base, rho^2 between two rows)."""
+    import numpy as np
+    base_attempt = _BATCH_ATTEMPT + batch * 64
+    base = x_row(wl, 0, base_attempt)
+    return np.stack([_mix(base, x_row(wl, m + 1, base_attempt), rho) for m in range(M)])
