@@ -55,7 +55,6 @@ namespace moe {
 #endif
 
 constexpr int kMaxPK = MOE_MAXM * 16;  // max (routed expert, row) pairs = M * K
-constexpr int kFastRows = 8;           // rows of the threshold-and-rank top-k
 constexpr int kOwnSlots = kMaxPK + 1;  // first per-wave slot table entry (one token row)
 
 struct LayerW {
@@ -111,7 +110,7 @@ struct ParamsT {
 };
 
 struct Small {
-  int nU, nP, abort_flag, pad;
+  int nU, nP, abort_flag, sel_ok;  // sel_ok: one token row selected on the fast path
   int gu_next, dn_next, pad2[2];   // the workgroup's task tickets (gate/up, down)
   int tk_idx[kMaxPK];
   float tk_gate[kMaxPK];
@@ -124,9 +123,7 @@ struct Small {
   uint32_t bm[32];           // expert bitmap (E <= 1024)
   int bpre[32];              // population-count prefix per bitmap word
   float rn[MOE_MAXM];        // RMSNorm scale per token row
-  alignas(16) uint32_t gmax[kFastRows * MOE_WAVES];  // top-k: group maxima per row
-  int ccount[kFastRows];                 // top-k: candidates per row
-  alignas(16) uint64_t cand[kFastRows * 64];  // top-k: (key << 32 | ~expert) candidates
+  alignas(16) uint64_t cand[MOE_WAVES * 128];  // top-k: each wave's candidates + spare slots
   uint16_t hres[MOE_MAXM * 64];  // residual input h_l of this workgroup's output rows
 };
 
@@ -501,15 +498,10 @@ __device__ __forceinline__ void compute_down8(const DownRegs8<C, DB>& r, int I8,
 // K = 8 from section "The model".  The selection order is: larger logit first,
 // lower expert index first among equal logits.
 //
-// Fast path (E <= 512 experts, one per thread, and K no larger than the number
-// of 64-expert groups): every wave takes the maximum of its group of 64
-// experts for each row; the smallest of a row's group maxima, tau, has at
-// least (groups) >= K experts at or above it, so the row's K winners are among
-// the experts with key >= tau.  Those candidates (typically 10-20 of 512) are
-// compacted into LDS and each one's rank is counted directly against the
-// others; ranks below K are the selection.  No step is a serial round over K.
-// A row with more than 64 candidates, and every row outside the fast path's
-// shapes, takes the plain method: K rounds of a wave-wide maximum.
+// Fast path (E = 512, K <= 8): one wave selects a row alone, with no barrier
+// and no atomic (select_row_wave below).  Every other shape, and a row whose
+// candidates do not fit one per lane, takes the plain method: K rounds of a
+// wave-wide maximum.
 //
 // K rounds over one row held by one wave, PER keys per lane in lane-major
 // blocks (lane L holds experts L*PER .. L*PER+PER-1); key 0 marks "no expert".
@@ -564,108 +556,109 @@ __device__ __forceinline__ void gates_from_idx(const float* lr, int K, Small* sm
   if (lane < K) sm->tk_gate[m * K + lane] = pk / s;
 }
 
-// Fast path for exactly MM token rows (see above).
-template <int MM>
-__device__ __forceinline__ void topk_fast(const float* lgs, float bv, Small* sm, int E, int K,
-                                          int nW, int tid, int wv, int lane) {
-  // (a) every wave: its group maximum, for every row (scores = logit + this
-  //     thread's expert bias, 0 without one)
-  uint32_t key[MM];
+// One row's selection by one wave, with no barrier and no atomic.  Lane l holds
+// the scores of experts 8l .. 8l+7 (E = 512), so an 8-lane group holds 64
+// experts.  The smallest of the eight group maxima, tau, has at least eight
+// scores at or above it, so for K <= 8 the row's K winners are among the scores
+// >= tau.  Those candidates (typically 20-30 of 512) are packed into this wave's
+// LDS area as (key << 32 | ~expert), an order in which no two are equal and the
+// larger comes first in the selection (higher score, then lower index).  Lane c
+// takes candidate c and counts the candidates above it: its rank.  Returns false,
+// having changed nothing but the wave's LDS area, when the candidates do not
+// fit one per lane or are fewer than K (only NaN scores make them fewer); the
+// caller then takes the plain rounds.  On success lane k < K holds the rank-k
+// expert in e_k.  cw: 128 entries of this wave (the candidates, then one spare
+// slot per lane).
+__device__ __forceinline__ bool select_row_wave(const float* lr, const float (&bl)[8], int K,
+                                                uint64_t* cw, int lane, int& e_k) {
+  const float4 a = reinterpret_cast<const float4*>(lr)[2 * lane];
+  const float4 b = reinterpret_cast<const float4*>(lr)[2 * lane + 1];
+  const float s[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t key[8];
 #pragma unroll
-  for (int m = 0; m < MM; ++m) key[m] = tid < E ? f_key(lgs[m * E + tid] + bv) : 0u;
-  uint32_t mine = 0u;
+  for (int i = 0; i < 8; ++i) key[i] = f_key(s[i] + bl[i]);
+  uint32_t lm = key[0];
 #pragma unroll
-  for (int m = 0; m < MM; ++m) {
-    const uint32_t gm = wave_max_u32(key[m]);
-    mine = lane == m ? gm : mine;
+  for (int i = 1; i < 8; ++i) lm = max(lm, key[i]);
+  // maximum of the 8-lane group (quad swaps, then the half-row mirror)
+  lm = max(lm, dpp_u<0xB1>(lm));
+  lm = max(lm, dpp_u<0x4E>(lm));
+  lm = max(lm, dpp_u<0x141>(lm));
+  const uint32_t tau = ~wave_max_u32(~lm);  // the smallest group maximum
+  uint32_t bits = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) bits |= (key[i] != 0u && key[i] >= tau) ? (1u << i) : 0u;
+  const int c = __builtin_popcount(bits);
+  const int incl = wave_incl_scan(c);
+  const int n = __builtin_amdgcn_readlane(incl, 63);
+  if (n < K || n > 64) return false;
+  const int base = incl - c;
+  // every lane stores all eight keys: candidates at their packed place, the
+  // others into the lane's spare slot (no branch per key)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool cnd = (bits >> i) & 1u;
+    const int at = cnd ? base + __builtin_popcount(bits & ((1u << i) - 1u)) : 64 + lane;
+    cw[at] = ((uint64_t)key[i] << 32) | (uint64_t)(uint32_t)~(8 * lane + i);
   }
-  if (lane < MM) sm->gmax[lane * MOE_WAVES + wv] = mine;
-  if (tid < kFastRows) sm->ccount[tid] = 0;
-  __syncthreads();
-  // (b) lane m: tau of row m = its smallest group maximum; every row's
-  //     candidates (key >= tau) are packed as (key << 32 | ~expert), so that
-  //     one unsigned 64-bit comparison orders them as the selection does
-  uint32_t tau_l = 0u;
-  if (lane < MM) {
-    const uint4 ga = *reinterpret_cast<const uint4*>(sm->gmax + lane * MOE_WAVES);
-    const uint4 gb = *reinterpret_cast<const uint4*>(sm->gmax + lane * MOE_WAVES + 4);
-    const uint32_t g8[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
-    tau_l = g8[0];
-#pragma unroll
-    for (int w = 1; w < 8; ++w) tau_l = w < nW ? min(tau_l, g8[w]) : tau_l;
-  }
-  uint64_t ball[MM];
-  int cnt = 0;
-#pragma unroll
-  for (int m = 0; m < MM; ++m) {
-    const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)tau_l, m);
-    ball[m] = __ballot(key[m] != 0u && key[m] >= tau);
-    cnt = lane == m ? (int)__builtin_popcountll(ball[m]) : cnt;
-  }
-  const int base = lane < MM ? atomicAdd(&sm->ccount[lane], cnt) : 0;
-#pragma unroll
-  for (int m = 0; m < MM; ++m) {
-    const int pos = __builtin_amdgcn_readlane(base, m) +
-                    (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(ball[m] >> 32),
-                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)ball[m], 0u));
-    if (((ball[m] >> lane) & 1ull) && pos < 64)
-      sm->cand[m * 64 + pos] = ((uint64_t)key[m] << 32) | (uint64_t)(uint32_t)~tid;
-  }
-  __syncthreads();
-}
-
-// Lane c < n takes candidate c of a row (cr: its n packed candidates) and
-// counts the candidates that precede it in the selection order: its rank.
-__device__ __forceinline__ int rank_candidates(const uint64_t* cr, int n, int lane,
-                                               uint64_t& mine) {
-  mine = lane < n ? cr[lane] : 0ull;
+  const int n8 = (n + 7) & ~7;
+  if (lane >= n && lane < n8) cw[lane] = 0ull;  // zero padding: never above a candidate
+  const uint64_t mine = lane < n ? cw[lane] : 0ull;
+  // rank: candidates above this one, eight at a time, the next eight in flight
   int rank = 0;
+  const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(cw);
+  ulonglong2 q0 = c2[0], q1 = c2[1], q2 = c2[2], q3 = c2[3];
 #pragma unroll 1
-  for (int j = 0; j < n; j += 8) {
-    const ulonglong2 c0 = *reinterpret_cast<const ulonglong2*>(cr + j);
-    const ulonglong2 c1 = *reinterpret_cast<const ulonglong2*>(cr + j + 2);
-    const ulonglong2 c2 = *reinterpret_cast<const ulonglong2*>(cr + j + 4);
-    const ulonglong2 c3 = *reinterpret_cast<const ulonglong2*>(cr + j + 6);
-    const uint64_t c8[8] = {c0.x, c0.y, c1.x, c1.y, c2.x, c2.y, c3.x, c3.y};
+  for (int j = 0; j < n8; j += 8) {
+    const uint64_t c8[8] = {q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
+    if (j + 8 < n8) {
+      q0 = c2[(j >> 1) + 4];
+      q1 = c2[(j >> 1) + 5];
+      q2 = c2[(j >> 1) + 6];
+      q3 = c2[(j >> 1) + 7];
+    }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) rank += (j + q < n && c8[q] > mine) ? 1 : 0;
+    for (int q = 0; q < 8; ++q) rank += c8[q] > mine ? 1 : 0;
   }
-  return rank;
+  // rank-k expert -> lane k, through the spare slots (free again)
+  int* ek = reinterpret_cast<int*>(cw + 64);
+  if (lane < n && rank < K) ek[rank] = (int)~(uint32_t)mine;
+  e_k = lane < K ? ek[lane] : -1;
+  return true;
 }
 
-// bv: the selection bias of expert tid (0 without a bias), loaded before the
-// logits arrive; bias: the bias vector for the plain path (or null).
+// Gate of the rank-k expert held by lane k < K, computed as gates_from_idx
+// computes it from the LDS table (shift by the rank-0 logit, sum over the K
+// lanes, divide); 0 on the other lanes.
+__device__ __forceinline__ float gate_of_rank(const float* lr, int K, int e_k, int lane) {
+  const float lk = lane < K ? lr[e_k] : 0.0f;
+  const float v0 = readlane_f(lk, 0);
+  const float pk = lane < K ? expf(lk - v0) : 0.0f;
+  const float s = group_sum(pk, 64);
+  return lane < K ? pk / s : 0.0f;
+}
+
+// Every row's selection and gates: wave w takes rows w, w + 8, ...  bl: this
+// lane's selection biases of experts 8 * lane .. 8 * lane + 7 (zeros without a
+// bias), loaded before the logits arrive; bias: the bias vector for the plain
+// path (or null).
 template <class P>
-__device__ __forceinline__ void topk_rows(const P& p, const float* lgs, float bv,
-                                          const float* bias, Small* sm, int tid, int wv,
-                                          int lane) {
+__device__ __forceinline__ void topk_rows(const P& p, const float* lgs, const float (&bl)[8],
+                                          const float* bias, Small* sm, int wv, int lane) {
   const int M = p.M, E = p.E, K = p.K;
-  const int nW = (E + 63) >> 6;
-  const bool fast = M <= kFastRows && E <= MOE_WG && K <= nW;
-  if (fast) {
-    switch (M) {
-      case 1: topk_fast<1>(lgs, bv, sm, E, K, nW, tid, wv, lane); break;
-      case 2: topk_fast<2>(lgs, bv, sm, E, K, nW, tid, wv, lane); break;
-      case 3: topk_fast<3>(lgs, bv, sm, E, K, nW, tid, wv, lane); break;
-      case 4: topk_fast<4>(lgs, bv, sm, E, K, nW, tid, wv, lane); break;
-      case 5: topk_fast<5>(lgs, bv, sm, E, K, nW, tid, wv, lane); break;
-      case 6: topk_fast<6>(lgs, bv, sm, E, K, nW, tid, wv, lane); break;
-      case 7: topk_fast<7>(lgs, bv, sm, E, K, nW, tid, wv, lane); break;
-      default: topk_fast<8>(lgs, bv, sm, E, K, nW, tid, wv, lane); break;
-    }
-  }
-  // (c) one wave per row: rank the candidates, or K plain rounds
+  const bool fast = E == 512 && K <= 8;
   for (int m = wv; m < M; m += MOE_WAVES) {
-    const int n = fast ? sm->ccount[m] : 0;
-    if (n >= K && n <= 64) {
-      uint64_t mine;
-      const int rank = rank_candidates(sm->cand + m * 64, n, lane, mine);
-      if (lane < n && rank < K) sm->tk_idx[m * K + rank] = (int)~(uint32_t)mine;
-      // gates in rank order (the candidates' lane order depends on timing)
-      gates_from_idx(lgs + m * E, K, sm, m, lane);
+    const float* lr = lgs + m * E;
+    int ek;
+    if (fast && select_row_wave(lr, bl, K, sm->cand + wv * 128, lane, ek)) {
+      const float gk = gate_of_rank(lr, K, ek, lane);
+      if (lane < K) {
+        sm->tk_idx[m * K + lane] = ek;
+        sm->tk_gate[m * K + lane] = gk;
+      }
     } else {
-      select_row_plain(lgs + m * E, bias, E, K, sm->tk_idx + m * K, lane);
-      gates_from_idx(lgs + m * E, K, sm, m, lane);
+      select_row_plain(lr, bias, E, K, sm->tk_idx + m * K, lane);
+      gates_from_idx(lr, K, sm, m, lane);
     }
   }
 }
@@ -921,7 +914,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     // ---------------- P4: routing
     // one token row (K <= 8): the routed slots are the ranks (see P5)
     const bool one_row = M == 1 && K <= 8 && !topk_in && !router_only;
-    bool ranked = false;  // one row ranked by every wave, slot tables filled
+    bool ranked = false;  // one row selected on the fast path, slot tables filled
     if (topk_in) {
       for (int i = tid; i < MK; i += MOE_WG) {
         int e = p.tk_idx_in[i];
@@ -934,9 +927,12 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       }
       __syncthreads();
     } else {
-      // the selection bias does not depend on the logits: load it before waiting
+      // the selection bias does not depend on the logits: this lane's eight
+      // (experts 8 * lane .. 8 * lane + 7) are loaded before waiting
       const float* bias = p.lw[l].bias;
-      const float bv = (bias && tid < E) ? bias[tid] : 0.0f;
+      float bl[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bl[i] = (bias && E == 512) ? bias[8 * lane + i] : 0.0f;
       const uint64_t* src = p.lg_buf + (size_t)l * M * E;
       if (!stage_tagged<8>(M * E, reinterpret_cast<uint32_t*>(lgs), tag, wt, tid,
                            [&](int i) { return src + i; }))
@@ -944,55 +940,48 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       __syncthreads();
       MOE_STAMP(3);
       if (sm->abort_flag == 1) break;
-      // One token row on the threshold path: every wave ranks the candidates
-      // itself and fills its own slot table (slot r = rank r); only wave 0
-      // goes on to the gates and the workgroup's tables (read after the
-      // barrier that opens the down projection), so no barrier follows the
-      // selection.  A row with more than 64 candidates takes the plain path.
-      const int nWg = (E + 63) >> 6;
-      if (one_row && E <= MOE_WG && K <= nWg) {
-        topk_fast<1>(lgs, bv, sm, E, K, nWg, tid, wv, lane);
-        const int n = sm->ccount[0];
-        if (n >= K && n <= 64) {
-          ranked = true;
+      // One token row: wave 0 selects alone and fills the workgroup's slot
+      // tables (slot r = rank r); one barrier publishes them.  The selection is
+      // a chain of dependent wave-wide steps, and a second wave on the same
+      // SIMD would only halve its issue rate.  A row whose candidates do not
+      // fit one per lane takes the plain path below.
+      if (one_row && E == 512) {
+        if (wv == 0) {
           int ln = lane;  // opaque lane number (no hoisted lane-dependent addresses)
           asm volatile("" : "+v"(ln));
-          uint64_t mine;
-          const int rank = rank_candidates(sm->cand, n, ln, mine);
-          const bool sel = ln < n && rank < K;
-          const int e = (int)~(uint32_t)mine;
-          if (sel) {
-            sm->uexp[kOwnSlots + wv * 8 + rank] = e;
-            sm->umask[kOwnSlots + wv * 8 + rank] = 1u;
-            sm->pbase[kOwnSlots + wv * 8 + rank] = rank;
-          }
-          if (wv == 0) {
-            if (sel) {
-              sm->tk_idx[rank] = e;
-              sm->uexp[rank] = e;
-              sm->umask[rank] = 1u;
-              sm->pbase[rank] = rank;
+          int ek;
+          const bool ok = select_row_wave(lgs, bl, K, sm->cand, ln, ek);
+          if (ok) {
+            const float gk = gate_of_rank(lgs, K, ek, ln);
+            if (ln < K) {
+              sm->tk_idx[ln] = ek;
+              sm->tk_gate[ln] = gk;
+              sm->uexp[ln] = ek;
+              sm->umask[ln] = 1u;
+              sm->pbase[ln] = ln;
+              sm->upos[ln] = ln;
             }
-            gates_from_idx(lgs, K, sm, 0, ln);
-            if (ln < K) sm->upos[ln] = ln;
             if (ln == 0) {
               sm->nU = K;
               sm->nP = K;
             }
             if (g == 0 && ln < K) {
-              if (p.tk_idx_out) p.tk_idx_out[(size_t)l * MK + ln] = sm->tk_idx[ln];
-              if (p.tk_gate_out && l == 0) p.tk_gate_out[ln] = sm->tk_gate[ln];
+              if (p.tk_idx_out) p.tk_idx_out[(size_t)l * MK + ln] = ek;
+              if (p.tk_gate_out && l == 0) p.tk_gate_out[ln] = gk;
             }
           }
+          if (ln == 0) sm->sel_ok = ok ? 1 : 0;
+        }
+        __syncthreads();
+        ranked = sm->sel_ok != 0;
+        if (ranked) {
           if (g == 0 && p.logits_out && l == 0)
             for (int i = tid; i < E; i += MOE_WG) p.logits_out[i] = lgs[i];
           MOE_STAMP(9);
-        } else {
-          __syncthreads();  // every wave has read the candidate count
         }
       }
       if (!ranked) {
-        topk_rows(p, lgs, bv, bias, sm, tid, wv, lane);
+        topk_rows(p, lgs, bl, bias, sm, wv, lane);
         __syncthreads();
         MOE_STAMP(9);
         if (g == 0 || router_only) {
@@ -1010,11 +999,12 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
 
     // ---------------- P5: routed slots
     // One token row (K <= 8): the routed slots are the ranks (slot r = rank r,
-    // one row each), so there is nothing to merge.  Each wave copies the
-    // selection into its own slot table, which only it reads, so no barrier
-    // stands between the selection and the routed gate/up stream; wave 0 fills
-    // the workgroup's tables, which the down projection and the combine read
-    // after the barrier that opens the down projection.
+    // one row each), so there is nothing to merge.  On the fast path wave 0 has
+    // filled the workgroup's tables already.  After the plain path each wave
+    // copies the selection into its own slot table, which only it reads, so no
+    // barrier stands between the selection and the routed gate/up stream; wave 0
+    // fills the workgroup's tables, which the down projection and the combine
+    // read after the barrier that opens the down projection.
     int U;
     if (ranked) {
       U = K;
@@ -1060,8 +1050,9 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     {
       const int H8 = H >> 3;
       // one task: SwiGLU of gate/up row pairs (2jp, 2jp + 1) for every row that chose slot rr
-      // the slot tables: the workgroup's, or with one token row this wave's own
-      const int so = one_row ? kOwnSlots + wv * 8 : 0;
+      // the slot tables: the workgroup's, or with one token row off the fast
+      // path this wave's own
+      const int so = (one_row && !ranked) ? kOwnSlots + wv * 8 : 0;
       auto emit_task = [&](const RowRegs<CPLH>& X, const RowRegs<CPLH>& Y,
                            const float (&S)[Fp8Row<CPLH>::C], int jp, int rr)
                            __attribute__((always_inline)) {
