@@ -744,6 +744,37 @@ __device__ __forceinline__ bool slice_piece(int g, int G, int U, int I, int H, i
   return true;
 }
 
+// Routed part of the combine for token row m and output rows (nl, nl + 1):
+// q = sum over k < K, in order, of gate_k * y(slot of rank k), skipping a rank
+// with no slot.  Every index is read before any value is summed (ranks past K
+// repeat rank K - 1 and are not summed), so the three dependent LDS reads of a
+// rank overlap across the ranks instead of following one another.
+template <int KM>
+__device__ __forceinline__ void routed_sum(const Small* sm, const float* ysr, int K, int m, int NR,
+                                           int nl, float& q0, float& q1) {
+  int pr[KM];
+  float gk[KM];
+  bool ok[KM];
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    const int kk = k < K ? k : K - 1;
+    const int r = sm->upos[m * K + kk];
+    ok[k] = k < K && r >= 0;
+    const int rr = r >= 0 ? r : 0;
+    const int pv = sm->pbase[rr] + __builtin_popcount(sm->umask[rr] & ((1u << m) - 1u));
+    pr[k] = ok[k] ? pv : 0;
+    gk[k] = sm->tk_gate[m * K + kk];
+  }
+  q0 = 0.0f;
+  q1 = 0.0f;
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    const float y0 = ysr[pr[k] * NR + nl], y1 = ysr[pr[k] * NR + nl + 1];
+    q0 = ok[k] ? q0 + gk[k] * y0 : q0;
+    q1 = ok[k] ? q1 + gk[k] * y1 : q1;
+  }
+}
+
 // ---------------------------------------------------------------- the kernel
 
 // W8: expert weights are fp8 e4m3 codes with 128 x 128 block scales (the
@@ -1249,15 +1280,11 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
         const int np = i / M, m = i - np * M;
         const int nl = 2 * np, n = n0 + nl;
         // routed sum in fp32, scaled once, then the shared expert
-        float q0 = 0.0f, q1 = 0.0f;
-        for (int k = 0; k < K; ++k) {
-          const int r = sm->upos[m * K + k];
-          if (r < 0) continue;
-          const int pr = sm->pbase[r] + __builtin_popcount(sm->umask[r] & ((1u << m) - 1u));
-          const float gk = sm->tk_gate[m * K + k];
-          q0 = q0 + gk * ysr[pr * NR + nl];
-          q1 = q1 + gk * ysr[pr * NR + nl + 1];
-        }
+        float q0, q1;
+        if (K <= 8)
+          routed_sum<8>(sm, ysr, K, m, NR, nl, q0, q1);
+        else
+          routed_sum<MOE_MAX_TOPK>(sm, ysr, K, m, NR, nl, q0, q1);
         const float a0 = (S ? ysh[m * p.nr_max + nl] : 0.0f) + p.scale * q0;
         const float a1 = (S ? ysh[m * p.nr_max + nl + 1] : 0.0f) + p.scale * q1;
         if (p.flags & F_RESIDUAL) {
