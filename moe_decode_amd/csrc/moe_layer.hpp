@@ -676,14 +676,20 @@ __device__ __forceinline__ void build_union(const P& p, Small* sm, int wv, int l
     asm volatile("" : "+v"(lane_o));
     const int lane = lane_o;
     const int MK = p.M * p.K;
+    // passes of 64 entries that hold any (row, rank) entry: one up to M * K = 64
+    const int NJ = (MK + 63) >> 6;
     if (lane < 32) sm->bm[lane] = 0u;
 #pragma unroll
-    for (int j = 0; j < NE; ++j) sm->umask[lane + 64 * j] = 0u;
+    for (int j = 0; j < NE; ++j)
+      if (j < NJ) sm->umask[lane + 64 * j] = 0u;
     int e[NE];
 #pragma unroll
     for (int j = 0; j < NE; ++j) {
-      e[j] = lane + 64 * j < MK ? sm->tk_idx[lane + 64 * j] : -1;
-      if (e[j] >= 0) atomicOr(&sm->bm[e[j] >> 5], 1u << (e[j] & 31));
+      e[j] = -1;
+      if (j < NJ) {
+        e[j] = lane + 64 * j < MK ? sm->tk_idx[lane + 64 * j] : -1;
+        if (e[j] >= 0) atomicOr(&sm->bm[e[j] >> 5], 1u << (e[j] & 31));
+      }
     }
     const uint32_t w = lane < 32 ? sm->bm[lane] : 0u;
     const int c = __builtin_popcount(w);
@@ -694,6 +700,7 @@ __device__ __forceinline__ void build_union(const P& p, Small* sm, int wv, int l
     // routed slot of each entry = number of selected experts below it
 #pragma unroll
     for (int j = 0; j < NE; ++j) {
+      if (j >= NJ) break;
       int r = -1;
       if (e[j] >= 0) {
         r = sm->bpre[e[j] >> 5] + __builtin_popcount(sm->bm[e[j] >> 5] & ((1u << (e[j] & 31)) - 1u));
@@ -702,10 +709,11 @@ __device__ __forceinline__ void build_union(const P& p, Small* sm, int wv, int l
       }
       if (lane + 64 * j < MK) sm->upos[lane + 64 * j] = r;
     }
-    // first (slot, row) pair of every slot
+    // first (slot, row) pair of every slot (U <= M * K: no more passes than above)
     int run = 0;
 #pragma unroll
     for (int j = 0; j < NE; ++j) {
+      if (j >= NJ) break;
       const int cj = lane + 64 * j < U ? __builtin_popcount(sm->umask[lane + 64 * j]) : 0;
       const int ij = wave_incl_scan(cj);
       sm->pbase[lane + 64 * j] = run + ij - cj;
