@@ -247,11 +247,12 @@ int check_expert_scales(const moe_dims& d, const moe_layer_weights& w) {
 }
 
 // Workspace regions after the header (all tagged 64-bit words):
-//   lg  [L][M][E]        router logits
-//   hs  [L][M][I/2]      shared expert SwiGLU output (bf16 pairs)
+//   lg  [L][kCopies][M][E]    router logits
+//   hs  [L][kCopies][M][I/2]  shared expert SwiGLU output (bf16 pairs)
 //   hr  [L][M*K][I/2]    routed (expert, row) SwiGLU outputs (bf16 pairs)
 //   y   [L][M*K][H]      routed (expert, row) down-projection outputs (fp32)
-//   res [L+1][M][H/2]    residual stream between chained layers (bf16 pairs)
+//   res [L+1][kCopies][M][H/2] residual stream between chained layers (bf16 pairs)
+// (the words every workgroup reads are kept in one copy per XCD)
 struct WsLayout {
   size_t lg, hs, hr, y, res, total;
 };
@@ -261,11 +262,12 @@ WsLayout ws_layout(const moe_dims& d, int M, int L) {
   const size_t E = (size_t)d.n_experts, H = (size_t)d.hidden, I = (size_t)d.inter;
   const size_t MK = (size_t)M * d.top_k;
   w.lg = kHdrBytes;
-  w.hs = align_up(w.lg + (size_t)L * M * E * 8, 256);
-  w.hr = align_up(w.hs + (size_t)L * M * (I / 2) * 8, 256);
+  const size_t C = (size_t)kCopies;
+  w.hs = align_up(w.lg + (size_t)L * C * M * E * 8, 256);
+  w.hr = align_up(w.hs + (size_t)L * C * M * (I / 2) * 8, 256);
   w.y = align_up(w.hr + (size_t)L * MK * (I / 2) * 8, 256);
   w.res = align_up(w.y + (size_t)L * MK * H * 8, 256);
-  w.total = align_up(w.res + (size_t)(L + 1) * M * (H / 2) * 8, 256);
+  w.total = align_up(w.res + (size_t)(L + 1) * C * M * (H / 2) * 8, 256);
   return w;
 }
 

@@ -55,6 +55,12 @@ namespace moe {
 #endif
 
 constexpr int kMaxPK = MOE_MAXM * 16;  // max (routed expert, row) pairs = M * K
+// Words that every workgroup reads (the logits, the shared expert's SwiGLU
+// row, the next layer's input) are published in kCopies copies; workgroup g
+// reads copy g % kCopies, the one of its own XCD.  When all workgroups poll
+// one copy, their reads of the same lines queue at the memory side and a
+// wave sees the last word about 0.4 us later than with one copy per XCD.
+constexpr int kCopies = 8;
 constexpr int kOwnSlots = kMaxPK + 1;  // first per-wave slot table entry (one token row)
 
 struct LayerW {
@@ -101,11 +107,11 @@ struct ParamsT {
   float* logits_out;     // [M][E]
   uint16_t* h_all;       // [L+1][M][H] residual stream per layer (optional)
   uint32_t* hdr;
-  uint64_t* lg_buf;      // [L][M][E]       tagged fp32 logits
-  uint64_t* hs_buf;      // [L][M][I/2]     tagged bf16 pairs, shared expert
+  uint64_t* lg_buf;      // [L][kCopies][M][E]   tagged fp32 logits
+  uint64_t* hs_buf;      // [L][kCopies][M][I/2] tagged bf16 pairs, shared expert
   uint64_t* hr_buf;      // [L][M*K][I/2]   tagged bf16 pairs, routed (expert, row) pairs
   uint64_t* y_buf;       // [L][M*K][H]     tagged fp32 down outputs of routed pairs
-  uint64_t* res_buf;     // [L+1][M][H/2]   tagged bf16 pairs, residual stream
+  uint64_t* res_buf;     // [L+1][kCopies][M][H/2] tagged bf16 pairs, residual stream
   LayerW lw[NL];
 };
 
@@ -362,17 +368,19 @@ __device__ __forceinline__ void p1_compute(const P& p, int l, int it, int NRI,
                                            uint32_t tag, int lane, uint32_t dbg) {
   const int H8 = p.H >> 3;
   if (it < NRI) {
-    const int e = 2 * it + (lane >> 5);
-    const bool publish =
-        e < p.E && (lane & 31) == 0 && !(dbg & DBG_NO_ROUTER_PUBLISH);
+    // every lane of a half-wave holds its row's sum: lane c < kCopies of the
+    // half writes copy c
+    const int e = 2 * it + (lane >> 5), c = lane & 31;
+    const bool publish = e < p.E && c < kCopies && !(dbg & DBG_NO_ROUTER_PUBLISH);
 #pragma unroll 1
     for (int m = 0; m < p.M; ++m) {
       const float acc = dot_rows<CPLH>(A, xs4, H8, m, lane);
-      if (publish) st_tag(p.lg_buf + ((size_t)l * p.M + m) * p.E + e, __float_as_uint(acc), tag);
+      if (publish)
+        st_tag(p.lg_buf + (((size_t)l * kCopies + c) * p.M + m) * p.E + e, __float_as_uint(acc), tag);
     }
   } else {
     const int jp = it - NRI, I2 = p.I >> 1;
-    uint64_t* dst = p.hs_buf + (size_t)l * p.M * I2 + jp;
+    uint64_t* dst = p.hs_buf + (size_t)l * kCopies * p.M * I2 + jp;
 #pragma unroll 1
     for (int m = 0; m < p.M; ++m) {
       float a0, a1;
@@ -385,7 +393,7 @@ __device__ __forceinline__ void p1_compute(const P& p, int l, int it, int NRI,
       }
       const uint32_t word = f_to_bf(swiglu(readlane_f(a0, 0), readlane_f(a0, 32))) |
                             (f_to_bf(swiglu(readlane_f(a1, 0), readlane_f(a1, 32))) << 16);
-      if (lane == 0) st_tag(dst + (size_t)m * I2, word, tag);
+      if (lane < kCopies) st_tag(dst + ((size_t)lane * p.M + m) * I2, word, tag);  // copy lane
     }
   }
 }
@@ -806,6 +814,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
 
   const int G = gridDim.x, g = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int cp = g % kCopies;  // the copy this workgroup reads (see kCopies)
   const int NW = G * MOE_WAVES;
   const int gw = wv * G + g;  // consecutive wave ids land on different CUs
   // The step tag, debug flags and deadline come with the launch: no word of
@@ -877,7 +886,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       uint4* dst = reinterpret_cast<uint4*>(xs);
       for (int i = tid; i < (M * H) >> 3; i += MOE_WG) dst[i] = src[i];
     } else {
-      const uint64_t* src = p.res_buf + (size_t)l * M * H2;
+      const uint64_t* src = p.res_buf + ((size_t)l * kCopies + cp) * M * H2;
       if (!stage_tagged<8>(M * H2, reinterpret_cast<uint32_t*>(xs), tag, wt, tid,
                            [&](int i) { return src + i; }))
         sm->abort_flag = 1;
@@ -972,7 +981,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       float bl[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) bl[i] = (bias && E == 512) ? bias[8 * lane + i] : 0.0f;
-      const uint64_t* src = p.lg_buf + (size_t)l * M * E;
+      const uint64_t* src = p.lg_buf + ((size_t)l * kCopies + cp) * M * E;
       if (!stage_tagged<8>(M * E, reinterpret_cast<uint32_t*>(lgs), tag, wt, tid,
                            [&](int i) { return src + i; }))
         sm->abort_flag = 1;
@@ -1207,7 +1216,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       const int ws0 = nbs ? M * I2 : 0;
       const int ws1 = nb0 ? nrow0 * I2 : 0;
       const int ws2 = nb1 ? nrow1 * I2 : 0;
-      const uint64_t* hsrc = p.hs_buf + (size_t)l * M * I2;
+      const uint64_t* hsrc = p.hs_buf + ((size_t)l * kCopies + cp) * M * I2;
       const uint64_t* r0src = hr_l + (size_t)(has0 ? sm->pbase[pc0.r] : 0) * I2;
       const uint64_t* r1src = hr_l + (size_t)(has1 ? sm->pbase[pc1.r] : 0) * I2;
       if (!stage_tagged<4>(ws0 + ws1 + ws2, hs32, tag, wt, tid, [&](int i) {
@@ -1299,10 +1308,13 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
           const float h0 = bf_to_f(sm->hres[m * p.nr_max + nl]);
           const float h1 = bf_to_f(sm->hres[m * p.nr_max + nl + 1]);
           const uint32_t word = f_to_bf(h0 + a0) | (f_to_bf(h1 + a1) << 16);
-          if (last)
+          if (last) {
             reinterpret_cast<uint32_t*>(p.out)[(m * H + n) >> 1] = word;
-          else
-            st_tag(p.res_buf + (size_t)(l + 1) * M * H2 + ((m * H + n) >> 1), word, tag);
+          } else {
+            uint64_t* r = p.res_buf + (size_t)(l + 1) * kCopies * M * H2 + ((m * H + n) >> 1);
+#pragma unroll
+            for (int c = 0; c < kCopies; ++c) st_tag(r + (size_t)c * M * H2, word, tag);
+          }
           if (p.h_all)
             reinterpret_cast<uint32_t*>(p.h_all)[((size_t)(l + 1) * M * H + (size_t)m * H + n) >> 1] =
                 word;

@@ -65,12 +65,13 @@ def test_workspace_size_layout_and_errors():
     def up(v):
         return (v + 255) // 256 * 256
     M, L, E, H, I, K, S = 6, 16, 512, 2560, 768, 8, 1
+    C = 8  # the words every workgroup reads: one copy per XCD
     lg = 4096 + 256 * 32 * 8 + 512 * 16 * 2 * 8   # control words, phase stamps, lm_head slots
-    hs = up(lg + L * M * E * 8)       # logits
-    hr = up(hs + L * M * (I // 2) * 8)          # shared SwiGLU pairs
+    hs = up(lg + L * C * M * E * 8)             # logits
+    hr = up(hs + L * C * M * (I // 2) * 8)      # shared SwiGLU pairs
     y = up(hr + L * M * K * (I // 2) * 8)       # routed SwiGLU pairs
     res = up(y + L * M * K * H * 8)             # routed down outputs
-    assert b6 == up(res + (L + 1) * M * (H // 2) * 8)
+    assert b6 == up(res + (L + 1) * C * M * (H // 2) * 8)
     assert md.moe_workspace_size(None, 1, 1)[0] == md.MOE_E_ARG
     assert md.moe_workspace_size(d, 0, 1)[0] == md.MOE_E_ARG
     assert md.moe_workspace_size(d, 17, 1)[0] == md.MOE_E_UNSUPPORTED
