@@ -61,6 +61,16 @@ constexpr int kMaxPK = MOE_MAXM * 16;  // max (routed expert, row) pairs = M * K
 // one copy, their reads of the same lines queue at the memory side and a
 // wave sees the last word about 0.4 us later than with one copy per XCD.
 constexpr int kCopies = 8;
+
+// Lane 0's value of v, whatever lanes are active, held in a scalar register
+// from here on (a ticket taken by lane 0 and used by the whole wave: the
+// compiler may not recompute it from the lane's register under another
+// exec mask).
+__device__ __forceinline__ int lane0_scalar(int v) {
+  int s = __builtin_amdgcn_readlane(v, 0);
+  asm volatile("" : "+s"(s));
+  return s;
+}
 constexpr int kOwnSlots = kMaxPK + 1;  // first per-wave slot table entry (one token row)
 
 struct LayerW {
@@ -117,7 +127,9 @@ struct ParamsT {
 
 struct Small {
   int nU, nP, abort_flag, sel_ok;  // sel_ok: one token row selected on the fast path
-  int gu_next, dn_next, pad2[2];   // the workgroup's task tickets (gate/up, down)
+  int gu_next, dn_next;      // the workgroup's task tickets (gate/up, down)
+  int st_next, pad2;         // staging chunks of the down inputs: next to claim
+  uint64_t st_done;          // and the chunks staged (bit c)
   int tk_idx[kMaxPK];
   float tk_gate[kMaxPK];
   int upos[kMaxPK];          // routed slot of (row, rank), -1 if skipped
@@ -157,15 +169,16 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // so a stage costs about one load latency per poll round rather than one per
 // word.  addr(i) gives the source word of element i.  Returns false on a
 // missed deadline (recorded in the workspace status).
-template <int B, typename Addr>
+// NT threads take part (tid < NT: the workgroup, or one wave with tid = lane).
+template <int B, int NT = MOE_WG, typename Addr>
 __device__ __forceinline__ bool stage_tagged(int n, uint32_t* dst32, uint32_t tag,
                                              const Waiter& wt, int tid, Addr addr) {
   const uint64_t ready = (uint64_t)tag << 32;
-  for (int base = tid; base < n; base += B * MOE_WG) {
+  for (int base = tid; base < n; base += B * NT) {
     uint64_t v[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const int i = base + b * MOE_WG;
+      const int i = base + b * NT;
       v[b] = i < n ? ld_tag(addr(i)) : ready;
     }
     for (;;) {
@@ -180,11 +193,11 @@ __device__ __forceinline__ bool stage_tagged(int n, uint32_t* dst32, uint32_t ta
       __builtin_amdgcn_s_sleep(MOE_POLL_SLEEP);
 #pragma unroll
       for (int b = 0; b < B; ++b)
-        if ((uint32_t)(v[b] >> 32) != tag) v[b] = ld_tag(addr(base + b * MOE_WG));
+        if ((uint32_t)(v[b] >> 32) != tag) v[b] = ld_tag(addr(base + b * NT));
     }
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const int i = base + b * MOE_WG;
+      const int i = base + b * NT;
       if (i < n) dst32[i] = (uint32_t)v[b];
     }
   }
@@ -880,6 +893,8 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     if (tid == 0) {
       sm->gu_next = 0;  // read after the barriers of the routing phase
       sm->dn_next = 0;
+      sm->st_next = 0;
+      sm->st_done = 0ull;
     }
     if (l == 0) {
       const uint4* src = reinterpret_cast<const uint4*>(p.x_in);
@@ -1178,8 +1193,9 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
 
     // ---------------- P7: down projection
     // This workgroup's down tasks: the shared expert's blocks of its own output
-    // rows, then its slice's blocks of the routed experts, after the SwiGLU
-    // inputs of all of them are staged in LDS with one batched wait.
+    // rows, then its slice's blocks of the routed experts.  Their SwiGLU inputs
+    // are staged in LDS in chunks, and each task waits only for its own
+    // segment's chunks (see below).
     uint64_t* y_l = p.y_buf + (size_t)l * MK * H;
     {
       // (the thread number made opaque again: the lane-dependent values of the
@@ -1219,13 +1235,53 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       const uint64_t* hsrc = p.hs_buf + ((size_t)l * kCopies + cp) * M * I2;
       const uint64_t* r0src = hr_l + (size_t)(has0 ? sm->pbase[pc0.r] : 0) * I2;
       const uint64_t* r1src = hr_l + (size_t)(has1 ? sm->pbase[pc1.r] : 0) * I2;
-      if (!stage_tagged<4>(ws0 + ws1 + ws2, hs32, tag, wt, tid, [&](int i) {
-            return i < ws0 ? hsrc + i : (i < ws0 + ws1 ? r0src + (i - ws0) : r1src + (i - ws0 - ws1));
-          }))
-        sm->abort_flag = 1;
-      __syncthreads();
+      // The inputs are staged in chunks of up to 512 words, each within one
+      // segment (shared | piece 0 | piece 1), which the waves claim from an LDS
+      // counter; a down task waits only for its own segment's chunks, so the
+      // shared blocks and an early slot's blocks start while a later slot's
+      // rows are still on their way.  Bit c of st_done: chunk c is in LDS (also
+      // after a missed deadline, so that no wave waits on it).  At most
+      // 3 ceil(MOE_MAXM I / 1024) chunks (36 for I = 768).
+      static_assert(3 * ((MOE_MAXM * 32 * CPLI + 511) / 512) <= 64, "staging chunks fit the mask");
+      const int nws = ws0 + ws1 + ws2;
+      auto hsrc_at = [&](int i) {
+        return i < ws0 ? hsrc + i : (i < ws0 + ws1 ? r0src + (i - ws0) : r1src + (i - ws0 - ws1));
+      };
+      // (the same in every lane: held as scalars)
+      const int nc0 = lane0_scalar((ws0 + 511) >> 9), nc1 = lane0_scalar((ws1 + 511) >> 9),
+                nc2 = lane0_scalar((ws2 + 511) >> 9);
+      {
+        // a wave claims at most 65 times (at most 64 chunks)
+        for (int claim = 0; claim <= 64; ++claim) {
+          int c = 0;
+          if (lane == 0) c = atomicAdd(&sm->st_next, 1);
+          c = lane0_scalar(c);
+          if (c >= nc0 + nc1 + nc2) break;
+          const int a = c < nc0 ? c * 512
+                                : (c < nc0 + nc1 ? ws0 + (c - nc0) * 512 : ws0 + ws1 + (c - nc0 - nc1) * 512);
+          const int b = c < nc0 ? ws0 : (c < nc0 + nc1 ? ws0 + ws1 : nws);
+          if (!stage_tagged<8, 64>(min(512, b - a), hs32 + a, tag, wt, lane,
+                                   [&](int i) { return hsrc_at(a + i); }))
+            sm->abort_flag = 1;
+          if (lane == 0)
+            __hip_atomic_fetch_or(&sm->st_done, 1ull << c, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+      }
       MOE_STAMP(6);
-      if (sm->abort_flag == 1) break;
+      // the chunks of segment kd
+      auto await_inputs = [&](int kd) __attribute__((always_inline)) {
+        const int c0 = kd == 0 ? 0 : (kd == 1 ? nc0 : nc0 + nc1);
+        const int nc = kd == 0 ? nc0 : (kd == 1 ? nc1 : nc2);
+        const uint64_t need = (nc >= 64 ? ~0ull : ((1ull << nc) - 1ull)) << c0;
+        while ((__hip_atomic_load(&sm->st_done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) & need) != need) {
+          if (wt.expired()) {
+            record_status(p.hdr, -6 /* MOE_E_TIMEOUT */);
+            sm->abort_flag = 1;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+      };
       const int pb0 = has0 ? sm->pbase[pc0.r] : 0, pb1 = has1 ? sm->pbase[pc1.r] : 0;
       auto down = [&](const DR& R, int nn, int ne, int nrows, const uint4* hv, auto emit)
                       __attribute__((always_inline)) {
@@ -1237,6 +1293,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       auto run = [&](int f, const DR& R) __attribute__((always_inline)) {
         int e2, nn, ne, kd;
         task(f, e2, nn, ne, kd);
+        await_inputs(kd);
         if (kd == 0) {
           down(R, nn, ne, M, hs4, [&](int m, int row, float y) {
             ysh[m * p.nr_max + (row - n0)] = y;
@@ -1253,7 +1310,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       int tk = 0;
       if (lane == 0) tk = atomicAdd(&sm->dn_next, 1);
       for (;;) {
-        const int f = __builtin_amdgcn_readfirstlane(tk);
+        const int f = lane0_scalar(tk);
         if (f >= ntask) break;
         task(f, e, n, n_end, kind);
         if constexpr (W8)
@@ -1264,6 +1321,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
         run(f, DA);
       }
       __syncthreads();
+      if (sm->abort_flag == 1) break;
     }
     MOE_STAMP(7);
 
