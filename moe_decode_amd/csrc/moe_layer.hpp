@@ -880,7 +880,11 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     // ---------------- P1 prefetch: this wave's first router / shared gate-up rows
     // do not depend on x, so their loads fly while x is staged
     const int NRI = topk_in ? 0 : (E + 1) >> 1;
-    const int NSI = (router_only || !S) ? 0 : I2;
+    // One token row (fast selection shape): the shared expert's gate/up items
+    // wait for the selection window (see P4), so that the first loads of the
+    // call are the router rows and x alone.
+    const bool sh_late = M == 1 && K <= 8 && !topk_in && !router_only && E == 512 && S;
+    const int NSI = (router_only || !S || sh_late) ? 0 : I2;
     RowRegs<CPLH> A, B;
     float SC[Fp8Row<CPLH>::C];
     if (gw < NRI + NSI) p1_load<CPLH, W8>(p, l, gw, NRI, A, B, SC, lane, false);
@@ -1034,6 +1038,12 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
             }
           }
           if (ln == 0) sm->sel_ok = ok ? 1 : 0;
+        } else if (sh_late && wv <= 2) {
+          // the shared expert's gate/up items, while wave 0 selects
+          for (int j = (wv - 1) * G + g; j < I2; j += 2 * G) {
+            p1_load<CPLH, W8>(p, l, NRI + j, NRI, A, B, SC, lane, true);
+            p1_compute<CPLH, W8>(p, l, NRI + j, NRI, A, B, SC, xs4, tag, lane, dbg);
+          }
         }
         __syncthreads();
         ranked = sm->sel_ok != 0;
