@@ -272,15 +272,16 @@ WsLayout ws_layout(const moe_dims& d, int M, int L) {
 }
 
 struct LdsPlan {
-  int xs, lg, hs, ysh, ysr, small, gn, total, nr_max;
+  int xs, lg, hs, ysh, ysr, small, gn, p1w, total, nr_max;
 };
 
 // LDS of the layer kernel: x [M][H] bf16, aliased by the SwiGLU rows of the
 // shared expert and of up to two routed slice pieces [3][M][I] bf16 once the
 // routed gate/up rows are done; logits [M][E] fp32; the shared expert's
 // outputs for the owned rows [M][nr_max] fp32; the routed (expert, row)
-// outputs of the owned rows [M*K][nr_max] fp32; the small tables and the
-// norm's gain [H] bf16.
+// outputs of the owned rows [M*K][nr_max] fp32; the small tables; the
+// norm's gain [H] bf16; and, where they fit, the P1 rows of waves 0-2 (bf16,
+// two token rows on).
 int plan_lds(const moe_dims& d, int M, int G, int max_lds, LdsPlan* lp) {
   const int H = d.hidden, E = d.n_experts, I = d.inter;
   lp->nr_max = 2 * (((H / 2) + G - 1) / G);
@@ -303,6 +304,16 @@ int plan_lds(const moe_dims& d, int M, int G, int max_lds, LdsPlan* lp) {
   o = align_up(o + sizeof(Small), 16);
   lp->gn = (int)o;  // the norm's gain
   o = align_up(o + (size_t)H * 2, 16);
+  // bf16 from two token rows on: the router / shared-expert rows of waves 0-2
+  // (two units of H bf16 per half-wave row each), where they fit (-1: none)
+  lp->p1w = -1;
+  if (M >= 2 && d.expert_format == MOE_EXPERT_BF16) {
+    const size_t w = (size_t)3 * 2 * H * 2 * 2;
+    if (o + w <= (size_t)max_lds) {
+      lp->p1w = (int)o;
+      o += w;
+    }
+  }
   lp->total = (int)o;
   return o <= (size_t)max_lds ? MOE_OK : MOE_E_UNSUPPORTED;
 }
@@ -353,6 +364,7 @@ int launch_layer_nl(const moe_dims& d, int M, int L, uint32_t flags,
   p.lds_ysr = lp.ysr;
   p.lds_small = lp.small;
   p.lds_gn = lp.gn;
+  p.lds_p1w = lp.p1w;
   p.x_in = x;
   p.out = out;
   p.tk_idx_in = tk_in;

@@ -108,6 +108,7 @@ struct ParamsT {
   // LDS byte offsets
   int lds_xs, lds_lg, lds_hs, lds_ysh, lds_ysr, lds_small;  // lds_hs: [3*M][I] bf16
   int lds_gn;         // [H] bf16 norm gain
+  int lds_p1w;        // bf16, two token rows on: the router / shared rows of waves 0-2, or -1 (see P1)
   const uint16_t* x_in;
   void* out;
   const int32_t* tk_idx_in;
@@ -227,15 +228,21 @@ __device__ __forceinline__ void load_rows(RowRegs<CPLH>& r, const uint16_t* row0
 }
 
 // Dot product of each half-wave's row with token row m (all lanes of a half
-// receive the sum).
-template <int CPLH>
-__device__ __forceinline__ float dot_rows(const RowRegs<CPLH>& r, const uint4* xs4, int H8, int m,
-                                          int lane) {
+// receive the sum); wat(q) gives this lane's 16-byte chunk q of its row (from
+// registers or from LDS).
+template <int CPLH, typename WAt>
+__device__ __forceinline__ float dot_rows_w(WAt wat, const uint4* xs4, int H8, int m, int lane) {
   const int li = lane & 31;
   float acc = 0.0f;
 #pragma unroll
-  for (int q = 0; q < CPLH; ++q) acc = dot8(r.w[q], xs4[m * H8 + li + 32 * q], acc);
+  for (int q = 0; q < CPLH; ++q) acc = dot8(wat(q), xs4[m * H8 + li + 32 * q], acc);
   return group_sum(acc, 32);
+}
+
+template <int CPLH>
+__device__ __forceinline__ float dot_rows(const RowRegs<CPLH>& r, const uint4* xs4, int H8, int m,
+                                          int lane) {
+  return dot_rows_w<CPLH>([&](int q) { return r.w[q]; }, xs4, H8, m, lane);
 }
 
 // ---- fp8 e4m3 weights with 128 x 128 block scales
@@ -374,6 +381,28 @@ __device__ __forceinline__ void p1_load_second(const P& p, int l, int it, int NR
   }
 }
 
+// Router item it, token row m: the logit of expert 2 it + (lane >> 5), which
+// every lane of the half-wave holds; lane c < kCopies of the half writes copy c.
+template <class P>
+__device__ __forceinline__ void publish_logit(const P& p, int l, int it, int m, float acc,
+                                              uint32_t tag, int lane, uint32_t dbg) {
+  const int e = 2 * it + (lane >> 5), c = lane & 31;
+  if (e < p.E && c < kCopies && !(dbg & DBG_NO_ROUTER_PUBLISH))
+    st_tag(p.lg_buf + (((size_t)l * kCopies + c) * p.M + m) * p.E + e, __float_as_uint(acc), tag);
+}
+
+// Shared-expert pair jp, token row m: a0 holds gate (lanes 0-31) and up (lanes
+// 32-63) of unit 2jp, a1 those of unit 2jp + 1; lane c < kCopies writes copy c.
+template <class P>
+__device__ __forceinline__ void publish_shared(const P& p, int l, int jp, int m, float a0, float a1,
+                                               uint32_t tag, int lane) {
+  const int I2 = p.I >> 1;
+  const uint32_t word = f_to_bf(swiglu(readlane_f(a0, 0), readlane_f(a0, 32))) |
+                        (f_to_bf(swiglu(readlane_f(a1, 0), readlane_f(a1, 32))) << 16);
+  if (lane < kCopies)
+    st_tag(p.hs_buf + (size_t)l * kCopies * p.M * I2 + jp + ((size_t)lane * p.M + m) * I2, word, tag);
+}
+
 template <int CPLH, bool W8, class P>
 __device__ __forceinline__ void p1_compute(const P& p, int l, int it, int NRI,
                                            const RowRegs<CPLH>& A, const RowRegs<CPLH>& B,
@@ -381,19 +410,10 @@ __device__ __forceinline__ void p1_compute(const P& p, int l, int it, int NRI,
                                            uint32_t tag, int lane, uint32_t dbg) {
   const int H8 = p.H >> 3;
   if (it < NRI) {
-    // every lane of a half-wave holds its row's sum: lane c < kCopies of the
-    // half writes copy c
-    const int e = 2 * it + (lane >> 5), c = lane & 31;
-    const bool publish = e < p.E && c < kCopies && !(dbg & DBG_NO_ROUTER_PUBLISH);
 #pragma unroll 1
-    for (int m = 0; m < p.M; ++m) {
-      const float acc = dot_rows<CPLH>(A, xs4, H8, m, lane);
-      if (publish)
-        st_tag(p.lg_buf + (((size_t)l * kCopies + c) * p.M + m) * p.E + e, __float_as_uint(acc), tag);
-    }
+    for (int m = 0; m < p.M; ++m)
+      publish_logit(p, l, it, m, dot_rows<CPLH>(A, xs4, H8, m, lane), tag, lane, dbg);
   } else {
-    const int jp = it - NRI, I2 = p.I >> 1;
-    uint64_t* dst = p.hs_buf + (size_t)l * kCopies * p.M * I2 + jp;
 #pragma unroll 1
     for (int m = 0; m < p.M; ++m) {
       float a0, a1;
@@ -404,9 +424,7 @@ __device__ __forceinline__ void p1_compute(const P& p, int l, int it, int NRI,
         a0 = dot_rows<CPLH>(A, xs4, H8, m, lane);
         a1 = dot_rows<CPLH>(B, xs4, H8, m, lane);
       }
-      const uint32_t word = f_to_bf(swiglu(readlane_f(a0, 0), readlane_f(a0, 32))) |
-                            (f_to_bf(swiglu(readlane_f(a1, 0), readlane_f(a1, 32))) << 16);
-      if (lane < kCopies) st_tag(dst + ((size_t)lane * p.M + m) * I2, word, tag);  // copy lane
+      publish_shared(p, l, it - NRI, m, a0, a1, tag, lane);
     }
   }
 }
@@ -885,6 +903,19 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     // call are the router rows and x alone.
     const bool sh_late = M == 1 && K <= 8 && !topk_in && !router_only && E == 512 && S;
     const int NSI = (router_only || !S || sh_late) ? 0 : I2;
+    // bf16, two token rows on (where LDS has room): the token rows of a P1 item
+    // are spread over all eight waves.  The item's wave (0-2) loads its rows as
+    // before and copies them into its LDS slot, [unit][chunk][lane]; each wave
+    // then computes whole token rows from LDS.  One wave would otherwise take
+    // M dependent dot products per item (about 1.9 us for a router pair at
+    // M = 6, twice that for a shared item), which the logits wait for.
+    // (made again where used, from the launch's values, not held through P0)
+    auto p1s_on = [&]() __attribute__((always_inline)) {
+      return !W8 && p.M >= 2 && p.lds_p1w >= 0 && NRI + NSI <= 3 * (int)gridDim.x;
+    };
+    auto p1w_at = [&]() __attribute__((always_inline)) {
+      return reinterpret_cast<uint4*>(lds + p.lds_p1w);
+    };
     RowRegs<CPLH> A, B;
     float SC[Fp8Row<CPLH>::C];
     if (gw < NRI + NSI) p1_load<CPLH, W8>(p, l, gw, NRI, A, B, SC, lane, false);
@@ -961,16 +992,57 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
         }
       }
     }
+    if (p1s_on() && gw < NRI + NSI) {
+      uint4* sl = p1w_at() + (size_t)wv * 2 * CPLH * 64;
+#pragma unroll
+      for (int q = 0; q < CPLH; ++q) sl[q * 64 + lane] = A.w[q];
+    }
     __syncthreads();
     MOE_STAMP(1);
 
     // ---------------- P1: router rows + shared expert gate/up rows
-    for (int it = gw; it < NRI + NSI; it += NW) {
-      if (it != gw)
-        p1_load<CPLH, W8>(p, l, it, NRI, A, B, SC, lane, true);
-      else if (it >= NRI)  // the prefetched gate/up item still needs its second row
-        p1_load_second<CPLH, W8>(p, l, it, NRI, B, lane);
-      p1_compute<CPLH, W8>(p, l, it, NRI, A, B, SC, xs4, tag, lane, dbg);
+    if (!p1s_on()) {
+      for (int it = gw; it < NRI + NSI; it += NW) {
+        if (it != gw)
+          p1_load<CPLH, W8>(p, l, it, NRI, A, B, SC, lane, true);
+        else if (it >= NRI)  // the prefetched gate/up item still needs its second row
+          p1_load_second<CPLH, W8>(p, l, it, NRI, B, lane);
+        p1_compute<CPLH, W8>(p, l, it, NRI, A, B, SC, xs4, tag, lane, dbg);
+      }
+    } else {
+      // items of waves 0-2: router items first (w G + g < NRI), then shared ones
+      const int H8 = H >> 3;
+      int nri = 0, nsi = 0;
+#pragma unroll
+      for (int w = 0; w < 3; ++w) {
+        const int it = w * G + g;
+        nri += it < NRI ? 1 : 0;
+        nsi += (it >= NRI && it < NRI + NSI) ? 1 : 0;
+      }
+      const bool own_sh = gw >= NRI && gw < NRI + NSI;
+      uint4* p1w = p1w_at();
+      if (own_sh) p1_load_second<CPLH, W8>(p, l, gw, NRI, B, lane);  // flies during the router rows
+      for (int u = wv; u < nri * M; u += MOE_WAVES) {
+        const int w = u / M, m = u - w * M;
+        const uint4* sl = p1w + (size_t)w * 2 * CPLH * 64;
+        publish_logit(p, l, w * G + g, m,
+                      dot_rows_w<CPLH>([&](int q) { return sl[q * 64 + lane]; }, xs4, H8, m, lane),
+                      tag, lane, dbg);
+      }
+      if (own_sh) {
+        uint4* sl = p1w + (size_t)wv * 2 * CPLH * 64 + CPLH * 64;
+#pragma unroll
+        for (int q = 0; q < CPLH; ++q) sl[q * 64 + lane] = B.w[q];
+      }
+      __syncthreads();
+      for (int u = wv; u < nsi * M; u += MOE_WAVES) {
+        const int w = nri + u / M, m = u - (u / M) * M;
+        const uint4* sl = p1w + (size_t)w * 2 * CPLH * 64;
+        const float a0 = dot_rows_w<CPLH>([&](int q) { return sl[q * 64 + lane]; }, xs4, H8, m, lane);
+        const float a1 =
+            dot_rows_w<CPLH>([&](int q) { return sl[(CPLH + q) * 64 + lane]; }, xs4, H8, m, lane);
+        publish_shared(p, l, w * G + g - NRI, m, a0, a1, tag, lane);
+      }
     }
     MOE_STAMP(2);
 
