@@ -280,8 +280,8 @@ struct LdsPlan {
 // routed gate/up rows are done; logits [M][E] fp32; the shared expert's
 // outputs for the owned rows [M][nr_max] fp32; the routed (expert, row)
 // outputs of the owned rows [M*K][nr_max] fp32; the small tables; the
-// norm's gain [H] bf16; and, where they fit, the P1 rows of waves 0-2 (bf16,
-// two token rows on).
+// norm's gain [H] bf16; and, where they fit, the P1 rows of waves 0-2 (two
+// token rows on).
 int plan_lds(const moe_dims& d, int M, int G, int max_lds, LdsPlan* lp) {
   const int H = d.hidden, E = d.n_experts, I = d.inter;
   lp->nr_max = 2 * (((H / 2) + G - 1) / G);
@@ -304,11 +304,13 @@ int plan_lds(const moe_dims& d, int M, int G, int max_lds, LdsPlan* lp) {
   o = align_up(o + sizeof(Small), 16);
   lp->gn = (int)o;  // the norm's gain
   o = align_up(o + (size_t)H * 2, 16);
-  // bf16 from two token rows on: the router / shared-expert rows of waves 0-2
+  // from two token rows on: the router / shared-expert rows of waves 0-2
   // (two units of H bf16 per half-wave row each), where they fit (-1: none)
   lp->p1w = -1;
-  if (M >= 2 && d.expert_format == MOE_EXPERT_BF16) {
-    const size_t w = (size_t)3 * 2 * H * 2 * 2;
+  if (M >= 2) {
+    // 3 slots: two units of 2H bf16 (a bf16 row pair per half-wave); fp8
+    // shared items use less plus their scales after the units
+    const size_t w = (size_t)3 * (2 * H * 2 * 2 + 64 * 4 * ((H / 256 + 1) / 2));
     if (o + w <= (size_t)max_lds) {
       lp->p1w = (int)o;
       o += w;

@@ -323,6 +323,22 @@ __device__ __forceinline__ float dot_rows8(const RowRegs<CPLH>& r,
   return group_sum(acc, 32);
 }
 
+// The same with the codes and scales in LDS ([chunk][lane]); same order of
+// additions as dot_rows8.
+template <int CPLH>
+__device__ __forceinline__ float dot_rows8_lds(const uint4* sl, const float* ss, const uint4* xs4,
+                                               int H, int m, int lane) {
+  const int li = lane & 31, H8 = H >> 3;
+  float acc = 0.0f;
+#pragma unroll
+  for (int q = 0; q < Fp8Row<CPLH>::C; ++q) {
+    const int c = Fp8Row<CPLH>::valid(li + 32 * q, H) ? li + 32 * q : 0;
+    const float part = dot16_fp8(sl[q * 64 + lane], xs4[m * H8 + 2 * c], xs4[m * H8 + 2 * c + 1]);
+    acc = fmaf(ss[q * 64 + lane], part, acc);
+  }
+  return group_sum(acc, 32);
+}
+
 // P1 item `it`: router rows (it < NRI) or a shared-expert gate/up row pair.
 // The first unit goes to A; a gate/up item's second unit goes to B when
 // `second` is set.
@@ -911,11 +927,14 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     // M = 6, twice that for a shared item), which the logits wait for.
     // (made again where used, from the launch's values, not held through P0)
     auto p1s_on = [&]() __attribute__((always_inline)) {
-      return !W8 && p.M >= 2 && p.lds_p1w >= 0 && NRI + NSI <= 3 * (int)gridDim.x;
+      return p.M >= 2 && p.lds_p1w >= 0 && NRI + NSI <= 3 * (int)gridDim.x;
     };
     auto p1w_at = [&]() __attribute__((always_inline)) {
       return reinterpret_cast<uint4*>(lds + p.lds_p1w);
     };
+    // one slot, in 16-byte units: unit A [CPLH][64], unit B [CPLH][64], then
+    // an fp8 shared item's scales [C][64] fp32
+    constexpr int kP1Slot = 2 * CPLH * 64 + 16 * Fp8Row<CPLH>::C;
     RowRegs<CPLH> A, B;
     float SC[Fp8Row<CPLH>::C];
     if (gw < NRI + NSI) p1_load<CPLH, W8>(p, l, gw, NRI, A, B, SC, lane, false);
@@ -993,9 +1012,19 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       }
     }
     if (p1s_on() && gw < NRI + NSI) {
-      uint4* sl = p1w_at() + (size_t)wv * 2 * CPLH * 64;
+      // slot: unit A [CPLH][64], unit B [CPLH][64] (16-byte chunks); fp8 shared
+      // items use C chunks of each and keep their scales [C][64] after B
+      uint4* sl = p1w_at() + (size_t)wv * kP1Slot;
+      if (W8 && gw >= NRI) {
 #pragma unroll
-      for (int q = 0; q < CPLH; ++q) sl[q * 64 + lane] = A.w[q];
+        for (int q = 0; q < Fp8Row<CPLH>::C; ++q) {
+          sl[q * 64 + lane] = A.w[q];
+          reinterpret_cast<float*>(sl + 2 * CPLH * 64)[q * 64 + lane] = SC[q];
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < CPLH; ++q) sl[q * 64 + lane] = A.w[q];
+      }
     }
     __syncthreads();
     MOE_STAMP(1);
@@ -1024,23 +1053,30 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       if (own_sh) p1_load_second<CPLH, W8>(p, l, gw, NRI, B, lane);  // flies during the router rows
       for (int u = wv; u < nri * M; u += MOE_WAVES) {
         const int w = u / M, m = u - w * M;
-        const uint4* sl = p1w + (size_t)w * 2 * CPLH * 64;
+        const uint4* sl = p1w + (size_t)w * kP1Slot;
         publish_logit(p, l, w * G + g, m,
                       dot_rows_w<CPLH>([&](int q) { return sl[q * 64 + lane]; }, xs4, H8, m, lane),
                       tag, lane, dbg);
       }
       if (own_sh) {
-        uint4* sl = p1w + (size_t)wv * 2 * CPLH * 64 + CPLH * 64;
+        uint4* sl = p1w + (size_t)wv * kP1Slot + CPLH * 64;
+        constexpr int NB = W8 ? Fp8Row<CPLH>::C : CPLH;
 #pragma unroll
-        for (int q = 0; q < CPLH; ++q) sl[q * 64 + lane] = B.w[q];
+        for (int q = 0; q < NB; ++q) sl[q * 64 + lane] = B.w[q];
       }
       __syncthreads();
       for (int u = wv; u < nsi * M; u += MOE_WAVES) {
         const int w = nri + u / M, m = u - (u / M) * M;
-        const uint4* sl = p1w + (size_t)w * 2 * CPLH * 64;
-        const float a0 = dot_rows_w<CPLH>([&](int q) { return sl[q * 64 + lane]; }, xs4, H8, m, lane);
-        const float a1 =
-            dot_rows_w<CPLH>([&](int q) { return sl[(CPLH + q) * 64 + lane]; }, xs4, H8, m, lane);
+        const uint4* sl = p1w + (size_t)w * kP1Slot;
+        float a0, a1;
+        if constexpr (W8) {
+          const float* ss = reinterpret_cast<const float*>(sl + 2 * CPLH * 64);
+          a0 = dot_rows8_lds<CPLH>(sl, ss, xs4, H, m, lane);
+          a1 = dot_rows8_lds<CPLH>(sl + CPLH * 64, ss, xs4, H, m, lane);
+        } else {
+          a0 = dot_rows_w<CPLH>([&](int q) { return sl[q * 64 + lane]; }, xs4, H8, m, lane);
+          a1 = dot_rows_w<CPLH>([&](int q) { return sl[(CPLH + q) * 64 + lane]; }, xs4, H8, m, lane);
+        }
         publish_shared(p, l, w * G + g - NRI, m, a0, a1, tag, lane);
       }
     }
