@@ -1267,6 +1267,28 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       // so a fixed deal per wave leaves half the waves a task or more behind.
       // The next ticket is taken while the current task's rows are in flight.
       const int T = U * I2;
+      // Workgroups 2i (on an even XCD) and 2i + 1 (on an odd one) hold the
+      // tasks 2i + G k and 2i + 1 + G k.  The odd XCDs stream a few percent
+      // slower (their workgroups end the phase about 4.5 us later at M = 6),
+      // so the even partner also takes the odd one's task of every
+      // k = XW - 1 (mod XW), right after its own of the same k: the tasks
+      // still complete in slot order, and the even side does 16/15 of the
+      // odd side's tasks.  Only for bf16 and at least 32 tasks per workgroup
+      // (fewer, as at one token row or the TP4 shard, measured no gain).
+      // Ticket j of this workgroup -> task:
+      constexpr int XW = 16;
+      const bool xw_on = !W8 && (G & 1) == 0 && T >= 32 * G;
+      auto task_of = [&](int j) __attribute__((always_inline)) {
+        if (xw_on && (g & 1) == 0) {
+          const int b = j / (XW + 1), r = j - b * (XW + 1);
+          return r == XW ? g + 1 + G * (XW * b + XW - 1) : g + G * (XW * b + r);
+        }
+        if (xw_on) {
+          const int b = j / (XW - 1), r = j - b * (XW - 1);
+          return g + G * (XW * b + r);
+        }
+        return g + G * j;
+      };
       auto ticket = [&]() __attribute__((always_inline)) {
         int v = 0;
         if (lane == 0) v = atomicAdd(&sm->gu_next, 1);
@@ -1276,7 +1298,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
         const size_t HB = (size_t)(H >> 7);
         int tk = ticket();
         for (;;) {
-          const int t = g + G * __builtin_amdgcn_readfirstlane(tk);
+          const int t = task_of(__builtin_amdgcn_readfirstlane(tk));
           if (t >= T) break;
           const int rr = t / I2;
           const int jp = t - rr * I2;
@@ -1293,7 +1315,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       } else {
         int tk = ticket();
         for (;;) {
-          const int t = g + G * __builtin_amdgcn_readfirstlane(tk);
+          const int t = task_of(__builtin_amdgcn_readfirstlane(tk));
           if (t >= T) break;
           const int rr = t / I2;
           const int jp = t - rr * I2;
