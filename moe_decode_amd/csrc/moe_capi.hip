@@ -272,12 +272,12 @@ WsLayout ws_layout(const moe_dims& d, int M, int L) {
 }
 
 struct LdsPlan {
-  int xs, lg, hs, ysh, ysr, small, gn, p1w, total, nr_max;
+  int xs, lg, hs, ysh, ysr, small, gn, p1w, total, nr_max, fold;
 };
 
 // LDS of the layer kernel: x [M][H] bf16, aliased by the SwiGLU rows of the
-// shared expert and of up to two routed slice pieces [3][M][I] bf16 once the
-// routed gate/up rows are done; logits [M][E] fp32; the shared expert's
+// shared expert and of up to two (four, folded) routed slice pieces
+// [3 or 5][M][I] bf16 once the routed gate/up rows are done; logits [M][E] fp32; the shared expert's
 // outputs for the owned rows [M][nr_max] fp32; the routed (expert, row)
 // outputs of the owned rows [M*K][nr_max] fp32; the small tables; the
 // norm's gain [H] bf16; and, where they fit, the P1 rows of waves 0-2 (two
@@ -287,12 +287,24 @@ int plan_lds(const moe_dims& d, int M, int G, int max_lds, LdsPlan* lp) {
   lp->nr_max = 2 * (((H / 2) + G - 1) / G);
   if (lp->nr_max > 64) return MOE_E_UNSUPPORTED;  // residual rows kept in LDS
   // x (read until the routed gate/up rows are done) and the SwiGLU rows of the
-  // down tasks (shared | first piece | second piece, written after) share a region
+  // down tasks (shared | pieces, written after) share a region: three segments,
+  // or five with the down slices folded (four pieces), which is chosen where
+  // it fits
   size_t o = 0;
   lp->xs = (int)o;
   lp->hs = (int)o;
-  const size_t xh = (size_t)M * H * 2 > (size_t)3 * M * I * 2 ? (size_t)M * H * 2
-                                                                 : (size_t)3 * M * I * 2;
+  auto rest = [&](int segs) {
+    const size_t xh = std::max((size_t)M * H * 2, (size_t)segs * M * I * 2);
+    size_t q = align_up(xh, 16);
+    q = align_up(q + (size_t)M * E * 4, 16);
+    q = align_up(q + (size_t)M * lp->nr_max * 4, 16);
+    q = align_up(q + (size_t)M * d.top_k * lp->nr_max * 4, 16);
+    q = align_up(q + sizeof(Small), 16);
+    q = align_up(q + (size_t)H * 2, 16);
+    return q;
+  };
+  lp->fold = rest(5) <= (size_t)max_lds ? 1 : 0;
+  const size_t xh = std::max((size_t)M * H * 2, (size_t)(lp->fold ? 5 : 3) * M * I * 2);
   o = align_up(o + xh, 16);
   lp->lg = (int)o;
   o = align_up(o + (size_t)M * E * 4, 16);
@@ -366,6 +378,7 @@ int launch_layer_nl(const moe_dims& d, int M, int L, uint32_t flags,
   p.lds_ysr = lp.ysr;
   p.lds_small = lp.small;
   p.lds_gn = lp.gn;
+  p.fold = lp.fold;
   p.lds_p1w = lp.p1w;
   p.x_in = x;
   p.out = out;

@@ -108,6 +108,7 @@ struct ParamsT {
   // LDS byte offsets
   int lds_xs, lds_lg, lds_hs, lds_ysh, lds_ysr, lds_small;  // lds_hs: [3*M][I] bf16
   int lds_gn;         // [H] bf16 norm gain
+  int fold;           // down slices folded: half from the first slots, half from the last (see P6)
   int lds_p1w;        // bf16, two token rows on: the router / shared rows of waves 0-2, or -1 (see P1)
   const uint16_t* x_in;
   void* out;
@@ -144,6 +145,12 @@ struct Small {
   float rn[MOE_MAXM];        // RMSNorm scale per token row
   alignas(16) uint64_t cand[MOE_WAVES * 128];  // top-k: each wave's candidates + spare slots
   uint16_t hres[MOE_MAXM * 64];  // residual input h_l of this workgroup's output rows
+  // this workgroup's down tasks (P7): per piece k < 4 its slot, rows [n0, n1),
+  // blocks, token rows and first (slot, row) pair; per segment (shared |
+  // pieces) its first staged word and first staging chunk (entry 5: the ends)
+  int dk_r[4], dk_n0[4], dk_n1[4], dk_nb[4], dk_nrow[4], dk_pb[4];
+  int dk_ws[6], dk_nc[6];
+  int dk_ntask;
 };
 
 __device__ __forceinline__ float swiglu(float a, float b) {
@@ -788,17 +795,20 @@ struct Piece {
   int r, j0, j1, n0, n1;
 };
 
-// (32-bit arithmetic: g, U <= 256 and a, b <= G, so every product stays below 2^31)
-__device__ __forceinline__ bool slice_piece(int g, int G, int U, int I, int H, int q, Piece& pc) {
+// Piece q (0 or 1) of the range [s0, s1) of the (slot, output row) space, in
+// units of 1/SG slot; a range of at most one slot lies in at most two slots.
+// (32-bit arithmetic: s0, s1 <= 512 U, U <= 256, and a, b <= SG <= 512, so
+// every product stays below 2^31)
+__device__ __forceinline__ bool range_piece(int s0, int s1, int SG, int U, int I, int H, int q,
+                                            Piece& pc) {
   if (U <= 0) return false;
-  const int s0 = g * U, s1 = (g + 1) * U;  // in units of 1/G
-  const int r = (int)((uint32_t)s0 / (uint32_t)G) + q;
-  if (r * G >= s1 || r >= U) return false;
-  int a = s0 - r * G, b = s1 - r * G;
+  const int r = (int)((uint32_t)s0 / (uint32_t)SG) + q;
+  if (r * SG >= s1 || r >= U) return false;
+  int a = s0 - r * SG, b = s1 - r * SG;
   if (a < 0) a = 0;
-  if (b > G) b = G;
+  if (b > SG) b = SG;
   if (b <= a) return false;
-  const uint32_t I2 = (uint32_t)I >> 1, H2 = (uint32_t)H >> 1, uG = (uint32_t)G;
+  const uint32_t I2 = (uint32_t)I >> 1, H2 = (uint32_t)H >> 1, uG = (uint32_t)SG;
   pc.r = r;
   pc.j0 = 2 * (int)(((uint32_t)a * I2 + uG / 2) / uG);
   pc.j1 = 2 * (int)(((uint32_t)b * I2 + uG / 2) / uG);
@@ -1225,9 +1235,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     // used.  This workgroup's slice (pieces of at most two slots) still fixes
     // its down-projection work below.
     uint64_t* hr_l = p.hr_buf + (size_t)l * MK * I2;
-    Piece pc0, pc1;
-    const bool has0 = slice_piece(g, G, U, I, H, 0, pc0);
-    const bool has1 = slice_piece(g, G, U, I, H, 1, pc1);
+
     {
       const int H8 = H >> 3;
       // one task: SwiGLU of gate/up row pairs (2jp, 2jp + 1) for every row that chose slot rr
@@ -1344,64 +1352,92 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       asm volatile("" : "+v"(tid_p7));
       const int tid = tid_p7;
       const int lane = tid & 63;
-      // the SwiGLU rows staged below overwrite x, which the routed gate/up rows
-      // read; and the slot tables read below may come from wave 0 alone (one
-      // token row)
-      __syncthreads();
       const int BR = 8 * DB;
       const int nbs = (S && NR > 0) ? (NR + BR - 1) / BR : 0;
-      const int nb0 = has0 ? (pc0.n1 - pc0.n0 + BR - 1) / BR : 0;
-      const int nb1 = has1 ? (pc1.n1 - pc1.n0 + BR - 1) / BR : 0;
-      const int nrow0 = has0 ? __builtin_popcount(sm->umask[pc0.r]) : 0;
-      const int nrow1 = has1 ? __builtin_popcount(sm->umask[pc1.r]) : 0;
-      const int ntask = nbs + nb0 + nb1;
-      // task f -> (expert, first row, end row, h rows in LDS, rows, emit kind)
+      // This workgroup's down slice of the (slot, output row) space: G equal
+      // slices in slot order (at most two pieces), or, folded, half-slice g of
+      // the first half of the space and half-slice 2G - 1 - g of the second
+      // (at most four pieces): every workgroup then starts on rows of early
+      // slots while the last slots' gate/up tasks, whose finish varies most
+      // between workgroups, are still completing.  Thread 0 writes the table
+      // of pieces and staging segments into LDS (kept out of registers, which
+      // the streaming loops need); the barrier below publishes it.
+      if (tid == 0) {
+        const int SG = p.fold ? 2 * G : G;
+        int ws = nbs ? M * I2 : 0, nc = (ws + 511) >> 9, nt = nbs;
+        sm->dk_ws[0] = 0;
+        sm->dk_nc[0] = 0;
+        for (int k = 0; k < 4; ++k) {
+          Piece pc;
+          const int hb = k >> 1;  // half-slice: 0 the first (or the only), 1 the folded one
+          const int h0 = hb ? (2 * G - 1 - g) * U : g * U;
+          const bool has = (hb == 0 || p.fold) && range_piece(h0, h0 + U, SG, U, I, H, k & 1, pc);
+          const int nb = has ? (pc.n1 - pc.n0 + BR - 1) / BR : 0;
+          const int nrow = has ? __builtin_popcount(sm->umask[pc.r]) : 0;
+          sm->dk_r[k] = has ? pc.r : 0;
+          sm->dk_n0[k] = has ? pc.n0 : 0;
+          sm->dk_n1[k] = has ? pc.n1 : 0;
+          sm->dk_nb[k] = nb;
+          sm->dk_nrow[k] = nrow;
+          sm->dk_pb[k] = has ? sm->pbase[pc.r] : 0;
+          sm->dk_ws[k + 1] = ws;
+          sm->dk_nc[k + 1] = nc;
+          const int w = nb ? nrow * I2 : 0;
+          ws += w;
+          nc += (w + 511) >> 9;
+          nt += nb;
+        }
+        sm->dk_ws[5] = ws;
+        sm->dk_nc[5] = nc;
+        sm->dk_ntask = nt;
+      }
+      // (without the barrier the SwiGLU rows staged below would overwrite x,
+      // which the routed gate/up rows read; the slot tables read below may
+      // come from wave 0 alone with one token row)
+      __syncthreads();
+      const int ntask = sm->dk_ntask;
+      // task f -> (expert, first row, end row, kind: 0 shared, 1 + k piece k)
       auto task = [&](int f, int& e, int& n, int& n_end, int& kind) __attribute__((always_inline)) {
-        if (f < nbs) {
-          e = E; n = n0 + f * BR; n_end = n0 + NR; kind = 0;
-        } else if (f < nbs + nb0) {
-          e = sm->uexp[pc0.r]; n = pc0.n0 + (f - nbs) * BR; n_end = pc0.n1; kind = 1;
-        } else {
-          e = sm->uexp[pc1.r]; n = pc1.n0 + (f - nbs - nb0) * BR; n_end = pc1.n1; kind = 2;
+        e = E; n = n0 + f * BR; n_end = n0 + NR; kind = 0;
+        if (f < nbs) return;
+        f -= nbs;
+        for (int k = 0; k < 4; ++k) {
+          const int nb = sm->dk_nb[k];
+          if (f < nb) {
+            e = sm->uexp[sm->dk_r[k]]; n = sm->dk_n0[k] + f * BR; n_end = sm->dk_n1[k]; kind = 1 + k;
+            return;
+          }
+          f -= nb;
         }
       };
       using DR = std::conditional_t<W8, DownRegs8<C8I, DB8>, DownRegs<CPLI, DBLK>>;
       DR DA;
       int e, n, n_end, kind;
-      // SwiGLU inputs of all this workgroup's down tasks -> LDS: shared | piece 0 | piece 1
-      const int ws0 = nbs ? M * I2 : 0;
-      const int ws1 = nb0 ? nrow0 * I2 : 0;
-      const int ws2 = nb1 ? nrow1 * I2 : 0;
       const uint64_t* hsrc = p.hs_buf + ((size_t)l * kCopies + cp) * M * I2;
-      const uint64_t* r0src = hr_l + (size_t)(has0 ? sm->pbase[pc0.r] : 0) * I2;
-      const uint64_t* r1src = hr_l + (size_t)(has1 ? sm->pbase[pc1.r] : 0) * I2;
-      // The inputs are staged in chunks of up to 512 words, each within one
-      // segment (shared | piece 0 | piece 1), which the waves claim from an LDS
-      // counter; a down task waits only for its own segment's chunks, so the
-      // shared blocks and an early slot's blocks start while a later slot's
-      // rows are still on their way.  Bit c of st_done: chunk c is in LDS (also
-      // after a missed deadline, so that no wave waits on it).  At most
-      // 3 ceil(MOE_MAXM I / 1024) chunks (36 for I = 768).
-      static_assert(3 * ((MOE_MAXM * 32 * CPLI + 511) / 512) <= 64, "staging chunks fit the mask");
-      const int nws = ws0 + ws1 + ws2;
-      auto hsrc_at = [&](int i) {
-        return i < ws0 ? hsrc + i : (i < ws0 + ws1 ? r0src + (i - ws0) : r1src + (i - ws0 - ws1));
-      };
-      // (the same in every lane: held as scalars)
-      const int nc0 = lane0_scalar((ws0 + 511) >> 9), nc1 = lane0_scalar((ws1 + 511) >> 9),
-                nc2 = lane0_scalar((ws2 + 511) >> 9);
+      // The SwiGLU inputs of the tasks are staged into LDS in segments (shared
+      // | piece 0 .. piece 3, words of two bf16), in chunks of up to 512 words,
+      // each within one segment, which the waves claim from an LDS counter; a
+      // down task waits only for its own segment's chunks, so the shared blocks
+      // and an earlier slot's blocks start while a later slot's rows are still
+      // on their way.  Bit c of st_done: chunk c is in LDS (also after a missed
+      // deadline, so that no wave waits on it).  At most 5 ceil(MOE_MAXM I /
+      // 1024) chunks (60 for I = 768).
+      static_assert(5 * ((MOE_MAXM * 32 * CPLI + 511) / 512) <= 64, "staging chunks fit the mask");
       {
+        const int nct = sm->dk_nc[5];
         // a wave claims at most 65 times (at most 64 chunks)
         for (int claim = 0; claim <= 64; ++claim) {
           int c = 0;
           if (lane == 0) c = atomicAdd(&sm->st_next, 1);
           c = lane0_scalar(c);
-          if (c >= nc0 + nc1 + nc2) break;
-          const int a = c < nc0 ? c * 512
-                                : (c < nc0 + nc1 ? ws0 + (c - nc0) * 512 : ws0 + ws1 + (c - nc0 - nc1) * 512);
-          const int b = c < nc0 ? ws0 : (c < nc0 + nc1 ? ws0 + ws1 : nws);
+          if (c >= nct) break;
+          int sg = 0;
+          while (sg < 4 && c >= sm->dk_nc[sg + 1]) ++sg;
+          sg = lane0_scalar(sg);
+          const int a = sm->dk_ws[sg] + (c - sm->dk_nc[sg]) * 512, b = sm->dk_ws[sg + 1];
+          const uint64_t* src = (sg == 0 ? hsrc : hr_l + (size_t)sm->dk_pb[sg - 1] * I2) - sm->dk_ws[sg];
           if (!stage_tagged<8, 64>(min(512, b - a), hs32 + a, tag, wt, lane,
-                                   [&](int i) { return hsrc_at(a + i); }))
+                                   [&](int i) { return src + (a + i); }))
             sm->abort_flag = 1;
           if (lane == 0)
             __hip_atomic_fetch_or(&sm->st_done, 1ull << c, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -1410,8 +1446,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       MOE_STAMP(6);
       // the chunks of segment kd
       auto await_inputs = [&](int kd) __attribute__((always_inline)) {
-        const int c0 = kd == 0 ? 0 : (kd == 1 ? nc0 : nc0 + nc1);
-        const int nc = kd == 0 ? nc0 : (kd == 1 ? nc1 : nc2);
+        const int c0 = sm->dk_nc[kd], nc = sm->dk_nc[kd + 1] - c0;
         const uint64_t need = (nc >= 64 ? ~0ull : ((1ull << nc) - 1ull)) << c0;
         while ((__hip_atomic_load(&sm->st_done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) & need) != need) {
           if (wt.expired()) {
@@ -1422,7 +1457,6 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
           __builtin_amdgcn_s_sleep(1);
         }
       };
-      const int pb0 = has0 ? sm->pbase[pc0.r] : 0, pb1 = has1 ? sm->pbase[pc1.r] : 0;
       auto down = [&](const DR& R, int nn, int ne, int nrows, const uint4* hv, auto emit)
                       __attribute__((always_inline)) {
         if constexpr (W8)
@@ -1439,9 +1473,9 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
             ysh[m * p.nr_max + (row - n0)] = y;
           });
         } else {
-          const uint4* hv = hs4 + (size_t)(ws0 + (kd == 2 ? ws1 : 0)) / 4;
-          const int pb = kd == 1 ? pb0 : pb1;
-          down(R, nn, ne, kd == 1 ? nrow0 : nrow1, hv, [&](int t, int row, float y) {
+          const int pb = sm->dk_pb[kd - 1], nr = sm->dk_nrow[kd - 1];
+          const uint4* hv = hs4 + (size_t)sm->dk_ws[kd] / 4;
+          down(R, nn, ne, nr, hv, [&](int t, int row, float y) {
             st_tag(y_l + (size_t)(pb + t) * H + row, __float_as_uint(y), tag);
           });
         }
