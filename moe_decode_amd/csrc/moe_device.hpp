@@ -54,11 +54,13 @@ __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w <<
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float bf_to_f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f_to_bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two fp32 -> one word of two bf16 (lo in bits 0-15), round to nearest even
+// (finite inputs): one v_cvt_pk_bf16_f32.
+typedef __bf16 moe_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float moe_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf(float lo, float hi) {
+  const moe_f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, moe_bf16x2));
 }
 
 // acc + sum_{i<8} w_i * x_i over eight bf16 pairs packed in two uint4.

@@ -420,8 +420,8 @@ template <class P>
 __device__ __forceinline__ void publish_shared(const P& p, int l, int jp, int m, float a0, float a1,
                                                uint32_t tag, int lane) {
   const int I2 = p.I >> 1;
-  const uint32_t word = f_to_bf(swiglu(readlane_f(a0, 0), readlane_f(a0, 32))) |
-                        (f_to_bf(swiglu(readlane_f(a1, 0), readlane_f(a1, 32))) << 16);
+  const uint32_t word = pk_bf(swiglu(readlane_f(a0, 0), readlane_f(a0, 32)),
+                              swiglu(readlane_f(a1, 0), readlane_f(a1, 32)));
   if (lane < kCopies)
     st_tag(p.hs_buf + (size_t)l * kCopies * p.M * I2 + jp + ((size_t)lane * p.M + m) * I2, word, tag);
 }
@@ -985,40 +985,51 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     }
     if (p.flags & F_PRENORM) {
       if (tid < (H >> 3)) gn4[tid] = gpre;
-      // Sum of squares per row in double: every bf16 square is exact in fp32 and,
-      // over the value range of a residual stream, every partial sum is exact in
-      // double, so the sum (and the scale) does not depend on the order.
+      // Sum of squares per row in double: every bf16 value and its square are
+      // exact in double and, over the value range of a residual stream, every
+      // partial sum is exact in double, so the sum (and the scale) does not
+      // depend on the order.  A wave's chunks are all requested before any is
+      // used, into four partial sums.
+      const int H8 = H >> 3;
+      constexpr int J = (CPLH + 1) / 2;  // chunks per lane (H8 = 32 CPLH)
       for (int m = wv; m < M; m += MOE_WAVES) {
-        double ss = 0.0;
+        uint4 v[J];
 #pragma unroll
-        for (int j = 0; j < (CPLH + 1) / 2; ++j) {
+        for (int j = 0; j < J; ++j) {
           const int c = lane + 64 * j;
-          if (c < (H >> 3)) {
-            const uint4 v = xs4[m * (H >> 3) + c];
-            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+          v[j] = xs4[m * H8 + (c < H8 ? c : 0)];
+        }
+        double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float a = bf_lo(w4[q]), b = bf_hi(w4[q]);
-              ss += (double)(a * a);
-              ss += (double)(b * b);
-            }
+        for (int j = 0; j < J; ++j) {
+          const uint32_t mk = lane + 64 * j < H8 ? 0xFFFFFFFFu : 0u;
+          const uint32_t w4[4] = {v[j].x & mk, v[j].y & mk, v[j].z & mk, v[j].w & mk};
+#pragma unroll
+          for (int q = 0; q < 4; q += 2) {
+            const double a = bf_lo(w4[q]), b = bf_hi(w4[q]);
+            const double c = bf_lo(w4[q + 1]), d = bf_hi(w4[q + 1]);
+            s0 = __builtin_fma(a, a, s0);
+            s1 = __builtin_fma(b, b, s1);
+            s2 = __builtin_fma(c, c, s2);
+            s3 = __builtin_fma(d, d, s3);
           }
         }
-        ss = wave_sum_f64(ss);
+        const double ss = wave_sum_f64((s0 + s1) + (s2 + s3));
         if (lane == 0) sm->rn[m] = (float)(1.0 / sqrt(ss / (double)H + (double)kRmsEps));
       }
       __syncthreads();
-      // u = bf16((h * r) * gain): two fp32 products, one rounding
-      uint32_t* x32 = reinterpret_cast<uint32_t*>(xs);
-      const uint32_t* g32 = reinterpret_cast<const uint32_t*>(gn4);
-      for (int c = tid; c < H2; c += MOE_WG) {
-        const uint32_t gw = g32[c];
-        const float glo = bf_lo(gw), ghi = bf_hi(gw);
-        for (int m = 0; m < M; ++m) {
-          const float r = sm->rn[m];
-          const uint32_t w = x32[m * H2 + c];
-          x32[m * H2 + c] = f_to_bf((bf_lo(w) * r) * glo) | (f_to_bf((bf_hi(w) * r) * ghi) << 16);
-        }
+      // u = bf16((h * r) * gain): two fp32 products, one rounding; (row,
+      // 16-byte chunk) units over all threads
+      for (int i = tid; i < M * H8; i += MOE_WG) {
+        const int m = i / H8, c = i - m * H8;
+        const uint4 xv = xs4[i], gv = gn4[c];
+        const float r = sm->rn[m];
+        const uint32_t w4[4] = {xv.x, xv.y, xv.z, xv.w}, g4[4] = {gv.x, gv.y, gv.z, gv.w};
+        uint32_t o4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o4[e] = pk_bf((bf_lo(w4[e]) * r) * bf_lo(g4[e]), (bf_hi(w4[e]) * r) * bf_hi(g4[e]));
+        reinterpret_cast<uint4*>(xs)[i] = make_uint4(o4[0], o4[1], o4[2], o4[3]);
       }
     }
     if (p1s_on() && gw < NRI + NSI) {
@@ -1260,8 +1271,8 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
             a0 = dot_rows<CPLH>(X, xs4, H8, m, lane);
             a1 = dot_rows<CPLH>(Y, xs4, H8, m, lane);
           }
-          const uint32_t word = f_to_bf(swiglu(readlane_f(a0, 0), readlane_f(a0, 32))) |
-                                (f_to_bf(swiglu(readlane_f(a1, 0), readlane_f(a1, 32))) << 16);
+          const uint32_t word = pk_bf(swiglu(readlane_f(a0, 0), readlane_f(a0, 32)),
+                                      swiglu(readlane_f(a1, 0), readlane_f(a1, 32)));
           if (lane == 0) st_tag(dst + (size_t)t * I2, word, tag);
           ++t;
         }
@@ -1539,7 +1550,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
         if (p.flags & F_RESIDUAL) {
           const float h0 = bf_to_f(sm->hres[m * p.nr_max + nl]);
           const float h1 = bf_to_f(sm->hres[m * p.nr_max + nl + 1]);
-          const uint32_t word = f_to_bf(h0 + a0) | (f_to_bf(h1 + a1) << 16);
+          const uint32_t word = pk_bf(h0 + a0, h1 + a1);
           if (last) {
             reinterpret_cast<uint32_t*>(p.out)[(m * H + n) >> 1] = word;
           } else {
@@ -1553,7 +1564,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
         } else if (p.flags & F_OUT_F32) {
           reinterpret_cast<float2*>(p.out)[(m * H + n) >> 1] = make_float2(a0, a1);
         } else {
-          reinterpret_cast<uint32_t*>(p.out)[(m * H + n) >> 1] = f_to_bf(a0) | (f_to_bf(a1) << 16);
+          reinterpret_cast<uint32_t*>(p.out)[(m * H + n) >> 1] = pk_bf(a0, a1);
         }
       }
     }
