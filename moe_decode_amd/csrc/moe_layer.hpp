@@ -909,9 +909,13 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
   // A single-layer launch (one weight slot) has no layer loop: the compiler
   // then tracks every load and store of the call exactly and waits only for
   // the ones a value depends on, where a loop's back edge makes it wait for all
-  // of them (stores included) at many points.
+  // of them (stores included) at many points.  (A `for` loop of one iteration
+  // kept its back edge, taken when the abort flag is clear, so the loop's
+  // condition is written into the `while` itself: with one slot the body has no
+  // way back.)
   const int L = NL == 1 ? 1 : p.L;
-  for (int l = 0; l < L; ++l) {
+  int l = 0;
+  do {
     // the thread number, opaque to the compiler: values derived from it are
     // made again in every layer instead of being hoisted out of the layer loop
     // and held in registers through every phase
@@ -1571,7 +1575,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     __syncthreads();
     MOE_STAMP(8);
     if (sm->abort_flag == 1) break;
-  }
+  } while (NL > 1 && ++l < L);
 
   // ---------------- end of call
   __syncthreads();
