@@ -127,6 +127,10 @@ struct ParamsT {
   LayerW lw[NL];
 };
 
+// eight bf16 ones (the RMSNorm gain of a layer without one)
+__device__ const uint4 kBf16OnesChunk = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+typedef __attribute__((address_space(3))) void* LdsPtr;
+
 struct Small {
   int nU, nP, abort_flag, sel_ok;  // sel_ok: one token row selected on the fast path
   int gu_next, dn_next;      // the workgroup's task tickets (gate/up, down)
@@ -954,10 +958,18 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     if (gw < NRI + NSI) p1_load<CPLH, W8>(p, l, gw, NRI, A, B, SC, lane, false);
 
     // ---------------- P0: layer input -> LDS
-    // the norm's gain does not depend on the input: its load flies during the stage
-    const uint16_t* gain = (p.flags & F_PRENORM) ? p.lw[l].gain : nullptr;
-    uint4 gpre = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);  // bf16 ones
-    if (gain && tid < (H >> 3)) gpre = reinterpret_cast<const uint4*>(gain)[tid];
+    // The norm's gain does not depend on the input: its load flies during the
+    // stage.  It is loaded straight into LDS (lane l's 16 bytes land 16 l bytes past
+    // the wave's base): no registers hold it, and no default value is written
+    // into registers that the previous layer's loads may still be filling (the
+    // layer loop would wait there for every load in flight).  A layer without
+    // a gain reads a chunk of bf16 ones in every lane.
+    if ((p.flags & F_PRENORM) && tid < (H >> 3)) {
+      const uint16_t* gain = p.lw[l].gain;
+      const uint4* src = gain ? reinterpret_cast<const uint4*>(gain) + tid : &kBf16OnesChunk;
+      const int wvu = __builtin_amdgcn_readfirstlane(tid >> 6);
+      __builtin_amdgcn_global_load_lds(src, (LdsPtr)(gn4 + 64 * wvu), 16, 0, 0);
+    }
     if (tid == 0) {
       sm->gu_next = 0;  // read after the barriers of the routing phase
       sm->dn_next = 0;
@@ -974,6 +986,8 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
                            [&](int i) { return src + i; }))
         sm->abort_flag = 1;
     }
+    // (the gain's direct loads have landed: vmcnt(0), expcnt and lgkmcnt left free)
+    if (p.flags & F_PRENORM) __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     if (l == 0 && tid == 0 && (p.flags & F_ALIAS)) add_u32(p.hdr + xread, 1u);
     if (sm->abort_flag) break;
@@ -988,7 +1002,6 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       for (int i = tid; i < (M * H) >> 3; i += MOE_WG) dst[i] = xs4[i];
     }
     if (p.flags & F_PRENORM) {
-      if (tid < (H >> 3)) gn4[tid] = gpre;
       // Sum of squares per row in double: every bf16 value and its square are
       // exact in double and, over the value range of a residual stream, every
       // partial sum is exact in double, so the sum (and the scale) does not
