@@ -1147,9 +1147,17 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) bl[i] = (bias && E == 512) ? bias[8 * lane + i] : 0.0f;
       const uint64_t* src = p.lg_buf + ((size_t)l * kCopies + cp) * M * E;
-      if (!stage_tagged<8>(M * E, reinterpret_cast<uint32_t*>(lgs), tag, wt, tid,
-                           [&](int i) { return src + i; }))
+      // One token row: a single wave polls the 512 logit words (eight per
+      // lane, in flight together); 512 polling lanes in each of 256
+      // workgroups slowed the exchange they waited on.
+      if (one_row && E <= 512) {
+        if (wv == 1 && !stage_tagged<8, 64>(M * E, reinterpret_cast<uint32_t*>(lgs), tag, wt, lane,
+                                            [&](int i) { return src + i; }))
+          sm->abort_flag = 1;
+      } else if (!stage_tagged<8>(M * E, reinterpret_cast<uint32_t*>(lgs), tag, wt, tid,
+                                  [&](int i) { return src + i; })) {
         sm->abort_flag = 1;
+      }
       __syncthreads();
       MOE_STAMP(3);
       if (sm->abort_flag == 1) break;
