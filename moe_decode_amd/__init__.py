@@ -152,8 +152,13 @@ def dims(hidden, n_experts, top_k, inter, n_shared, routed_scale=0.0,
 
 def layer_weights(w_router, w_gate_up, w_down, router_bias=None, norm_gain=None,
                   s_gate_up=None, s_down=None):
-    return moe_layer_weights(_ptr(w_router), _ptr(w_gate_up), _ptr(w_down), _ptr(router_bias),
-                             _ptr(norm_gain), _ptr(s_gate_up), _ptr(s_down))
+    w = moe_layer_weights(_ptr(w_router), _ptr(w_gate_up), _ptr(w_down), _ptr(router_bias),
+                          _ptr(norm_gain), _ptr(s_gate_up), _ptr(s_down))
+    # the struct holds raw device addresses: keep the tensors they came from alive
+    # for as long as the struct is (a temporary passed here would otherwise be
+    # freed, and its memory handed to the next allocation, before the call runs)
+    w._keep = (w_router, w_gate_up, w_down, router_bias, norm_gain, s_gate_up, s_down)
+    return w
 
 
 # ---- the C entry points, same names -------------------------------------------

@@ -158,7 +158,9 @@ def test_layer_one_row_planted_ties_exact(gpu, E, K):
     gu = torch.zeros((E + 1, 2 * I, H), dtype=torch.int16, device=gpu)
     dn = torch.zeros((E + 1, H, I), dtype=torch.int16, device=gpu)
     assert gu.shape[0] == E + d.n_shared and dn.shape[0] == E + d.n_shared
-    lw = md.layer_weights(D.to_device(wb), gu, dn, D.to_device(b))
+    # (layer_weights holds the tensors too; named here so the dependency is plain)
+    wr, bias = D.to_device(wb), D.to_device(b)
+    lw = md.layer_weights(wr, gu, dn, bias)
     out = _empty((1, H), torch.int16, gpu)
     idx = _empty((1, K), torch.int32, gpu)
     say("layer_chain one row, bias planted E=%d K=%d" % (E, K))
