@@ -1193,13 +1193,27 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
           }
           if (ln == 0) sm->sel_ok = ok ? 1 : 0;
         } else if (sh_late && wv <= 2) {
-          // the shared expert's gate/up items, while wave 0 selects
-          for (int j = (wv - 1) * G + g; j < I2; j += 2 * G) {
-            p1_load<CPLH, W8>(p, l, NRI + j, NRI, A, B, SC, lane, true);
-            p1_compute<CPLH, W8>(p, l, NRI + j, NRI, A, B, SC, xs4, tag, lane, dbg);
+          // the shared expert's gate/up items.  In the single-layer kernel the
+          // first one's rows are requested while wave 0 selects and used after
+          // the barrier, so that the barrier does not wait for their memory
+          // latency (the layer loop has no registers to hold them across it).
+          const int j0 = (wv - 1) * G + g;
+          if (NL == 1) {
+            if (j0 < I2) p1_load<CPLH, W8>(p, l, NRI + j0, NRI, A, B, SC, lane, true);
+          } else {
+            for (int j = j0; j < I2; j += 2 * G) {
+              p1_load<CPLH, W8>(p, l, NRI + j, NRI, A, B, SC, lane, true);
+              p1_compute<CPLH, W8>(p, l, NRI + j, NRI, A, B, SC, xs4, tag, lane, dbg);
+            }
           }
         }
         __syncthreads();
+        if (NL == 1 && sh_late && wv >= 1 && wv <= 2) {
+          for (int j = (wv - 1) * G + g; j < I2; j += 2 * G) {
+            if (j != (wv - 1) * G + g) p1_load<CPLH, W8>(p, l, NRI + j, NRI, A, B, SC, lane, true);
+            p1_compute<CPLH, W8>(p, l, NRI + j, NRI, A, B, SC, xs4, tag, lane, dbg);
+          }
+        }
         ranked = sm->sel_ok != 0;
         if (ranked) {
           if (g == 0 && p.logits_out && l == 0)
