@@ -316,10 +316,11 @@ int plan_lds(const moe_dims& d, int M, int G, int max_lds, LdsPlan* lp) {
   o = align_up(o + sizeof(Small), 16);
   lp->gn = (int)o;  // the norm's gain
   o = align_up(o + (size_t)H * 2, 16);
-  // from two token rows on: the router / shared-expert rows of waves 0-2
-  // (two units of H bf16 per half-wave row each), where they fit (-1: none)
+  // the router / shared-expert rows of waves 0-2 (two units of H bf16 per
+  // half-wave row each), where they fit (-1: none): from two token rows on
+  // for P1, and at one token row for the shared items of the layer loop
   lp->p1w = -1;
-  if (M >= 2) {
+  {
     // 3 slots: two units of 2H bf16 (a bf16 row pair per half-wave); fp8
     // shared items use less plus their scales after the units
     const size_t w = (size_t)3 * (2 * H * 2 * 2 + 64 * 4 * ((H / 256 + 1) / 2));

@@ -109,7 +109,7 @@ struct ParamsT {
   int lds_xs, lds_lg, lds_hs, lds_ysh, lds_ysr, lds_small;  // lds_hs: [3*M][I] bf16
   int lds_gn;         // [H] bf16 norm gain
   int fold;           // down slices folded: half from the first slots, half from the last (see P6)
-  int lds_p1w;        // bf16, two token rows on: the router / shared rows of waves 0-2, or -1 (see P1)
+  int lds_p1w;        // the router / shared rows of waves 0-2 (see P1, P4), or -1
   const uint16_t* x_in;
   void* out;
   const int32_t* tk_idx_in;
@@ -130,6 +130,9 @@ struct ParamsT {
 // eight bf16 ones (the RMSNorm gain of a layer without one)
 __device__ const uint4 kBf16OnesChunk = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 typedef __attribute__((address_space(3))) void* LdsPtr;
+// cache-policy operand of a direct-to-LDS load: non-temporal, as the weight
+// loads into registers
+constexpr int kNtAux = MOE_WEIGHT_NT ? 2 : 0;
 
 struct Small {
   int nU, nP, abort_flag, sel_ok;  // sel_ok: one token row selected on the fast path
@@ -406,6 +409,28 @@ __device__ __forceinline__ void p1_load_second(const P& p, int l, int it, int NR
     const uint16_t* base = static_cast<const uint16_t*>(p.lw[l].wgu) + (size_t)p.E * (2 * I) * H;
     load_rows<CPLH>(B, base + j1 * H, base + (I + j1) * H, lane);
   }
+}
+
+// bf16 shared-expert item `it` copied from HBM straight into a wave's LDS slot
+// (unit A [CPLH][64] = gate | up of unit 2j, then unit B = those of unit
+// 2j + 1; 16-byte chunks in the register layout of load_rows), without
+// passing through registers.  The copy has landed once the wave's vmcnt is
+// zero; only the issuing wave reads the slot.
+template <int CPLH, class P>
+__device__ __forceinline__ void p1_shared_to_lds(const P& p, int l, int it, int NRI,
+                                                 uint4* slot, int lane) {
+  const size_t H = (size_t)p.H, I = (size_t)p.I;
+  const size_t j0 = 2 * (size_t)(it - NRI);
+  const uint16_t* base = static_cast<const uint16_t*>(p.lw[l].wgu) + (size_t)p.E * (2 * I) * H;
+  const size_t r0 = (lane >> 5) ? I + j0 : j0;
+  const uint4* sa = reinterpret_cast<const uint4*>(base + r0 * H) + (lane & 31);
+  const uint4* sb = reinterpret_cast<const uint4*>(base + (r0 + 1) * H) + (lane & 31);
+#pragma unroll
+  for (int q = 0; q < CPLH; ++q)
+    __builtin_amdgcn_global_load_lds(sa + 32 * q, (LdsPtr)(slot + q * 64), 16, 0, kNtAux);
+#pragma unroll
+  for (int q = 0; q < CPLH; ++q)
+    __builtin_amdgcn_global_load_lds(sb + 32 * q, (LdsPtr)(slot + (CPLH + q) * 64), 16, 0, kNtAux);
 }
 
 // Router item it, token row m: the logit of expert 2 it + (lane >> 5), which
@@ -935,7 +960,10 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     // One token row (fast selection shape): the shared expert's gate/up items
     // wait for the selection window (see P4), so that the first loads of the
     // call are the router rows and x alone.
-    const bool sh_late = M == 1 && K <= 8 && !topk_in && !router_only && E == 512 && S;
+    // In the layer loop the bf16 items go through the LDS slots of waves 1-2,
+    // at most one per wave (see P4); where those do not fit they stay in P1.
+    const bool sh_late = M == 1 && K <= 8 && !topk_in && !router_only && E == 512 && S &&
+                         (NL == 1 || W8 || (p.lds_p1w >= 0 && I2 <= 2 * G));
     const int NSI = (router_only || !S || sh_late) ? 0 : I2;
     // bf16, two token rows on (where LDS has room): the token rows of a P1 item
     // are spread over all eight waves.  The item's wave (0-2) loads its rows as
@@ -955,6 +983,13 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     constexpr int kP1Slot = 2 * CPLH * 64 + 16 * Fp8Row<CPLH>::C;
     RowRegs<CPLH> A, B;
     float SC[Fp8Row<CPLH>::C];
+    if constexpr (NL > 1) {
+      // left undefined on the waves without an item, the rows would be values
+      // that the layer loop carries from one layer to the next, held in
+      // registers through every phase
+      A = {};
+      B = {};
+    }
     if (gw < NRI + NSI) p1_load<CPLH, W8>(p, l, gw, NRI, A, B, SC, lane, false);
 
     // ---------------- P0: layer input -> LDS
@@ -1193,13 +1228,18 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
           }
           if (ln == 0) sm->sel_ok = ok ? 1 : 0;
         } else if (sh_late && wv <= 2) {
-          // the shared expert's gate/up items.  In the single-layer kernel the
-          // first one's rows are requested while wave 0 selects and used after
-          // the barrier, so that the barrier does not wait for their memory
-          // latency (the layer loop has no registers to hold them across it).
+          // the shared expert's gate/up items.  The first one's rows are
+          // requested while wave 0 selects and used after the barrier, so that
+          // the barrier does not wait for their memory latency: in the
+          // single-layer kernel into registers, in the layer loop (which has
+          // no registers to hold them across the barrier) straight into the
+          // wave's LDS slot; fp8 items in the loop are computed before it.
           const int j0 = (wv - 1) * G + g;
           if (NL == 1) {
             if (j0 < I2) p1_load<CPLH, W8>(p, l, NRI + j0, NRI, A, B, SC, lane, true);
+          } else if constexpr (!W8) {
+            const int wvu = __builtin_amdgcn_readfirstlane(wv);
+            if (j0 < I2) p1_shared_to_lds<CPLH>(p, l, NRI + j0, NRI, p1w_at() + (size_t)wvu * kP1Slot, lane);
           } else {
             for (int j = j0; j < I2; j += 2 * G) {
               p1_load<CPLH, W8>(p, l, NRI + j, NRI, A, B, SC, lane, true);
@@ -1212,6 +1252,20 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
           for (int j = (wv - 1) * G + g; j < I2; j += 2 * G) {
             if (j != (wv - 1) * G + g) p1_load<CPLH, W8>(p, l, NRI + j, NRI, A, B, SC, lane, true);
             p1_compute<CPLH, W8>(p, l, NRI + j, NRI, A, B, SC, xs4, tag, lane, dbg);
+          }
+        } else if (NL > 1 && !W8 && sh_late && wv >= 1 && wv <= 2) {
+          const int j0 = (wv - 1) * G + g;
+          if (j0 < I2) {
+            const int wvu = __builtin_amdgcn_readfirstlane(wv);
+            const uint4* sl = p1w_at() + (size_t)wvu * kP1Slot;
+            // the slot's direct loads have landed (they are the wave's only
+            // loads in flight since the barrier)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            const int H8 = H >> 3;
+            const float a0 = dot_rows_w<CPLH>([&](int q) { return sl[q * 64 + lane]; }, xs4, H8, 0, lane);
+            const float a1 =
+                dot_rows_w<CPLH>([&](int q) { return sl[(CPLH + q) * 64 + lane]; }, xs4, H8, 0, lane);
+            publish_shared(p, l, j0, 0, a0, a1, tag, lane);
           }
         }
         ranked = sm->sel_ok != 0;
