@@ -1016,10 +1016,20 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
       uint4* dst = reinterpret_cast<uint4*>(xs);
       for (int i = tid; i < (M * H) >> 3; i += MOE_WG) dst[i] = src[i];
     } else {
+      // One token row: waves 1-7 poll, three words per lane.  Wave 0's router
+      // rows are in flight and a wave's loads return in order, so its polls
+      // would wait behind them; fewer polling lanes also load the exchange
+      // less.  (From two token rows on, where waves 0-2 hold P1 items, polling
+      // from the other five waves measured slower.)
       const uint64_t* src = p.res_buf + ((size_t)l * kCopies + cp) * M * H2;
-      if (!stage_tagged<8>(M * H2, reinterpret_cast<uint32_t*>(xs), tag, wt, tid,
-                           [&](int i) { return src + i; }))
+      if (M == 1 && H2 <= 3 * (MOE_WG - 64)) {
+        if (tid >= 64 && !stage_tagged<3, MOE_WG - 64>(H2, reinterpret_cast<uint32_t*>(xs), tag, wt,
+                                                       tid - 64, [&](int i) { return src + i; }))
+          sm->abort_flag = 1;
+      } else if (!stage_tagged<8>(M * H2, reinterpret_cast<uint32_t*>(xs), tag, wt, tid,
+                                  [&](int i) { return src + i; })) {
         sm->abort_flag = 1;
+      }
     }
     // (the gain's direct loads have landed: vmcnt(0), expcnt and lgkmcnt left free)
     if (p.flags & F_PRENORM) __builtin_amdgcn_s_waitcnt(0x0F70);
