@@ -158,6 +158,7 @@ struct Small {
   int dk_r[4], dk_n0[4], dk_n1[4], dk_nb[4], dk_nrow[4], dk_pb[4];
   int dk_ws[6], dk_nc[6];
   int dk_ntask;
+  int dn_done;  // waves that have left the down loop, in order
 };
 
 __device__ __forceinline__ float swiglu(float a, float b) {
@@ -1008,6 +1009,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     if (tid == 0) {
       sm->gu_next = 0;  // read after the barriers of the routing phase
       sm->dn_next = 0;
+      sm->dn_done = 0;
       sm->st_next = 0;
       sm->st_done = 0ull;
     }
@@ -1459,6 +1461,7 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     // are staged in LDS in chunks, and each task waits only for its own
     // segment's chunks (see below).
     uint64_t* y_l = p.y_buf + (size_t)l * MK * H;
+    int dn_order = 0;  // one token row: this wave's place among the waves leaving the down loop
     {
       // (the thread number made opaque again: the lane-dependent values of the
       // down projection are made here, not hoisted into the gate/up phase)
@@ -1608,6 +1611,11 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
         if (lane == 0) tk = atomicAdd(&sm->dn_next, 1);
         run(f, DA);
       }
+      if (M == 1) {
+        int o = 0;
+        if (lane == 0) o = atomicAdd(&sm->dn_done, 1);
+        dn_order = lane0_scalar(o);
+      }
       __syncthreads();
       if (sm->abort_flag == 1) break;
     }
@@ -1629,12 +1637,21 @@ __global__ __launch_bounds__(MOE_WG, 1) void moe_layer_kernel(ParamsT<NL> p) {
     if (NR > 0) {
       // this workgroup's rows of every routed (expert, row) output -> LDS
       const int nP = sm->nP;
-      if (!stage_tagged<4>(nP * NR, reinterpret_cast<uint32_t*>(ysr), tag, wt, tid,
-                           [&](int i) {
-                             const int pr = i / NR;
-                             return y_l + (size_t)pr * H + n0 + (i - pr * NR);
-                           }))
+      auto yat = [&](int i) {
+        const int pr = i / NR;
+        return y_l + (size_t)pr * H + n0 + (i - pr * NR);
+      };
+      // One token row: the first two waves to leave the down loop poll (one
+      // word per lane).  A wave's loads and stores retire in order, so the
+      // waves whose own down-output stores are oldest see the words soonest.
+      if (M == 1 && nP * NR <= 128) {
+        if (dn_order < 2 &&
+            !stage_tagged<1, 128>(nP * NR, reinterpret_cast<uint32_t*>(ysr), tag, wt,
+                                  dn_order * 64 + lane, yat))
+          sm->abort_flag = 1;
+      } else if (!stage_tagged<4>(nP * NR, reinterpret_cast<uint32_t*>(ysr), tag, wt, tid, yat)) {
         sm->abort_flag = 1;
+      }
     }
     __syncthreads();
     if (sm->abort_flag == 1) break;
